@@ -1,0 +1,28 @@
+"""Float64 CPU oracle of causal scaled dot-product attention (prefill + decode).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the package's smoke
+check and the benchmark's CPU-baseline leg, never by the GPU library.  It is
+plain NumPy, materialises full score matrices, and shares no code with the
+HIP path.  Every function is pinned by the CPU tests against values printed on
+the source pages, closed forms, brute force and an independent library routine.
+"""
+
+from .attention import (
+    allowed_mask,
+    attention_ref,
+    attention_rows_ref,
+    decode_ref,
+    head_attention,
+    kv_head_of,
+    softmax_rows,
+)
+
+__all__ = [
+    "allowed_mask",
+    "attention_ref",
+    "attention_rows_ref",
+    "decode_ref",
+    "head_attention",
+    "kv_head_of",
+    "softmax_rows",
+]

@@ -1,0 +1,205 @@
+"""Float64 CPU oracle for causal scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it.
+
+What is computed, per batch entry b and query head h (sources: the attention
+chapter of the LLM-architecture textbook page, "Механизм внимания",
+section "Scaled dot-product attention" and its worked example
+"Численный пример"; the Chinese multi-head attention post "多头注意力机制",
+its mask and softmax sections):
+
+    g      = kv_head_of(h)                      (GQA/MQA mapping)
+    A      = scale * Q[b,h] @ K[b,g]^T          (scores)
+    A[i,j] = -inf where (i, j) is not allowed   (causal mask, sliding window)
+    m_i    = max_j A[i,j];  E = exp(A - m);  l_i = sum_j E[i,j];  P = E / l
+    O[b,h] = P @ V[b,g]
+    LSE[b,h,i] = m_i + ln l_i                   (natural-log log-sum-exp of
+                                                 the scaled, masked scores)
+
+The full score matrix is materialised on purpose: the oracle is the plain
+definition, not the tiled algorithm, so a reader can check it against the
+formula by eye.  Everything is float64; callers pass the exact stored input
+values (bf16 or fp32) already widened to float64.
+
+Readings taken where the pages leave a choice open:
+  * the mask value is -inf (the Swedish page uses -1e9, the other pages -inf;
+    the two agree whenever a row has a visible key, which the diagonal
+    guarantees here);
+  * the sliding window admits key j for query i iff 0 <= i - j < window
+    (window keys including the query itself); the textbook's own repository
+    admits i - j <= W, one more key;
+  * a window requires the causal mask (the textbook defines the window as a
+    cut of the causal past), so window > 0 with causal=False is an error;
+  * prefill has as many keys as queries and the causal mask is aligned at the
+    top-left corner: query i sees keys j <= i;
+  * a decode step's cached length counts the current token: the query row
+    sits at position lens-1 and sees keys 0..lens-1.
+"""
+
+import numpy as np
+
+
+def kv_head_of(h, n_q_heads, n_kv_heads):
+    """K/V head used by query head ``h``: g(h) = floor(h / (H / G)).
+
+    Textbook page, section "Виды по числу голов K/V: MHA, GQA, MQA": query
+    heads are split into G consecutive groups of H/G heads; MHA is G = H,
+    MQA is G = 1, and H not divisible by G is rejected (ValueError), as the
+    page's constructor does.
+    """
+    if n_kv_heads <= 0 or n_q_heads <= 0:
+        raise ValueError("head counts must be positive")
+    if n_q_heads % n_kv_heads != 0:
+        raise ValueError("number of query heads must be a multiple of K/V heads")
+    group = n_q_heads // n_kv_heads
+    return h // group
+
+
+def allowed_mask(row_positions, n_keys, causal, window):
+    """Boolean [len(row_positions), n_keys]: True where query may see key.
+
+    Causal mask (textbook page, section "Маскирование"; Chinese post, the
+    mask matrix M with -inf above the diagonal): key j is hidden from the
+    query at position i when j > i.  Sliding window (textbook page, section
+    "Скользящее окно", read with the window counted as in the long-context
+    GQA workload: the query sees keys i-window+1 .. i): hidden when
+    i - j >= window.
+    """
+    if window > 0 and not causal:
+        raise ValueError("a sliding window needs the causal mask")
+    i = np.asarray(row_positions, dtype=np.int64)[:, None]
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], n_keys), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        ok &= (i - j) < window
+    return ok
+
+
+def softmax_rows(A):
+    """Numerically stable row softmax: subtract the row max, exp, normalise.
+
+    Swedish/English attention note (its ``softmax`` helper) and the German
+    page's hand computation ("Von Hand"): x - max, e = exp, e / sum.
+    Entries equal to -inf get weight exactly 0 (Chinese post, the
+    softmax(3, 1, -inf) example).  Returns (P, m, l) with m the row max and
+    l the row sum of exp(A - m).
+    """
+    A = np.asarray(A, dtype=np.float64)
+    m = A.max(axis=-1, keepdims=True)
+    E = np.exp(A - m)
+    l = E.sum(axis=-1, keepdims=True)
+    return E / l, m[..., 0], l[..., 0]
+
+
+def head_attention(q_rows, row_positions, K, V, causal, window, scale,
+                   return_probs=False):
+    """Attention of some query rows of one head against one K/V head.
+
+    q_rows: [R, Dh] float64, row_positions: [R] absolute query positions,
+    K, V: [T_kv, Dh].  Returns (O [R, Dh], LSE [R]) and, if asked, P [R, T_kv].
+    Steps follow the textbook's formula softmax(QK^T / sqrt(d_h) + M) V
+    (section "Scaled dot-product attention") with the scale passed in.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    A = scale * (q_rows @ K.T)
+    ok = allowed_mask(row_positions, K.shape[0], causal, window)
+    A = np.where(ok, A, -np.inf)
+    P, m, l = softmax_rows(A)
+    O = P @ V
+    LSE = m + np.log(l)
+    if return_probs:
+        return O, LSE, P
+    return O, LSE
+
+
+def _check_prefill_shapes(Q, K, V):
+    if Q.ndim != 4 or K.ndim != 4 or V.ndim != 4:
+        raise ValueError("Q, K, V must be [B, heads, S, Dh]")
+    B, Nq, S, Dh = Q.shape
+    if K.shape != V.shape or K.shape[0] != B or K.shape[2] != S or K.shape[3] != Dh:
+        raise ValueError("K and V must be [B, Nkv, S, Dh] matching Q")
+    return B, Nq, K.shape[1], S, Dh
+
+
+def attention_ref(Q, K, V, causal=True, window=0, scale=None):
+    """Full prefill attention.  Q: [B,Nq,S,Dh], K,V: [B,Nkv,S,Dh].
+
+    Returns O [B,Nq,S,Dh] and LSE [B,Nq,S], both float64.  ``scale`` defaults
+    to 1/sqrt(Dh), the head size (textbook, "Почему делить на корень из d_h").
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, Nq, Nkv, S, Dh = _check_prefill_shapes(Q, K, V)
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    O = np.empty((B, Nq, S, Dh))
+    LSE = np.empty((B, Nq, S))
+    rows = np.arange(S)
+    for b in range(B):
+        for h in range(Nq):
+            g = kv_head_of(h, Nq, Nkv)
+            O[b, h], LSE[b, h] = head_attention(Q[b, h], rows, K[b, g], V[b, g],
+                                                causal, window, scale)
+    return O, LSE
+
+
+def attention_rows_ref(Q, K, V, triples, causal=True, window=0, scale=None):
+    """Selected output rows of prefill attention.
+
+    ``triples`` is a sequence of (b, h, i).  Each row is computed on its own
+    as a 1 x S score vector; returns O [n, Dh] and LSE [n].
+    """
+    B, Nq, Nkv, S, Dh = _check_prefill_shapes(Q, K, V)
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    n = len(triples)
+    O = np.empty((n, Dh))
+    LSE = np.empty(n)
+    for t, (b, h, i) in enumerate(triples):
+        g = kv_head_of(h, Nq, Nkv)
+        q = np.asarray(Q[b, h, i], dtype=np.float64)[None, :]
+        o, lse = head_attention(q, [i], np.asarray(K[b, g], dtype=np.float64),
+                                np.asarray(V[b, g], dtype=np.float64),
+                                causal, window, scale)
+        O[t], LSE[t] = o[0], lse[0]
+    return O, LSE
+
+
+def decode_ref(q, Kc, Vc, lens, scale=None, rows=None):
+    """One decode step against a KV cache.
+
+    q: [B,Nq,Dh], Kc, Vc: [B,Nkv,Tcap,Dh], lens: [B] with 1 <= lens[b] <= Tcap.
+    Sequence b's query sees its cached keys 0..lens[b]-1 (the new token's
+    key is already in the cache) -- textbook, sections "KV-кэш" and
+    "Prefill и decode": a decode step is a single score row of length t.
+    Entries past lens[b] are never read.  ``scale`` defaults to 1/sqrt(Dh).
+    ``rows`` optionally restricts the work to (b, h) pairs; then O is
+    [len(rows), Dh] and LSE [len(rows)].  Otherwise O [B,Nq,Dh], LSE [B,Nq].
+    """
+    B, Nq, Dh = q.shape
+    Nkv = Kc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    pairs = rows if rows is not None else [(b, h) for b in range(B) for h in range(Nq)]
+    O = np.empty((len(pairs), Dh))
+    LSE = np.empty(len(pairs))
+    for t, (b, h) in enumerate(pairs):
+        n = int(lens[b])
+        if n < 1 or n > Kc.shape[2]:
+            raise ValueError("cache length out of range")
+        g = kv_head_of(h, Nq, Nkv)
+        qrow = np.asarray(q[b, h], dtype=np.float64)[None, :]
+        Kb = np.asarray(Kc[b, g, :n], dtype=np.float64)
+        Vb = np.asarray(Vc[b, g, :n], dtype=np.float64)
+        o, lse = head_attention(qrow, [n - 1], Kb, Vb, True, 0, scale)
+        O[t], LSE[t] = o[0], lse[0]
+    if rows is None:
+        return O.reshape(B, Nq, Dh), LSE.reshape(B, Nq)
+    return O, LSE
