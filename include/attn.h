@@ -1,0 +1,116 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal attention library libattn.so.
+ *
+ * Computes causal scaled dot-product multi-head attention
+ *     O = softmax(Q K^T * scale + M) V        per (batch, query head)
+ * with the grouped-query K/V head map, an optional sliding window, and the
+ * KV-cache decode step.  The operation is the one defined in the attention
+ * chapter of the LLM-architecture textbook ("Механизм внимания", sections
+ * "Scaled dot-product attention", "Маскирование", "Виды по числу голов K/V",
+ * "Скользящее окно", "KV-кэш" and "Prefill и decode").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to dense row-major (contiguous)
+ *     buffers owned by the caller.  The library never allocates, frees,
+ *     synchronises or keeps a pointer after the call returns; the caller keeps
+ *     every buffer alive until the stream has passed the call.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Work is enqueued asynchronously on it.
+ *   - Return value: ATTN_OK (0) or a negative attn_status.  Argument errors
+ *     are detected on the host before anything is enqueued and leave the
+ *     outputs untouched.  ATTN_EHIP reports a HIP launch error.
+ *   - Head map: query head h reads K/V head h / (Nq / Nkv) (integer
+ *     division), so consecutive query heads share a K/V head; Nq must be a
+ *     multiple of Nkv (MHA: Nkv == Nq, MQA: Nkv == 1).
+ *   - Element types: ATTN_BF16 (inputs and O in bfloat16, accumulation in
+ *     fp32) or ATTN_F32.  LSE is always fp32.
+ *   - The library is stateless and re-entrant.
+ */
+#ifndef TCH_ATTN_H
+#define TCH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,        /* null pointer, non-positive size, bad flag/scale  */
+  ATTN_EGQA = -2,          /* Nq is not a multiple of Nkv                      */
+  ATTN_EUNSUPPORTED = -3,  /* dtype or head size outside what is implemented   */
+  ATTN_EWORKSPACE = -4,    /* workspace missing or smaller than required       */
+  ATTN_EHIP = -5           /* HIP runtime reported an error at launch          */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+/*
+ * attn_prefill -- attention of S queries against the same S keys.
+ *
+ *   Q   [B, Nq,  S, Dh]   queries
+ *   K   [B, Nkv, S, Dh]   keys
+ *   V   [B, Nkv, S, Dh]   values
+ *   O   [B, Nq,  S, Dh]   output, same element type as Q
+ *   LSE [B, Nq,  S]       fp32 natural-log log-sum-exp of the scaled, masked
+ *                         score row (m + ln l); may be NULL
+ *   causal   1: query i sees keys j <= i (mask aligned at the top-left);
+ *            0: every key is visible
+ *   window   <= 0: no window; > 0: query i sees only keys with i - j < window,
+ *            i.e. keys max(0, i-window+1) .. i; requires causal == 1
+ *   scale    multiplier of Q K^T; > 0 and finite.  The standard definition
+ *            uses 1/sqrt(Dh) (the head size).
+ *   dtype    attn_dtype of Q, K, V and O.
+ * Supported: Dh in 1..256 for both dtypes; bf16 with Dh == 128 takes the
+ * MFMA kernel, the rest a general kernel.  B, Nq, Nkv, S >= 1.
+ * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int Nq, int Nkv, int S, int Dh,
+                 int causal, int window, float scale,
+                 int dtype, void* stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
+ * for these dimensions (0 when the chosen kernel needs none).  Pure host
+ * function; returns 0 for invalid arguments.
+ */
+size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int dtype);
+
+/*
+ * attn_decode -- one generation step: each sequence's single new query row
+ * against its KV cache (the textbook's decode phase: a 1 x t score row).
+ *
+ *   q       [B, Nq, Dh]          the new token's queries
+ *   Kcache  [B, Nkv, Tcap, Dh]   keys; rows 0 .. lens[b]-1 of sequence b hold
+ *                                its cached keys, the new token's included
+ *   Vcache  [B, Nkv, Tcap, Dh]   values, same layout
+ *   lens    [B] int32, DEVICE    cached length of each sequence, counting the
+ *                                new token; must satisfy 1 <= lens[b] <= Tcap
+ *   O       [B, Nq, Dh]          output, same element type as q
+ *   LSE     [B, Nq] fp32 or NULL
+ *   workspace / workspace_bytes  device scratch of at least
+ *                                attn_decode_workspace_bytes(...) bytes
+ *                                (may be NULL when that is 0)
+ * The scale is 1/sqrt(Dh).  No mask applies beyond the length; cache rows at
+ * or past lens[b] are never read.
+ * lens lives on the device, so the host cannot check it: a value above Tcap
+ * is clamped to Tcap, and a value below 1 yields a NaN output row.
+ * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP.
+ */
+int attn_decode(const void* q, const void* Kcache, const void* Vcache,
+                const int32_t* lens, void* O,
+                int B, int Nq, int Nkv, int Dh, int Tcap,
+                float* LSE, void* workspace, size_t workspace_bytes,
+                int dtype, void* stream);
+
+/* attn_strerror -- static description of an attn_status value. */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCH_ATTN_H */

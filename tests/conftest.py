@@ -9,3 +9,14 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    # name the case before it touches the GPU, so a lost run still says which
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n>>> {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,125 @@
+"""The C ABI: library loads, exports what include/attn.h declares, and rejects
+bad arguments on the host before anything is enqueued.
+
+These tests never launch a kernel: every call carries an argument the library
+must refuse.  They only run where no GPU is visible, so that even a
+validation bug cannot send the fake pointers below to a device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import transformer_causal_head_amd as tch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="host-validation tests use fake pointers; CPU only")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(tch.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = tch.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_covers_all_codes():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert tch.attn_strerror(code) and "unknown" not in tch.attn_strerror(code)
+    assert "unknown" in tch.attn_strerror(-99)
+
+
+def test_workspace_query():
+    n = tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_BF16)
+    # one (m, l, o[128]) fp32 record per (sequence, query head, 1024-key chunk)
+    assert n == 64 * 32 * 32 * (128 + 2) * 4
+    assert tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_F32) == 0
+    assert tch.attn_decode_workspace_bytes(64, 30, 8, 128, 32768, tch.ATTN_BF16) == 0
+    assert tch.attn_decode_workspace_bytes(0, 32, 8, 128, 32768, tch.ATTN_BF16) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _prefill(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, LSE=None, B=1, Nq=4, Nkv=2, S=16, Dh=128,
+             causal=1, window=0, scale=0.125, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_prefill(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Nq"],
+                                  a["Nkv"], a["S"], a["Dh"], a["causal"], a["window"],
+                                  a["scale"], a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), tch.ATTN_EINVAL),
+    (dict(K=None), tch.ATTN_EINVAL),
+    (dict(V=None), tch.ATTN_EINVAL),
+    (dict(O=None), tch.ATTN_EINVAL),
+    (dict(B=0), tch.ATTN_EINVAL),
+    (dict(Nq=0), tch.ATTN_EINVAL),
+    (dict(Nkv=-2), tch.ATTN_EINVAL),
+    (dict(S=0), tch.ATTN_EINVAL),
+    (dict(Dh=0), tch.ATTN_EINVAL),
+    (dict(Nq=6, Nkv=4), tch.ATTN_EGQA),
+    (dict(Dh=257), tch.ATTN_EUNSUPPORTED),
+    (dict(dtype=7), tch.ATTN_EUNSUPPORTED),
+    (dict(causal=0, window=4), tch.ATTN_EINVAL),
+    (dict(causal=2), tch.ATTN_EINVAL),
+    (dict(scale=0.0), tch.ATTN_EINVAL),
+    (dict(scale=-1.0), tch.ATTN_EINVAL),
+    (dict(scale=float("inf")), tch.ATTN_EINVAL),
+    (dict(scale=float("nan")), tch.ATTN_EINVAL),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, K=FAKE, V=FAKE, lens=FAKE, O=FAKE, B=2, Nq=8, Nkv=2, Dh=128, Tcap=64,
+             LSE=None, ws=FAKE, ws_bytes=1 << 30, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_decode(a["q"], a["K"], a["V"], a["lens"], a["O"], a["B"], a["Nq"],
+                                 a["Nkv"], a["Dh"], a["Tcap"], a["LSE"], a["ws"],
+                                 a["ws_bytes"], a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), tch.ATTN_EINVAL),
+    (dict(K=None), tch.ATTN_EINVAL),
+    (dict(V=None), tch.ATTN_EINVAL),
+    (dict(lens=None), tch.ATTN_EINVAL),
+    (dict(O=None), tch.ATTN_EINVAL),
+    (dict(B=0), tch.ATTN_EINVAL),
+    (dict(Tcap=0), tch.ATTN_EINVAL),
+    (dict(Nq=8, Nkv=3), tch.ATTN_EGQA),
+    (dict(Dh=300), tch.ATTN_EUNSUPPORTED),
+    (dict(dtype=5), tch.ATTN_EUNSUPPORTED),
+    (dict(ws=None), tch.ATTN_EWORKSPACE),
+    (dict(ws_bytes=16), tch.ATTN_EWORKSPACE),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_python_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 2, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tch.attn_prefill(q, q, q, q.clone(), None)

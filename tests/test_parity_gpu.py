@@ -1,0 +1,268 @@
+"""GPU parity: the HIP library against the float64 oracle on seeded inputs.
+
+The named workloads run at their full sizes in the launch configuration the
+benchmark times; long ones are checked on seeded sampled rows (plus forced
+rows at the boundaries), the others on every output element.  Edge cases
+cover ragged lengths, every grouped-query layout the kernels specialise, the
+window boundary, non-causal attention and the general kernel.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_causal_head_amd as tch
+import workloads
+from helpers import check, device, run_decode, run_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def _prefill_case(cfg, seed=0):
+    q, k, v = workloads.prefill_inputs(cfg["B"], cfg["Nq"], cfg["Nkv"], cfg["S"], cfg["Dh"],
+                                       cfg["dtype"], seed=seed)
+    return q, k, v
+
+
+# --- the named workloads ----------------------------------------------------
+
+def test_tiny_fp32_full():
+    cfg = W["tiny_fp32_b1_h2_s5_d4"]
+    q, k, v = _prefill_case(cfg)
+    O, L = run_prefill(q, k, v, "f32", True, 0, cfg["scale"])
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "f32") for x in (q, k, v)),
+                                  causal=True, scale=cfg["scale"])
+    say(f"tiny fp32 errors {check(O, L, Or, Lr, 'f32', 'tiny')}")
+
+
+def test_mha_s1024_full():
+    cfg = W["mha_bf16_b2_h32_s1024_d128"]
+    q, k, v = _prefill_case(cfg)
+    O, L = run_prefill(q, k, v, "bf16", True, 0, None)
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)), causal=True)
+    say(f"mha s1024 errors {check(O, L, Or, Lr, 'bf16', 'mha_s1024')}")
+
+
+def _sampled(cfg):
+    q, k, v = _prefill_case(cfg)
+    say(f"inputs ready {cfg['S']}")
+    O, L = run_prefill(q, k, v, "bf16", True, cfg["window"], None)
+    tr = workloads.sample_rows(cfg["B"], cfg["Nq"], cfg["S"], cfg["sample"], seed=1,
+                               forced_rows=cfg["forced_rows"])
+    Qf, Kf, Vf = (workloads.to_f64(x, "bf16") for x in (q, k, v))
+    Or, Lr = oracle.attention_rows_ref(Qf, Kf, Vf, tr, causal=True, window=cfg["window"])
+    idx = tuple(np.array(tr).T)
+    return check(O[idx], L[idx], Or, Lr, "bf16", cfg)
+
+
+def test_mha_s32768_sampled_rows():
+    say(f"mha s32768 errors {_sampled(W['mha_bf16_b1_h32_s32768_d128'])}")
+
+
+def test_gqa_window_s8192_sampled_rows():
+    say(f"gqa window errors {_sampled(W['gqa_bf16_b4_h32kv8_s8192_w4096_d128'])}")
+
+
+def test_decode_b64_full():
+    cfg = W["decode_bf16_b64_h32kv8_t32768_d128"]
+    lens, q, kc, vc = workloads.decode_inputs(cfg["B"], cfg["Nq"], cfg["Nkv"], cfg["Dh"],
+                                              cfg["Tcap"], cfg["len_lo"], cfg["len_hi"])
+    say(f"decode inputs ready, sum(lens)={int(lens.sum())}")
+    O, L = run_decode(q, kc, vc, lens, "bf16")
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), _LazyF64(kc), _LazyF64(vc), lens)
+    say(f"decode errors {check(O, L, Or, Lr, 'bf16', 'decode')}")
+
+
+class _LazyF64:
+    """Widens bf16 cache slices on access, so the full cache is never copied."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+        self._last = (None, None)
+
+    def __getitem__(self, idx):
+        key = repr(idx)
+        if self._last[0] != key:  # consecutive query heads share a K/V slice
+            self._last = (key, workloads.to_f64(self.bits[idx], "bf16"))
+        return self._last[1]
+
+
+# --- prefill edge cases -------------------------------------------------------
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,causal,window", [
+    (1, 1, 1, 1, True, 0),        # one token
+    (1, 4, 4, 2, True, 0),
+    (2, 2, 2, 63, True, 0),       # below one key tile
+    (1, 2, 2, 65, True, 0),       # one key past a tile
+    (1, 4, 1, 200, True, 0),      # MQA, ragged
+    (2, 8, 2, 257, True, 0),      # GQA 4, ragged past a query tile
+    (1, 6, 3, 300, True, 0),      # GQA 2
+    (1, 8, 1, 129, True, 0),      # GQA 8 (two head subgroups)
+    (1, 3, 1, 100, True, 0),      # GQA 3 (odd group)
+    (1, 4, 4, 700, True, 1),      # window 1: only the diagonal
+    (1, 4, 2, 700, True, 64),     # window equal to a tile
+    (2, 8, 2, 600, True, 100),    # window not aligned to tiles
+    (1, 2, 2, 513, True, 600),    # window longer than the sequence
+    (1, 4, 4, 130, False, 0),     # non-causal
+    (1, 4, 2, 77, False, 0),      # non-causal GQA ragged
+])
+def test_prefill_edge_cases_bf16(B, Nq, Nkv, S, causal, window):
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, 128, "bf16", seed=S + 7 * Nq)
+    O, L = run_prefill(q, k, v, "bf16", causal, window, None)
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
+                                  causal=causal, window=window)
+    check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, S, causal, window), storage_allowance=True)
+
+
+@pytest.mark.parametrize("Dh,S,Nq,Nkv,window,dtype", [
+    (4, 5, 2, 2, 0, "f32"),
+    (64, 100, 4, 2, 0, "f32"),
+    (128, 70, 4, 1, 20, "f32"),
+    (256, 33, 2, 2, 0, "f32"),
+    (1, 9, 2, 1, 3, "f32"),
+    (64, 90, 4, 2, 0, "bf16"),
+    (80, 50, 2, 2, 7, "bf16"),
+    (256, 40, 4, 4, 0, "bf16"),
+])
+def test_prefill_general_kernel(Dh, S, Nq, Nkv, window, dtype):
+    q, k, v = workloads.prefill_inputs(1, Nq, Nkv, S, Dh, dtype, seed=Dh + S)
+    scale = 0.5 / math.sqrt(Dh)
+    O, L = run_prefill(q, k, v, dtype, True, window, scale)
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, dtype) for x in (q, k, v)),
+                                  causal=True, window=window, scale=scale)
+    check(O, L, Or, Lr, dtype, (Dh, S, dtype), storage_allowance=True)
+
+
+def test_prefill_scale_is_respected():
+    q, k, v = workloads.prefill_inputs(1, 4, 2, 150, 128, "bf16", seed=3)
+    for scale in (0.02, 0.3):
+        O, L = run_prefill(q, k, v, "bf16", True, 0, scale)
+        Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
+                                      causal=True, scale=scale)
+        check(O, L, Or, Lr, "bf16", scale, storage_allowance=True)
+
+
+# --- properties on the GPU ----------------------------------------------------
+
+def test_causality_bitwise_on_gpu():
+    # perturbing the last token leaves every earlier output row bit-identical
+    q, k, v = workloads.prefill_inputs(1, 8, 2, 333, 128, "bf16", seed=11)
+    O1, L1 = run_prefill(q, k, v, "bf16", True, 0, None)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x, other in ((q2, 12), (k2, 13), (v2, 14)):
+        x[:, :, -1] = workloads.draw(x[:, :, -1].shape, "bf16", 99, other)
+    O2, L2 = run_prefill(q2, k2, v2, "bf16", True, 0, None)
+    assert np.array_equal(O1[:, :, :-1], O2[:, :, :-1])
+    assert np.array_equal(L1[:, :, :-1], L2[:, :, :-1])
+    assert not np.array_equal(O1[:, :, -1], O2[:, :, -1])
+
+
+def test_prefill_deterministic():
+    q, k, v = workloads.prefill_inputs(2, 8, 2, 1000, 128, "bf16", seed=5)
+    O1, L1 = run_prefill(q, k, v, "bf16", True, 300, None)
+    O2, L2 = run_prefill(q, k, v, "bf16", True, 300, None)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_gqa_matches_mha_on_repeated_kv():
+    q, k, v = workloads.prefill_inputs(1, 8, 2, 400, 128, "bf16", seed=21)
+    O, L = run_prefill(q, k, v, "bf16", True, 0, None)
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    Om, Lm = run_prefill(q, kr, vr, "bf16", True, 0, None)
+    np.testing.assert_allclose(O, Om, atol=1e-6)
+    np.testing.assert_allclose(L, Lm, atol=1e-6)
+
+
+def test_window_covering_sequence_equals_causal():
+    q, k, v = workloads.prefill_inputs(1, 4, 4, 300, 128, "bf16", seed=8)
+    Oc, Lc = run_prefill(q, k, v, "bf16", True, 0, None)
+    Ow, Lw = run_prefill(q, k, v, "bf16", True, 300, None)
+    np.testing.assert_allclose(Oc, Ow, atol=1e-6)
+    np.testing.assert_allclose(Lc, Lw, atol=1e-6)
+
+
+def test_lse_may_be_null():
+    dev = device()
+    q, k, v = workloads.prefill_inputs(1, 4, 4, 100, 128, "bf16", seed=2)
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+    O = torch.empty_like(tq)
+    tch.attn_prefill(tq, tk, tv, O, None)
+    torch.cuda.synchronize()
+    O_ref, _ = run_prefill(q, k, v, "bf16", True, 0, None)
+    assert np.array_equal(workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16"), O_ref)
+
+
+def test_bad_flags_rejected_with_real_tensors():
+    dev = device()
+    t = torch.zeros(1, 4, 16, 128, dtype=torch.bfloat16, device=dev)
+    O = torch.empty_like(t)
+    with pytest.raises(tch.AttnError) as e:
+        tch.attn_prefill(t, t, t, O, None, causal=0, window=4)
+    assert e.value.status == tch.ATTN_EINVAL
+    k3 = torch.zeros(1, 3, 16, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tch.AttnError) as e:
+        tch.attn_prefill(t, k3, k3, O, None)
+    assert e.value.status == tch.ATTN_EGQA
+
+
+# --- decode edge cases --------------------------------------------------------
+
+@pytest.mark.parametrize("B,Nq,Nkv,Tcap,lens", [
+    (4, 32, 8, 3000, [1, 2, 1023, 3000]),           # length 1, chunk edges, full cache
+    (3, 8, 8, 2100, [1024, 1025, 2048]),            # MHA (G = 1)
+    (2, 16, 8, 700, [700, 63]),                      # G = 2
+    (2, 16, 2, 5000, [4097, 5000]),                 # G = 8
+    (2, 4, 1, 333, [333, 17]),                       # MQA G = 4
+    (2, 6, 2, 300, [300, 5]),                        # G = 3: general kernel
+    (1, 4, 4, 65, [65]),
+])
+def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, 128, Tcap, 1, Tcap, seed=Tcap,
+                                                lens=lens)
+    O, L = run_decode(q, kc, vc, lens_a, "bf16")
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), workloads.to_f64(kc, "bf16"),
+                               workloads.to_f64(vc, "bf16"), lens_a)
+    check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, Tcap, lens), storage_allowance=True)
+
+
+@pytest.mark.parametrize("Dh", [4, 64, 128])
+def test_decode_fp32(Dh):
+    lens_a, q, kc, vc = workloads.decode_inputs(3, 4, 2, Dh, 50, 1, 50, dtype="f32", seed=Dh,
+                                                lens=[50, 1, 20])
+    O, L = run_decode(q, kc, vc, lens_a, "f32")
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "f32"), workloads.to_f64(kc, "f32"),
+                               workloads.to_f64(vc, "f32"), lens_a)
+    check(O, L, Or, Lr, "f32", Dh)
+
+
+def test_decode_equals_prefill_row():
+    # a decode step of row t-1 against t cached keys reproduces prefill row t-1
+    S = 1500
+    q, k, v = workloads.prefill_inputs(2, 8, 2, S, 128, "bf16", seed=31)
+    Op, Lp = run_prefill(q, k, v, "bf16", True, 0, None)
+    for t in (1, 64, 1024, 1025, S):
+        lens = np.array([t, t], dtype=np.int32)
+        Od, Ld = run_decode(np.ascontiguousarray(q[:, :, t - 1]), k, v, lens, "bf16")
+        np.testing.assert_allclose(Od, Op[:, :, t - 1], atol=2e-2)
+        np.testing.assert_allclose(Ld, Lp[:, :, t - 1], atol=2e-3)
+
+
+def test_decode_deterministic_and_workspace_checked():
+    lens, q, kc, vc = workloads.decode_inputs(8, 32, 8, 128, 4096, 1, 4096, seed=4)
+    O1, L1 = run_decode(q, kc, vc, lens, "bf16")
+    O2, L2 = run_decode(q, kc, vc, lens, "bf16")
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    dev = device()
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+    tl = torch.from_numpy(lens).to(dev)
+    O = torch.empty_like(tq)
+    small = torch.empty(64, dtype=torch.uint8, device=dev)
+    with pytest.raises(tch.AttnError) as e:
+        tch.attn_decode(tq, tk, tv, tl, O, None, small)
+    assert e.value.status == tch.ATTN_EWORKSPACE

@@ -1,0 +1,85 @@
+// C ABI of libattn.so: argument validation, kernel choice, launch.
+// Every check runs on the host before anything is enqueued.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+bool positive(int x) { return x > 0; }
+
+int validate_common(int B, int Nq, int Nkv, int Dh, int dtype) {
+  if (!positive(B) || !positive(Nq) || !positive(Nkv) || !positive(Dh)) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_EUNSUPPORTED;
+  if (Nq % Nkv != 0) return ATTN_EGQA;
+  if (Dh > 256) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                 int Nq, int Nkv, int S, int Dh, int causal, int window, float scale,
+                 int dtype, void* stream) {
+  if (!Q || !K || !V || !O) return ATTN_EINVAL;
+  int st = validate_common(B, Nq, Nkv, Dh, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive(S)) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  if (window < 0) window = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16 && Dh == 128)
+    return from_hip(attn::launch_prefill_bf16_d128(Q, K, V, O, LSE, B, Nq, Nkv, S, causal,
+                                                   window, scale, s));
+  return from_hip(attn::launch_rows_general(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
+                                            causal, window, scale, dtype == ATTN_BF16, s));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int dtype) {
+  if (validate_common(B, Nq, Nkv, Dh, dtype) != ATTN_OK || !positive(Tcap)) return 0;
+  if (dtype == ATTN_BF16 && Dh == 128 && attn::decode_bf16_d128_supported(Nq, Nkv))
+    return attn::decode_bf16_d128_workspace(B, Nq, Nkv, Tcap);
+  return 0;
+}
+
+int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
+                void* O, int B, int Nq, int Nkv, int Dh, int Tcap, float* LSE, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
+  int st = validate_common(B, Nq, Nkv, Dh, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive(Tcap)) return ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
+    return from_hip(attn::launch_decode_bf16_d128(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv,
+                                                  Tcap, workspace, s));
+  }
+  return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap,
+                                            lens, 1, 0, 1.0f / sqrtf((float)Dh),
+                                            dtype == ATTN_BF16, s));
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument (null pointer, non-positive size, bad flag or scale)";
+    case ATTN_EGQA: return "number of query heads is not a multiple of the number of K/V heads";
+    case ATTN_EUNSUPPORTED: return "unsupported element type or head size";
+    case ATTN_EWORKSPACE: return "decode workspace missing or too small";
+    case ATTN_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// General attention row kernel: one wavefront computes one output row with a
+// streaming (running max, running sum) softmax.  It covers fp32 inputs, head
+// sizes other than 128, and decode shapes the MFMA kernels do not take.  It
+// is correct for every supported shape but not tuned: each key costs a
+// wavefront-wide dot-product reduction.
+//
+// Definition followed: softmax(q K^T * scale + M) V for one query row
+// (textbook attention chapter, "Scaled dot-product attention"), with the
+// causal / window visibility of sections "Маскирование" and "Скользящее окно"
+// (visible iff j <= i and i - j < window), and the decode row of section
+// "Prefill и decode" (the new query sees every cached key).
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+struct RowParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int B, Nq, Nkv, S, Dh, kv_rows;
+  const int32_t* lens;
+  int causal, window;
+  float scale;
+  long long n_rows;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n_rows) return;
+
+  const T* Q = static_cast<const T*>(p.Q);
+  const T* K = static_cast<const T*>(p.K);
+  const T* V = static_cast<const T*>(p.V);
+  T* O = static_cast<T*>(p.O);
+  const int G = p.Nq / p.Nkv;
+
+  int b, h, i, lo, hi;
+  if (p.lens == nullptr) {  // prefill row (b, h, i)
+    i = (int)(row % p.S);
+    const long long bh = row / p.S;
+    h = (int)(bh % p.Nq);
+    b = (int)(bh / p.Nq);
+    hi = p.causal ? i + 1 : p.S;
+    lo = (p.causal && p.window > 0) ? max(0, i - p.window + 1) : 0;
+  } else {  // decode row (b, h): keys 0 .. lens[b]-1
+    i = 0;
+    h = (int)(row % p.Nq);
+    b = (int)(row / p.Nq);
+    lo = 0;
+    hi = min(p.lens[b], p.kv_rows);
+  }
+  const int g = h / G;
+  const size_t qoff = (((size_t)b * p.Nq + h) * (p.lens ? 1 : p.S) + i) * p.Dh;
+  const size_t kvoff = ((size_t)b * p.Nkv + g) * (size_t)p.kv_rows * p.Dh;
+
+  float q[4], o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = lane + 64 * u;
+    q[u] = d < p.Dh ? to_float(Q[qoff + d]) : 0.f;
+    o[u] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = lo; j < hi; ++j) {
+    const size_t r = kvoff + (size_t)j * p.Dh;
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d < p.Dh) part = __builtin_fmaf(q[u], to_float(K[r + d]), part);
+    }
+    const float s = wave_sum(part) * p.scale;
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);  // m = -inf on the first key -> 0
+    const float e = expf(s - m_new);
+    l = l * alpha + e;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      const float v = d < p.Dh ? to_float(V[r + d]) : 0.f;
+      o[u] = __builtin_fmaf(e, v, o[u] * alpha);
+    }
+    m = m_new;
+  }
+  // hi <= lo (decode length below 1) leaves l = 0: the row becomes 0/0 = NaN
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = lane + 64 * u;
+    if (d < p.Dh) O[qoff + d] = from_float<T>(o[u] * inv);
+  }
+  if (p.LSE != nullptr && lane == 0) p.LSE[row] = m + logf(l);
+}
+
+}  // namespace
+
+hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void* O,
+                               float* LSE, int B, int Nq, int Nkv, int S, int Dh,
+                               int kv_rows, const int32_t* lens, int causal, int window,
+                               float scale, int is_bf16, hipStream_t stream) {
+  RowParams p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.LSE = LSE;
+  p.B = B;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.S = S;
+  p.Dh = Dh;
+  p.kv_rows = kv_rows;
+  p.lens = lens;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  p.n_rows = (long long)B * Nq * (lens ? 1 : S);
+  const long long nblocks = (p.n_rows + 3) / 4;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (is_bf16)
+    hipLaunchKernelGGL(rows_kernel<__bf16>, dim3((unsigned)nblocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(rows_kernel<float>, dim3((unsigned)nblocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -7,17 +7,25 @@ bfloat16 round-to-nearest-even, NaN poisoning of unused cache slots, row
 sampling, and the closed-form work counts used to express throughput.
 
 Recipe (all draws from ``numpy.random.default_rng``):
-  * prefill: seed 0; Q, K, V drawn in that order as float32 standard normals of
-    shape [B,Nq,S,Dh], [B,Nkv,S,Dh], [B,Nkv,S,Dh]; bf16 workloads round each
-    float32 to the nearest bfloat16 (ties to even).  The oracle sees the same
-    rounded values widened to float64.
-  * decode: seed 0; first the cached lengths lens[B] uniform on [lo, hi]
-    (both ends included), then q [B,Nq,Dh], then per sequence b the valid
-    cache part K[b, :, :lens[b]] followed by V[b, :, :lens[b]]; cache slots at
-    or past lens[b] hold NaN so that any read beyond the length shows up.
+  * a tensor is filled in row-major order by consecutive blocks of 2^20
+    float32 standard normals; block i of tensor stream t under seed s comes
+    from ``default_rng([s, t, i])``, so the values do not depend on how many
+    threads fill the blocks; bf16 tensors round each float32 to the nearest
+    bfloat16 (ties to even).  The oracle sees the same rounded values widened
+    to float64.
+  * prefill: seed 0; Q, K, V are streams 0, 1, 2 with shapes [B,Nq,S,Dh],
+    [B,Nkv,S,Dh], [B,Nkv,S,Dh].
+  * decode: seed 0; first the cached lengths lens[B] = default_rng(seed)
+    .integers(lo, hi, B, endpoint=True); q is stream 10; the valid part
+    K[b, :, :lens[b]] of sequence b is stream 1000 + b and V[b, :, :lens[b]]
+    is stream 2000 + b (each an [Nkv, lens[b], Dh] block); cache slots at or
+    past lens[b] hold NaN so that any read beyond the length shows up.
   * sampled output rows of the long workloads: seed 1, n draws of (b, h, i)
     with b, h, i drawn in that order per component, plus forced rows.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -46,12 +54,20 @@ WORKLOADS = {
 BF16_NAN_BITS = 0x7FC0
 
 
+BLOCK = 1 << 20
+_THREADS = min(16, os.cpu_count() or 1)
+
+
 def f32_to_bf16_bits(x):
     """Round float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
-    out = ((u + bias) >> 16).astype(np.uint16)
+    u = x.reshape(-1).view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    out = t.astype(np.uint16).reshape(x.shape)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = BF16_NAN_BITS
@@ -90,17 +106,32 @@ def from_torch(t, dtype):
     return t.numpy().astype(np.float32)
 
 
-def _draw(rng, shape, dtype):
-    x = rng.standard_normal(shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+def _fill_block(flat, seed, stream, i, dtype):
+    lo = i * BLOCK
+    n = min(BLOCK, flat.size - lo)
+    x = np.random.default_rng([seed, stream, i]).standard_normal(n, dtype=np.float32)
+    flat[lo:lo + n] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def draw(shape, dtype, seed, stream, pool=None):
+    """One seeded N(0,1) tensor (bf16 bits or float32), filled block by block."""
+    out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    flat = out.reshape(-1)
+    nblocks = (flat.size + BLOCK - 1) // BLOCK
+    if pool is None or nblocks == 1:
+        for i in range(nblocks):
+            _fill_block(flat, seed, stream, i, dtype)
+    else:
+        list(pool.map(lambda i: _fill_block(flat, seed, stream, i, dtype), range(nblocks)))
+    return out
 
 
 def prefill_inputs(B, Nq, Nkv, S, Dh, dtype, seed=0):
     """Q, K, V for a prefill workload, stored as bf16 bits or float32."""
-    rng = np.random.default_rng(seed)
-    q = _draw(rng, (B, Nq, S, Dh), dtype)
-    k = _draw(rng, (B, Nkv, S, Dh), dtype)
-    v = _draw(rng, (B, Nkv, S, Dh), dtype)
+    with ThreadPoolExecutor(_THREADS) as pool:
+        q = draw((B, Nq, S, Dh), dtype, seed, 0, pool)
+        k = draw((B, Nkv, S, Dh), dtype, seed, 1, pool)
+        v = draw((B, Nkv, S, Dh), dtype, seed, 2, pool)
     return q, k, v
 
 
@@ -116,17 +147,24 @@ def decode_inputs(B, Nq, Nkv, Dh, Tcap, len_lo, len_hi, dtype="bf16", seed=0,
     lens = np.asarray(lens, dtype=np.int64)
     if lens.shape != (B,) or lens.min() < 1 or lens.max() > Tcap:
         raise ValueError("lens must be [B] within [1, Tcap]")
-    q = _draw(rng, (B, Nq, Dh), dtype)
+    q = draw((B, Nq, Dh), dtype, seed, 10)
     if dtype == "bf16":
-        kc = np.full((B, Nkv, Tcap, Dh), BF16_NAN_BITS, dtype=np.uint16)
-        vc = np.full((B, Nkv, Tcap, Dh), BF16_NAN_BITS, dtype=np.uint16)
+        kc = np.empty((B, Nkv, Tcap, Dh), dtype=np.uint16)
+        vc = np.empty((B, Nkv, Tcap, Dh), dtype=np.uint16)
+        poison = BF16_NAN_BITS
     else:
-        kc = np.full((B, Nkv, Tcap, Dh), np.nan, dtype=np.float32)
-        vc = np.full((B, Nkv, Tcap, Dh), np.nan, dtype=np.float32)
-    for b in range(B):
+        kc = np.empty((B, Nkv, Tcap, Dh), dtype=np.float32)
+        vc = np.empty((B, Nkv, Tcap, Dh), dtype=np.float32)
+        poison = np.nan
+
+    def one(b):
         n = int(lens[b])
-        kc[b, :, :n] = _draw(rng, (Nkv, n, Dh), dtype)
-        vc[b, :, :n] = _draw(rng, (Nkv, n, Dh), dtype)
+        for cache, stream in ((kc, 1000 + b), (vc, 2000 + b)):
+            cache[b, :, :n] = draw((Nkv, n, Dh), dtype, seed, stream)
+            cache[b, :, n:] = poison
+
+    with ThreadPoolExecutor(_THREADS) as pool:
+        list(pool.map(one, range(B)))
     return lens.astype(np.int32), q, kc, vc
 
 
