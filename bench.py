@@ -1,0 +1,194 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole path over one batch of synthetic input:
+  * causal multi-head prefill, bf16, B=1, 32 heads, S=32768, Dh=128
+    (the long-context workload; 8.796e12 algorithmic FLOPs per call), then
+  * one KV-cache decode step, bf16, 64 sequences, 32 query / 8 K/V heads,
+    Dh=128, cached lengths uniform in [1024, 32768].
+Inputs are seeded N(0,1) draws (see workloads/), resident in HBM before the
+timed region.  W untimed steps, then K timed steps bracketed by device
+synchronisation; kernel durations come from HIP events recorded on the stream
+the kernels are launched on.  Prints ONE JSON line:
+  value = prefill TFLOP/s (2 FLOP per multiply-add, visible pairs only),
+  decode = decode throughput in GB/s of compulsory HBM traffic,
+  roofline = the prefill kernel (the dominant one) against bf16 dense MFMA peak,
+  cpu_baseline = the float64 oracle on a bounded sample of the same prefill.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PREFILL = "mha_bf16_b1_h32_s32768_d128"
+DECODE = "decode_bf16_b64_h32kv8_t32768_d128"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+# HBM traffic of one prefill launch measured with rocprofv3 --pmc FETCH_SIZE /
+# WRITE_SIZE, scaled by the same counters on a copy of known size; valid only
+# for the kernel source it was taken on (sha256 of prefill_bf16.hip).
+TRAFFIC = {}
+
+
+def _kernel_sha():
+    p = os.path.join(ROOT, "transformer_causal_head_amd", "csrc", "prefill_bf16.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _cpu_baseline(q, k, v, cfg, budget_s=12.0):
+    """Time the float64 oracle on sampled prefill rows of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    heads = 4  # the sample is drawn from heads 0..3 of batch 0
+    S, Dh = cfg["S"], cfg["Dh"]
+    tr = sorted(workloads.sample_rows(1, heads, S, 65536, seed=1))
+    Qh = workloads.to_f64(q[:, :heads], "bf16")
+    Kh = workloads.to_f64(k[:, :heads], "bf16")
+    Vh = workloads.to_f64(v[:, :heads], "bf16")
+    done, flops, t0 = 0, 0, time.perf_counter()
+    while done < len(tr) and time.perf_counter() - t0 < budget_s:
+        part = tr[done:done + 256]
+        oracle.attention_rows_ref(Qh, Kh, Vh, part, causal=True, window=cfg["window"])
+        # causal row i without a window sees i + 1 keys: 4 * Dh FLOPs each
+        flops += sum(4 * Dh * (i + 1) for _, _, i in part)
+        done += len(part)
+    dt = time.perf_counter() - t0
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} seeded (head, row) pairs of heads 0-3, {dt:.1f} s, "
+                      f"float64 NumPy full score rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path runs without sharding or collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_causal_head_amd as tch
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2}))
+        return
+
+    pc = workloads.WORKLOADS[PREFILL]
+    dc = workloads.WORKLOADS[DECODE]
+    B, Nq, Nkv, S, Dh = pc["B"], pc["Nq"], pc["Nkv"], pc["S"], pc["Dh"]
+    print(f"generating inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+    O = torch.empty_like(tq)
+    LSE = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+    lens, dq, kc, vc = workloads.decode_inputs(dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"],
+                                               dc["Tcap"], dc["len_lo"], dc["len_hi"])
+    tdq, tkc, tvc = (workloads.to_torch(x, "bf16", dev) for x in (dq, kc, vc))
+    del kc, vc
+    tl = torch.from_numpy(lens).to(dev)
+    dO = torch.empty_like(tdq)
+    dL = torch.empty((dc["B"], dc["Nq"]), dtype=torch.float32, device=dev)
+    ws_bytes = tch.attn_decode_workspace_bytes(dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"],
+                                               dc["Tcap"], tch.ATTN_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"inputs resident", file=sys.stderr, flush=True)
+
+    scale = 1.0 / math.sqrt(Dh)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        tch.attn_prefill(tq, tk, tv, O, LSE, causal=1, window=0, scale=scale)
+        if e: e[1].record(stream)
+        if e: e[2].record(stream)
+        tch.attn_decode(tdq, tkc, tvc, tl, dO, dL, ws)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    pflops, pbytes = workloads.prefill_work(B, Nq, Nkv, S, Dh, True, 0, 2)
+    dflops, dbytes = workloads.decode_work(lens, dc["Nq"], dc["Nkv"], dc["Dh"], 2)
+    tflops = pflops / (pre_ms * 1e-3) / 1e12
+    gbs = dbytes / (dec_ms * 1e-3) / 1e9
+
+    sha = _kernel_sha()
+    traffic = TRAFFIC.get(sha)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = _cpu_baseline(q, k, v, pc)
+
+    line = {
+        "metric": "causal attn prefill TFLOP/s (bf16, Dh=128) + KV-cache decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{PREFILL} prefill + {DECODE} decode",
+                   "prefill": {"B": B, "Nq": Nq, "Nkv": Nkv, "S": S, "Dh": Dh,
+                               "causal": True, "window": 0},
+                   "decode": {"B": dc["B"], "Nq": dc["Nq"], "Nkv": dc["Nkv"], "Dh": dc["Dh"],
+                              "Tcap": dc["Tcap"], "sum_lens": int(lens.sum())},
+                   "parallelism": "single GPU"},
+        "prefill": {"ms": round(pre_ms, 4), "tflops": round(tflops, 2),
+                    "algorithmic_flop": pflops},
+        "decode": {"ms": round(dec_ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+                   "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": dbytes},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_kernel", "kernel_sha": sha},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
