@@ -12,38 +12,64 @@
 // O(T W d)).
 //
 // gfx950 design
-//   * Scores are computed transposed, S^T = K Q^T: the key index runs along
-//     MFMA rows (A operand from LDS), the query index along columns (B
-//     operand, Q kept in VGPRs for the whole kernel).  A lane then owns one
-//     query column, so the row max and row sum of the softmax are in-register
-//     reductions plus one exchange between the two 32-lane halves.
-//   * The S^T accumulator layout is exactly the B-operand layout the PV
-//     product needs (O^T = V^T P^T), so P goes from fp32 accumulator to bf16
-//     operand with one v_cvt_pk_bf16_f32 per pair and no lane exchange.
-//   * V is stored transposed in LDS with its keys permuted inside each group
-//     of 16 so that each lane's 8 keys of the V^T operand are one 16-byte
-//     LDS read.
-//   * One workgroup = 4 waves sharing each K/V tile: for grouped-query
-//     attention the waves take different query heads of the same K/V head, so
-//     a K/V tile is fetched once per group; for MHA they take consecutive
-//     query blocks of one head.
-//   * Workgroups are ordered longest-key-range first (causal work grows with
-//     the query position); with a multiple of 8 (batch, K/V head, head-group)
-//     combinations, all workgroups of one K/V head land on the same XCD and
-//     share its L2.
+//   * Scores are computed transposed, S^T = K Q^T: keys run along MFMA rows
+//     (A operand, from LDS), queries along columns (B operand, Q held in VGPRs
+//     for the whole kernel).  A lane owns one query column, so the softmax row
+//     max and row sum are in-register reductions plus one v_permlane32_swap.
+//   * The S^T accumulator layout is exactly the B-operand layout of the PV
+//     product O^T = V^T P^T, so P goes from fp32 accumulator to bf16 operand
+//     with v_cvt_pk_bf16_f32 and no lane exchange.
+//   * K and V tiles (64 keys x 256 B) are copied HBM -> LDS by the DMA path
+//     (global_load_lds_dwordx4): no VGPR staging, no VALU, double-buffered and
+//     issued one tile ahead, so the copy overlaps the math.  Rows are stored
+//     with a GF(2)-linear 16-byte-chunk swizzle that keeps both the 16-byte K
+//     reads and the transposing V reads free of bank conflicts.
+//   * V stays row-major in LDS; ds_read_b64_tr_b16 transposes it on the way
+//     into the V^T operand.
+//   * The next tile's QK^T is issued before this tile's softmax, so the matrix
+//     core works while the VALU computes exponentials.
+//   * Lazy rescale: the running maximum moves only when a new score exceeds it
+//     by more than TAU (log2 units).  Exponentials stay <= 2^TAU, and the
+//     accumulator is rescaled only on those rare moves.  The final O / l and
+//     the LSE are unchanged (both use the same reference maximum).
+//   * One workgroup = 4 waves sharing every K/V tile: for grouped-query
+//     attention the waves take different query heads of one K/V head, so a
+//     K/V tile is fetched once per group; for MHA they take consecutive query
+//     blocks of one head.
+//   * Workgroups run longest-key-range first; with a multiple of 8 (batch,
+//     K/V head, head-group) combinations all workgroups of one K/V head land
+//     on the same XCD and share its L2.
 
 #include "common.h"
 #include "kernels.h"
+
+// Variant knobs (compile-time): 32-query blocks per wave, waves per
+// workgroup, and whether the next tile's QK^T is issued before this tile's
+// softmax (needs a second score buffer).
+#ifndef PREFILL_QB
+#define PREFILL_QB 1
+#endif
+#ifndef PREFILL_NW
+#define PREFILL_NW 8
+#endif
+#ifndef PREFILL_PIPE
+#define PREFILL_PIPE 1
+#endif
 
 namespace attn {
 
 namespace {
 
-constexpr int D = 128;        // head size
-constexpr int NW = 4;         // waves per workgroup
-constexpr int BN = 64;        // keys per K/V tile
-constexpr int KSTR = D + 8;   // K tile row stride (bf16), 16-byte pad
-constexpr int VSTR = BN + 8;  // V^T tile row stride (bf16), 16-byte pad
+constexpr int D = 128;         // head size
+constexpr int NW = PREFILL_NW; // waves per workgroup
+constexpr int QB = PREFILL_QB; // 32-query blocks per wave
+constexpr bool PIPE = PREFILL_PIPE != 0;
+constexpr int BN = 64;         // keys per K/V tile
+constexpr int TILE = BN * D * 2;
+constexpr float TAU = 8.f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
   const __bf16* Q;
@@ -61,20 +87,82 @@ struct Params {
   int n_hsub;     // G / hp
 };
 
-// Position of key k (0..BN-1) inside a V^T row: bits 2 and 3 swapped, which
-// puts the 8 keys one lane feeds to a 16-key MFMA step next to each other.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 1) << 2) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (r & 8);
 }
 
-template <int QB>
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
+
+// Copy keys [k0, k0+64) of one head into a swizzled LDS tile.  The tile is 16
+// pieces of 1 KB (4 rows); each wave issues 16 / NW of them.  Rows past the end
+// repeat the last row; the mask gives them zero weight.
+__device__ __forceinline__ void load_tile(const __bf16* head, int k0, int S, char* tile, int w,
+                                          int lane) {
+#pragma unroll
+  for (int j = 0; j < 16 / NW; ++j) {
+    const int piece = w * (16 / NW) + j;
+    const int r = piece * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    const int row = min(k0 + r, S - 1);
+    __builtin_amdgcn_global_load_lds(head + (size_t)row * D + c * 8,
+                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int QB_>
+__device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
+                                        const bf16x8 (&qf)[QB_][8], f32x16 (&s)[QB_][2]) {
+#pragma unroll
+  for (int qb = 0; qb < QB_; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + kb * 8192 + koff[ks]);
+#pragma unroll
+      for (int qb = 0; qb < QB_; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
+    }
+}
+
+template <int QB_>
+__device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
+                                        const bf16x8 (&pf)[QB_][4], f32x16 (&o)[QB_][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 4096 + voff[0][db]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 4096 + voff[1][db]));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB_; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][db], 0, 0, 0);
+    }
+}
+
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   constexpr int QW = 32 * QB;  // queries per wave
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VSTR];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int ln = lane & 31;
   const int hl = lane >> 5;
@@ -96,17 +184,51 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int wq1 = min(p.S, qa + QW);
   const bool wave_live = qa < p.S;
 
-  const size_t kv_base = ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
+  const __bf16* Kh = p.K + ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
+  const __bf16* Vh = p.V + ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
   const size_t q_base = ((size_t)b * p.Nq + head) * (size_t)p.S * D;
+
+  // key range of the workgroup
+  const int hi_key = p.causal ? q1 : p.S;
+  const int lo_key = (p.causal && p.window > 0) ? max(0, q0 - p.window + 1) : 0;
+  const int t_lo = lo_key / BN;
+  const int nt = (hi_key + BN - 1) / BN - t_lo;
+
+  char* const K0 = smem;
+  char* const K1 = smem + TILE;
+  char* const V0 = smem + 2 * TILE;
+  char* const V1 = smem + 3 * TILE;
+
+  // start the copies first, they overlap the set-up below
+  load_tile(Kh, t_lo * BN, p.S, K0, w, lane);
+  load_tile(Vh, t_lo * BN, p.S, V0, w, lane);
+  if (PIPE && nt > 1) load_tile(Kh, (t_lo + 1) * BN, p.S, K1, w, lane);
 
   // Q^T operand fragments: query column ln of block qb, d = 16*ks + 8*hl + i
   bf16x8 qf[QB][8];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    int qrow = min(qa + qb * 32 + ln, p.S - 1);
+    const int qrow = min(qa + qb * 32 + ln, p.S - 1);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.Q + q_base + (size_t)qrow * D + hl * 8);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = src[ks * 2];
+  }
+
+  // LDS byte offsets inside a tile
+  int koff[8];  // K operand: row ln (+32*kb), chunk 2*ks + hl
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = ln * 256 + (((2 * ks + hl) ^ swz(ln)) << 4);
+  int voff[2][4];  // V^T operand through the transposing read
+  {
+    const int gq = lane >> 4, j = lane & 15;
+    const int h = gq >> 1, dpart = gq & 1, ip = j >> 2, u = j & 3;
+#pragma unroll
+    for (int ih = 0; ih < 2; ++ih) {
+      const int r = 8 * ih + 4 * h + ip;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        voff[ih][db] = r * 256 + (((4 * db + 2 * dpart + (u >> 1)) ^ swz(r)) << 4) + (u & 1) * 8;
+    }
   }
 
   f32x16 oacc[QB][4];
@@ -119,145 +241,123 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
   }
 
-  // key range of the workgroup
-  const int hi = p.causal ? q1 : p.S;
-  const int lo = (p.causal && p.window > 0) ? max(0, q0 - p.window + 1) : 0;
-  const int t_lo = lo / BN;
-  const int t_hi = (hi + BN - 1) / BN;
-
-  // tile loader mapping: thread -> keys 4*kg..4*kg+3, d = 8*dc..8*dc+7
-  const int kg = tid >> 4;
-  const int dc = tid & 15;
-
-  for (int t = t_lo; t < t_hi; ++t) {
+  // does this wave see any (query, key) pair of tile t?
+  auto live = [&](int t) {
     const int k0 = t * BN;
-    __syncthreads();
-    {
-      u32x4 kv[4], vv[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int key = k0 + kg * 4 + c;
-        if (key < p.S) {
-          size_t off = kv_base + (size_t)key * D + dc * 8;
-          kv[c] = *reinterpret_cast<const u32x4*>(p.K + off);
-          vv[c] = *reinterpret_cast<const u32x4*>(p.V + off);
-        } else {
-          kv[c] = u32x4{0, 0, 0, 0};
-          vv[c] = u32x4{0, 0, 0, 0};
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<u32x4*>(&Ks[(kg * 4 + c) * KSTR + dc * 8]) = kv[c];
-      const int kpos = vt_pos(kg * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = e >> 1;
-        uint32_t w01, w23;
-        if (e & 1) {
-          w01 = (vv[0][j] >> 16) | (vv[1][j] & 0xffff0000u);
-          w23 = (vv[2][j] >> 16) | (vv[3][j] & 0xffff0000u);
-        } else {
-          w01 = (vv[0][j] & 0xffffu) | (vv[1][j] << 16);
-          w23 = (vv[2][j] & 0xffffu) | (vv[3][j] << 16);
-        }
-        *reinterpret_cast<u32x2*>(&Vt[(dc * 8 + e) * VSTR + kpos]) = u32x2{w01, w23};
-      }
-    }
-    __syncthreads();
+    bool ok = wave_live;
+    if (p.causal) ok = ok && (k0 <= wq1 - 1);
+    if (p.window > 0) ok = ok && (k0 + BN - 1 >= qa - p.window + 1);
+    return ok;
+  };
 
-    // does this wave see any (query, key) pair of the tile?
-    bool live = wave_live;
-    if (p.causal) live = live && (k0 <= wq1 - 1);
-    if (p.window > 0) live = live && (k0 + BN - 1 >= qa - p.window + 1);
-    if (!live) continue;
+  auto softmax_pv = [&](int t, f32x16 (&s)[QB][2], const char* Vt) {
+    const int k0 = t * BN;
     bool need_mask = (k0 + BN > p.S);
     if (p.causal) need_mask = need_mask || (k0 + BN - 1 > qa);
     if (p.window > 0) need_mask = need_mask || (wq1 - 1 - k0 >= p.window);
-
-    // S^T = K Q^T for the tile
-    f32x16 sacc[QB][BN / 32];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) sacc[qb][kb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + ln) * KSTR + ks * 16 + hl * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], sacc[qb][kb], 0, 0, 0);
-      }
-    }
-
-    // mask: accumulator register r of key block kb holds key
-    // k0 + 32*kb + 8*(r/4) + 4*hl + (r%4) for query column ln
     if (need_mask) {
+      // accumulator register r of key block kb holds key
+      // k0 + 32*kb + 8*(r/4) + 4*hl + (r%4) for query column ln
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qi = qa + qb * 32 + ln;
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
             bool ok = kj < p.S;
             if (p.causal) ok = ok && (kj <= qi);
             if (p.window > 0) ok = ok && (qi - kj < p.window);
-            if (!ok) sacc[qb][kb][r] = -INFINITY;
+            if (!ok) s[qb][kb][r] = -INFINITY;
           }
       }
     }
-
-    // online softmax per query column, then P^T operand fragments
-    bf16x8 pf[QB][BN / 16];
+    bf16x8 pf[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run[qb], mx * p.c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run[qb] - m_use);
-      m_run[qb] = m_new;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      const float m_cand = xhalf_max(mx) * p.c;
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run[qb] + TAU)) {
+        const float m_new = fmaxf(m_run[qb], m_cand);
+        const float alpha = exp2_fast(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[qb][db] *= alpha;
+      }
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = exp2_fast(__builtin_fmaf(sacc[qb][kb][r], p.c, -m_use));
-          sacc[qb][kb][r] = e;
+          const float e = exp2_fast(__builtin_fmaf(s[qb][kb][r], p.c, -m_use));
+          s[qb][kb][r] = e;
           rs += e;
         }
-      l_run[qb] = l_run[qb] * alpha + rs;
+      l_run[qb] += rs;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[qb][db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           u32x4 pk;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            pk[j] = pack_bf16x2(sacc[qb][kb][kk * 8 + 2 * j], sacc[qb][kb][kk * 8 + 2 * j + 1]);
+            pk[j] = pack_bf16x2(s[qb][kb][kk * 8 + 2 * j], s[qb][kb][kk * 8 + 2 * j + 1]);
           pf[qb][kb * 2 + kk] = __builtin_bit_cast(bf16x8, pk);
         }
     }
+    pv_tile<QB>(Vt, voff, pf, oacc);
+  };
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(db * 32 + ln) * VSTR + ks * 16 + hl * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][ks], oacc[qb][db], 0, 0, 0);
+  if constexpr (PIPE) {
+    f32x16 sa[QB][2], sb[QB][2];
+    wait_dma();
+    __syncthreads();
+    if (live(t_lo)) qk_tile<QB>(K0, koff, qf, sa);
+
+    // iteration i (tile t = t_lo + i): S(t) is in registers, K(t+1) and V(t)
+    // are in LDS; the copies of K(t+2) and V(t+1) are issued at the top.
+    auto iteration = [&](int i, f32x16 (&s_cur)[QB][2], f32x16 (&s_next)[QB][2]) {
+      const int t = t_lo + i;
+      char* const Kcur = (i & 1) ? K1 : K0;   // holds K(t), free after the barrier
+      char* const Knext = (i & 1) ? K0 : K1;  // holds K(t+1)
+      char* const Vcur = (i & 1) ? V1 : V0;   // holds V(t)
+      char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
+      wait_dma();
+      __syncthreads();
+      if (i + 2 < nt) load_tile(Kh, (t + 2) * BN, p.S, Kcur, w, lane);
+      if (i + 1 < nt) load_tile(Vh, (t + 1) * BN, p.S, Vnext, w, lane);
+      if (i + 1 < nt && live(t + 1)) qk_tile<QB>(Knext, koff, qf, s_next);
+      if (live(t)) softmax_pv(t, s_cur, Vcur);
+    };
+
+    int i = 0;
+    for (; i + 1 < nt; i += 2) {
+      iteration(i, sa, sb);
+      iteration(i + 1, sb, sa);
+    }
+    if (i < nt) iteration(i, sa, sb);
+  } else {
+    // iteration i (tile t): K(t), V(t) are in LDS; K(t+1), V(t+1) are copied
+    // into the other stage while tile t is computed.
+    f32x16 s[QB][2];
+    for (int i = 0; i < nt; ++i) {
+      const int t = t_lo + i;
+      wait_dma();
+      __syncthreads();
+      if (i + 1 < nt) {
+        load_tile(Kh, (t + 1) * BN, p.S, (i & 1) ? K0 : K1, w, lane);
+        load_tile(Vh, (t + 1) * BN, p.S, (i & 1) ? V0 : V1, w, lane);
+      }
+      if (live(t)) {
+        qk_tile<QB>((i & 1) ? K1 : K0, koff, qf, s);
+        softmax_pv(t, s, (i & 1) ? V1 : V0);
       }
     }
   }
@@ -267,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qa + qb * 32 + ln;
-    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    const float l_tot = xhalf_sum(l_run[qb]);
     if (qi >= p.S) continue;
     const float inv = 1.f / l_tot;
     __bf16* orow = p.O + q_base + (size_t)qi * D;
@@ -291,7 +391,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
                                     float* LSE, int B, int Nq, int Nkv, int S, int causal,
                                     int window, float scale, hipStream_t stream) {
-  constexpr int QB = 2;
   Params p;
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
@@ -312,7 +411,7 @@ hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V,
   p.n_qtiles = (S + p.qspan - 1) / p.qspan;
   const long long nblocks = (long long)p.n_qtiles * B * Nkv * p.n_hsub;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel<QB>, dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
