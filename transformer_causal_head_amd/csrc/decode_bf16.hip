@@ -6,20 +6,25 @@
 // K/V head) is cut into chunks of kDecodeChunk keys; each chunk yields a
 // partial (running max m, running sum l, unnormalised output o) for the G
 // query heads that share the K/V head, and a second kernel merges the
-// partials with the same rescaling identity the online softmax uses
-// (the Chinese post's Flash Attention section: rescale by exp(m_old - m_new)).
+// partials with the same rescaling identity the online softmax uses (the
+// Chinese post's Flash Attention section: rescale by exp(m_old - m_new)).
 //
 // gfx950 design
-//   * Chunks past a sequence's length exit at once, so the work follows the
-//     ragged lengths and fills the chip (thousands of workgroups).
-//   * K rows stream straight from HBM into MFMA B operands
-//     (v_mfma_f32_16x16x32_bf16, query heads on the M axis); every K byte is
-//     read once per K/V head and shared by its G query heads.
-//   * The probabilities go through a per-wave LDS slot and the PV update is
-//     a VALU FMA stream over 16-byte V loads (8 head-dims per lane, 4 keys
-//     per wavefront instruction), so V is read row-major and coalesced.
-//   * Rows at or beyond the length are never read: loads clamp to the last
-//     valid row and those keys get probability 0.
+//   * One wavefront per (sequence, K/V head, chunk); chunks past a sequence's
+//     length exit at once, so the work follows the ragged lengths and fills
+//     the chip with thousands of small workgroups.
+//   * The chunk streams in steps of 32 keys.  K rows are loaded into VGPRs two
+//     steps ahead; V rows are copied HBM -> LDS by the DMA path
+//     (global_load_lds_dwordx4) into a wave-private double buffer, also two
+//     steps ahead, so ~16 KB per wave stay in flight without VGPR cost.
+//   * Both products run on v_mfma_f32_16x16x32_bf16 in the transposed form of
+//     the prefill kernel: S^T = K q^T (keys on M, the G query heads on N), and
+//     O^T = V^T P^T, whose B operand is the S^T accumulator layout.  V is
+//     transposed on its way out of LDS by ds_read_b64_tr_b16; a row-bit
+//     rotation swizzle keeps those reads bank-conflict free.
+//   * Every K and V byte is read once per K/V head and shared by its G query
+//     heads.  Rows at or past the length are never read: addresses clamp to
+//     the last valid row and those keys get probability 0.
 
 #include "common.h"
 #include "kernels.h"
@@ -29,9 +34,14 @@ namespace attn {
 namespace {
 
 constexpr int D = 128;
-constexpr int CH = kDecodeChunk;   // keys per workgroup
-constexpr int WKEYS = CH / 4;      // keys per wave
-constexpr int STEP = 64;           // keys per inner step
+constexpr int CH = kDecodeChunk;  // keys per workgroup (one wavefront)
+constexpr int STEP = 32;          // keys per pipeline step
+constexpr int NS = CH / STEP;     // steps per chunk (fully unrolled)
+constexpr int STAGE = STEP * D * 2;  // bytes of V per step
+constexpr float TAU = 8.f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct DecParams {
   const __bf16* q;
@@ -42,193 +52,200 @@ struct DecParams {
   float* LSE;
   float* ws_o;    // [B, Nkv, n_chunks, G, D] unnormalised partial outputs
   float* ws_ml;   // [B, Nkv, n_chunks, G, 2]  (m in log2 units, l)
-  int B, Nq, Nkv, Tcap, n_chunks;
+  int B, Nq, Nkv, G, Tcap, n_chunks;
   float c;        // scale * log2(e)
 };
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// 16-byte chunk c of V row r sits at chunk position c ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return ((r << 1) & 14) | ((r >> 3) & 1); }
+
+// V rows [k0, k0+32) -> one LDS stage (8 pieces of 4 rows); rows are clamped
+// to the last valid one.
+__device__ __forceinline__ void load_v(const __bf16* head, int k0, int last, char* stage,
+                                       int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = j * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    const int row = min(k0 + r, last);
+    __builtin_amdgcn_global_load_lds(head + (size_t)row * D + c * 8,
+                                     (lds_void*)(stage + j * 1024), 16, 0, 0);
+  }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecParams p) {
-  static_assert(G >= 1 && G <= 8, "query heads per K/V head");
-  __shared__ float pbuf[4][STEP][G];
-  __shared__ float abuf[4][G];
-  __shared__ float ob[4][G][D];
-  __shared__ float mlb[4][G][2];
+// K operand for two 16-key blocks: lane (grp, l16) holds
+// K[k0 + 16*kb + l16][32*ks + 8*grp .. +7]
+__device__ __forceinline__ void load_k(const __bf16* head, int k0, int last, int l16, int grp,
+                                       bf16x8 (&kr)[2][4]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = min(k0 + kb * 16 + l16, last);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(head + (size_t)row * D + grp * 8);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kr[kb][ks] = src[ks * 4];
+  }
+}
+
+template <int VMCNT>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VMCNT == 0 || VMCNT == 16, "encoded counts");
+  if constexpr (VMCNT == 0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  else
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+}
+
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
+  // two separate LDS objects, so the compiler can tell that a DMA copy into
+  // one stage never aliases the transposing reads of the other
+  __shared__ __attribute__((aligned(1024))) char vs0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char vs1[STAGE];
 
   const int chunk = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int n = min(p.lens[b], p.Tcap);
-  if (chunk * CH >= n) return;
+  const int c0 = chunk * CH;
+  if (c0 >= n) return;
+  const int nsteps = (min(CH, n - c0) + STEP - 1) / STEP;
+  // prefetches run past the chunk's last step with addresses clamped to the
+  // chunk's last row: the loop body stays uniform and the extra copies hit L2
+  const int last = min(n, c0 + CH) - 1;
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x;
   const int l16 = lane & 15;
   const int grp = lane >> 4;
+  const int G = p.G;
 
-  const size_t kv_base = ((size_t)b * p.Nkv + g) * (size_t)p.Tcap * D;
+  const size_t kvh = ((size_t)b * p.Nkv + g) * (size_t)p.Tcap * D;
+  const __bf16* Kh = p.K + kvh;
+  const __bf16* Vh = p.V + kvh;
 
-  // A operand: q[head = l16][d = 32*ks + 8*grp + i], zero rows past G
-  bf16x8 qa[4];
+  // q^T operand: lane (grp, l16) holds q[head g*G + l16][32*ks + 8*grp + i]
+  bf16x8 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (l16 < G) {
       const __bf16* src = p.q + ((size_t)b * p.Nq + (size_t)g * G + l16) * D + ks * 32 + grp * 8;
-      qa[ks] = *reinterpret_cast<const bf16x8*>(src);
+      qf[ks] = *reinterpret_cast<const bf16x8*>(src);
     } else {
-      qa[ks] = bf16x8{};
+      qf[ks] = bf16x8{};
     }
   }
 
-  // running stats of head hh = 4*grp + r (valid for hh < G), replicated over
-  // the 16 lanes of the group
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
-  float o[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  // copies in flight, oldest first: q, K(0), V(0), K(1), V(1); vmcnt(16)
+  // before a step therefore means that step's K and V have landed
+  bf16x8 kr[2][2][4];
+  load_k(Kh, c0, last, l16, grp, kr[0]);
+  load_v(Vh, c0, last, vs0, lane);
+  load_k(Kh, c0 + STEP, last, l16, grp, kr[1]);
+  load_v(Vh, c0 + STEP, last, vs1, lane);
 
-  const int wk0 = chunk * CH + w * WKEYS;
-  for (int s = 0; s < WKEYS / STEP; ++s) {
-    const int k0 = wk0 + s * STEP;
-    if (k0 >= n) break;
-
-    // scores S[head][key] for 4 groups of 16 keys
-    f32x4 acc[4];
+  // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
+  // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
+  int voff[2][8];
+  {
+    const int ip = l16 >> 2, u = l16 & 3;
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      const int key = min(k0 + kg * 16 + l16, n - 1);
-      const __bf16* src = p.K + kv_base + (size_t)key * D + grp * 8;
-      acc[kg] = f32x4{};
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 16 * hf + 4 * grp + ip;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 kb = *reinterpret_cast<const bf16x8*>(src + ks * 32);
-        acc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc[kg], 0, 0, 0);
-      }
+      for (int db = 0; db < 8; ++db)
+        voff[hf][db] = r * 256 + (((2 * db + (u >> 1)) ^ swz(r)) << 4) + (u & 1) * 8;
     }
-    // acc[kg][r] at lane (grp, l16): head 4*grp + r, key k0 + 16*kg + l16
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg)
-      if (k0 + kg * 16 + l16 >= n) acc[kg] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
 
+  f32x4 o[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mx = fmaxf(fmaxf(acc[0][r], acc[1][r]), fmaxf(acc[2][r], acc[3][r]));
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto step = [&](int s, bf16x8 (&kr)[2][4], const char* vst) {
+    const int k0 = c0 + s * STEP;
+    // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
+    // query column l16
+    f32x4 sc[2];
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-      const float m_new = fmaxf(m_run[r], mx * p.c);
-      const float alpha = exp2_fast(m_run[r] - m_new);  // k0 < n: m_new is finite
-      m_run[r] = m_new;
-      float rs = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x4{};
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
-        const float e = exp2_fast(__builtin_fmaf(acc[kg][r], p.c, -m_new));
-        acc[kg][r] = e;
+      for (int ks = 0; ks < 4; ++ks)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kb][ks], qf[ks], sc[kb], 0, 0, 0);
+    }
+    if (k0 + STEP > n) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + kb * 16 + grp * 4 + r >= n) sc[kb][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_cand = mx * p.c;  // the step's first key is valid: finite
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = exp2_fast(__builtin_fmaf(sc[kb][r], p.c, -m_run));
+        sc[kb][r] = e;
         rs += e;
       }
-      l_run[r] = l_run[r] * alpha + rs;
-      const int hh = grp * 4 + r;
-      if (hh < G) {
+    l_run += rs;
+    u32x4 pk;
+    pk[0] = pack_bf16x2(sc[0][0], sc[0][1]);
+    pk[1] = pack_bf16x2(sc[0][2], sc[0][3]);
+    pk[2] = pack_bf16x2(sc[1][0], sc[1][1]);
+    pk[3] = pack_bf16x2(sc[1][2], sc[1][3]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) pbuf[w][kg * 16 + l16][hh] = acc[kg][r];
-        if (l16 == 0) abuf[w][hh] = alpha;
-      }
+    for (int db = 0; db < 8; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[db], 0, 0, 0);
     }
-    wave_sync_lds();
+  };
 
-    // PV: lane (grp, l16) takes keys k0 + 4*t + grp and head-dims 8*l16 .. +7
-    float al[G];
+  // Fully unrolled: step s reads K registers kr[s & 1] and V stage s & 1, and
+  // the copies for step s + 2 go into them right after.  Every copy is issued
+  // unconditionally (addresses clamp inside the chunk), so the outstanding
+  // count before each step is a compile-time constant.
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) al[hh] = abuf[w][hh];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] *= al[hh];
-#pragma unroll 4
-    for (int t = 0; t < STEP / 4; ++t) {
-      const int kl = t * 4 + grp;
-      const int key = min(k0 + kl, n - 1);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(p.V + kv_base + (size_t)key * D + l16 * 8);
-      float vf[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[2 * j] = bf16_lo(vv[j]);
-        vf[2 * j + 1] = bf16_hi(vv[j]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float pr = pbuf[w][kl][hh];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = __builtin_fmaf(pr, vf[e], o[hh][e]);
-      }
+  for (int s = 0; s < NS; ++s) {
+    if (s + 1 < NS) wait_vm<16>(); else wait_vm<0>();
+    if (s < nsteps) step(s, kr[s & 1], (s & 1) ? vs1 : vs0);
+    if (s + 2 < NS) {
+      load_k(Kh, c0 + (s + 2) * STEP, last, l16, grp, kr[s & 1]);
+      load_v(Vh, c0 + (s + 2) * STEP, last, (s & 1) ? vs1 : vs0, lane);
     }
-    wave_sync_lds();
   }
+  wait_vm<0>();  // no copy may still target LDS when the wave ends
 
-  // reduce the wave: o over the 4 key subsets, l over the 16 lanes of a group
+  // partial of this chunk: O^T register r of block db is d = 16*db + 4*grp + r
+  // of query column l16
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (l16 < G) {
+    const size_t part = (((size_t)b * p.Nkv + g) * p.n_chunks + chunk) * G + l16;
+    float* dst = p.ws_o + part * D + 4 * grp;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[hh][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      o[hh][e] = v;
-    }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float v = l_run[r];
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    l_run[r] = v;
-  }
-  if (grp == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ob[w][hh][l16 * 8 + e] = o[hh][e];
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hh = grp * 4 + r;
-    if (hh < G && l16 == 0) {
-      mlb[w][hh][0] = m_run[r];
-      mlb[w][hh][1] = l_run[r];
-    }
-  }
-  __syncthreads();
-
-  // combine the 4 waves and write the chunk's partial
-  const size_t part = (((size_t)b * p.Nkv + g) * p.n_chunks + chunk) * G;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mlb[ww][hh][0]);
-    float acc_o = 0.f, acc_l = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = exp2_fast(mlb[ww][hh][0] - M);  // idle wave: m = -inf -> 0
-      acc_o = __builtin_fmaf(f, ob[ww][hh][d], acc_o);
-      acc_l = __builtin_fmaf(f, mlb[ww][hh][1], acc_l);
-    }
-    p.ws_o[(part + hh) * D + d] = acc_o;
-    if (d == 0) {
-      p.ws_ml[(part + hh) * 2 + 0] = M;
-      p.ws_ml[(part + hh) * 2 + 1] = acc_l;
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db];
+    if (grp == 0) {
+      p.ws_ml[part * 2 + 0] = m_run;
+      p.ws_ml[part * 2 + 1] = l_run;
     }
   }
 }
@@ -240,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   if (row >= p.B * p.Nq) return;
   const int b = row / p.Nq;
   const int h = row % p.Nq;
-  const int G = p.Nq / p.Nkv;
+  const int G = p.G;
   const int g = h / G;
   const int hh = h % G;
   const int n = min(p.lens[b], p.Tcap);
@@ -267,10 +284,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
 
 }  // namespace
 
-bool decode_bf16_d128_supported(int Nq, int Nkv) {
-  const int G = Nq / Nkv;
-  return G == 1 || G == 2 || G == 4 || G == 8;
-}
+bool decode_bf16_d128_supported(int Nq, int Nkv) { return Nq / Nkv <= 16; }
 
 size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap) {
   const size_t n_chunks = ((size_t)Tcap + CH - 1) / CH;
@@ -291,20 +305,15 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
   p.B = B;
   p.Nq = Nq;
   p.Nkv = Nkv;
+  p.G = Nq / Nkv;
   p.Tcap = Tcap;
   p.n_chunks = (Tcap + CH - 1) / CH;
   const size_t parts = (size_t)B * Nq * p.n_chunks;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * D;
   p.c = kLog2e / sqrtf((float)D);
-  const dim3 grid(p.n_chunks, Nkv, B);
-  switch (Nq / Nkv) {
-    case 1: hipLaunchKernelGGL(decode_partial_kernel<1>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(decode_partial_kernel<2>, grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(decode_partial_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL(decode_partial_kernel<8>, grid, dim3(256), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (p.n_chunks > 0x7fffffff || Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_chunks, Nkv, B), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = B * Nq;

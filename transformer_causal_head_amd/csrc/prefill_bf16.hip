@@ -159,7 +159,12 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
 
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   constexpr int QW = 32 * QB;  // queries per wave
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  // four separate LDS objects, so the compiler can tell that the DMA copies
+  // into one stage never alias reads of another
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -194,10 +199,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int t_lo = lo_key / BN;
   const int nt = (hi_key + BN - 1) / BN - t_lo;
 
-  char* const K0 = smem;
-  char* const K1 = smem + TILE;
-  char* const V0 = smem + 2 * TILE;
-  char* const V1 = smem + 3 * TILE;
+  char* const K0 = k0s;
+  char* const K1 = k1s;
+  char* const V0 = v0s;
+  char* const V1 = v1s;
 
   // start the copies first, they overlap the set-up below
   load_tile(Kh, t_lo * BN, p.S, K0, w, lane);
