@@ -37,6 +37,11 @@ constexpr int D = 128;
 constexpr int CH = kDecodeChunk;  // keys per workgroup (one wavefront)
 constexpr int STEP = 32;          // keys per pipeline step
 constexpr int NS = CH / STEP;     // steps per chunk (fully unrolled)
+#ifndef DECODE_DIST
+#define DECODE_DIST 2
+#endif
+constexpr int DIST = DECODE_DIST;  // steps of K and V in flight ahead of the math
+static_assert(DIST == 2 || DIST == 3, "prefetch distance");
 constexpr int STAGE = STEP * D * 2;  // bytes of V per step
 constexpr float TAU = 8.f;
 
@@ -86,13 +91,12 @@ __device__ __forceinline__ void load_k(const __bf16* head, int k0, int last, int
   }
 }
 
-template <int VMCNT>
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15)
+template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(VMCNT == 0 || VMCNT == 16, "encoded counts");
-  if constexpr (VMCNT == 0)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  else
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
@@ -100,6 +104,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // one stage never aliases the transposing reads of the other
   __shared__ __attribute__((aligned(1024))) char vs0[STAGE];
   __shared__ __attribute__((aligned(1024))) char vs1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char vs2[DIST > 2 ? STAGE : 16];
 
   const int chunk = blockIdx.x;
   const int g = blockIdx.y;
@@ -133,13 +138,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   }
 
-  // copies in flight, oldest first: q, K(0), V(0), K(1), V(1); vmcnt(16)
-  // before a step therefore means that step's K and V have landed
-  bf16x8 kr[2][2][4];
-  load_k(Kh, c0, last, l16, grp, kr[0]);
-  load_v(Vh, c0, last, vs0, lane);
-  load_k(Kh, c0 + STEP, last, l16, grp, kr[1]);
-  load_v(Vh, c0 + STEP, last, vs1, lane);
+  // copies in flight, oldest first: q, then K(j), V(j) for j < DIST; each
+  // step's copies are 16 vector-memory instructions, so vmcnt(16 * k) before
+  // a step means that step's K and V have landed while k later steps fly
+  bf16x8 kr[DIST][2][4];
+  auto vstage = [&](int j) -> char* { return j == 0 ? vs0 : (j == 1 ? vs1 : vs2); };
+#pragma unroll
+  for (int j = 0; j < DIST; ++j) {
+    load_k(Kh, c0 + j * STEP, last, l16, grp, kr[j]);
+    load_v(Vh, c0 + j * STEP, last, vstage(j), lane);
+  }
 
   // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
   // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
@@ -219,17 +227,19 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   };
 
-  // Fully unrolled: step s reads K registers kr[s & 1] and V stage s & 1, and
-  // the copies for step s + 2 go into them right after.  Every copy is issued
-  // unconditionally (addresses clamp inside the chunk), so the outstanding
-  // count before each step is a compile-time constant.
+  // Fully unrolled: step s reads K registers kr[s % DIST] and V stage
+  // s % DIST, and the copies for step s + DIST go into them right after.
+  // Every copy is issued unconditionally (addresses clamp inside the chunk),
+  // so the outstanding count before each step is a compile-time constant.
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s + 1 < NS) wait_vm<16>(); else wait_vm<0>();
-    if (s < nsteps) step(s, kr[s & 1], (s & 1) ? vs1 : vs0);
-    if (s + 2 < NS) {
-      load_k(Kh, c0 + (s + 2) * STEP, last, l16, grp, kr[s & 1]);
-      load_v(Vh, c0 + (s + 2) * STEP, last, (s & 1) ? vs1 : vs0, lane);
+    if (s + 2 < NS && DIST > 2) wait_vm<32>();
+    else if (s + 1 < NS) wait_vm<16>();
+    else wait_vm<0>();
+    if (s < nsteps) step(s, kr[s % DIST], vstage(s % DIST));
+    if (s + DIST < NS) {
+      load_k(Kh, c0 + (s + DIST) * STEP, last, l16, grp, kr[s % DIST]);
+      load_v(Vh, c0 + (s + DIST) * STEP, last, vstage(s % DIST), lane);
     }
   }
   wait_vm<0>();  // no copy may still target LDS when the wave ends
@@ -250,7 +260,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   }
 }
 
-// One wavefront per (sequence, query head): merge the chunk partials.
+// One wavefront per (sequence, query head): merge the chunk partials.  Lanes
+// first read the chunks' (m, l) side by side and reduce them across the
+// wavefront; then each lane accumulates two head-dims over the chunks, with
+// the chunk weights broadcast from the lane that computed them.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -262,21 +275,44 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int hh = h % G;
   const int n = min(p.lens[b], p.Tcap);
   const int nc = n > 0 ? (n + CH - 1) / CH : 0;
+  const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_chunks * G + hh;  // chunk c: part0 + c*G
 
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) {
-    const size_t part = (((size_t)b * p.Nkv + g) * p.n_chunks + c) * G + hh;
-    M = fmaxf(M, p.ws_ml[part * 2]);
-  }
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)c * G) * 2]);
+  M = wave_max(M);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t part = (((size_t)b * p.Nkv + g) * p.n_chunks + c) * G + hh;
-    const float f = exp2_fast(p.ws_ml[part * 2] - M);
-    L = __builtin_fmaf(f, p.ws_ml[part * 2 + 1], L);
-    const f32x2 ov = *reinterpret_cast<const f32x2*>(p.ws_o + part * D + lane * 2);
-    o0 = __builtin_fmaf(f, ov[0], o0);
-    o1 = __builtin_fmaf(f, ov[1], o1);
+  for (int cb = 0; cb < nc; cb += 64) {
+    // lane j of this batch holds chunk cb + j's weight
+    float wgt = 0.f;
+    if (cb + lane < nc) {
+      const size_t part = part0 + (size_t)(cb + lane) * G;
+      wgt = exp2_fast(p.ws_ml[part * 2] - M);
+      L = __builtin_fmaf(wgt, p.ws_ml[part * 2 + 1], L);
+    }
+    const int cnt = min(64, nc - cb);
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      f32x2 ov[4];
+      float wj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ov[u] = *reinterpret_cast<const f32x2*>(p.ws_o + (part0 + (size_t)(cb + j + u) * G) * D + lane * 2);
+        wj[u] = __shfl(wgt, j + u, 64);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o0 = __builtin_fmaf(wj[u], ov[u][0], o0);
+        o1 = __builtin_fmaf(wj[u], ov[u][1], o1);
+      }
+    }
+    for (; j < cnt; ++j) {
+      const f32x2 ov = *reinterpret_cast<const f32x2*>(p.ws_o + (part0 + (size_t)(cb + j) * G) * D + lane * 2);
+      const float wj = __shfl(wgt, j, 64);
+      o0 = __builtin_fmaf(wj, ov[0], o0);
+      o1 = __builtin_fmaf(wj, ov[1], o1);
+    }
   }
+  L = wave_sum(L);
   const float inv = 1.f / L;  // n < 1 leaves L = 0: NaN row
   *reinterpret_cast<uint32_t*>(p.O + (size_t)row * D + lane * 2) = pack_bf16x2(o0 * inv, o1 * inv);
   if (p.LSE != nullptr && lane == 0) p.LSE[row] = (M + __log2f(L)) * kLn2;

@@ -19,20 +19,24 @@
 //   * The S^T accumulator layout is exactly the B-operand layout of the PV
 //     product O^T = V^T P^T, so P goes from fp32 accumulator to bf16 operand
 //     with v_cvt_pk_bf16_f32 and no lane exchange.
-//   * K and V tiles (64 keys x 256 B) are copied HBM -> LDS by the DMA path
-//     (global_load_lds_dwordx4): no VGPR staging, no VALU, double-buffered and
-//     issued one tile ahead, so the copy overlaps the math.  Rows are stored
+//   * K and V tiles (64 keys x 256 B) are copied HBM -> LDS by the buffer DMA
+//     path (buffer_load_dwordx4 ... lds): no VGPR staging, one offset per lane,
+//     rows past the sequence read as zero (buffer range check), double-
+//     buffered and issued one tile ahead, so the copy overlaps the math.  Rows are stored
 //     with a GF(2)-linear 16-byte-chunk swizzle that keeps both the 16-byte K
 //     reads and the transposing V reads free of bank conflicts.
 //   * V stays row-major in LDS; ds_read_b64_tr_b16 transposes it on the way
 //     into the V^T operand.
-//   * The next tile's QK^T is issued before this tile's softmax, so the matrix
-//     core works while the VALU computes exponentials.
+//   * The next tile's QK^T is issued before this tile's softmax, and a wave
+//     raises its issue priority while it issues that MFMA block, so the two
+//     waves on a SIMD drift out of lock-step and one wave's MFMAs overlap the
+//     other's exponentials.
 //   * Lazy rescale: the running maximum moves only when a new score exceeds it
 //     by more than TAU (log2 units).  Exponentials stay <= 2^TAU, and the
 //     accumulator is rescaled only on those rare moves.  The final O / l and
 //     the LSE are unchanged (both use the same reference maximum).
-//   * One workgroup = 4 waves sharing every K/V tile: for grouped-query
+//   * One workgroup = 8 waves (2 per SIMD) of 32 queries sharing every K/V
+//     tile: for grouped-query
 //     attention the waves take different query heads of one K/V head, so a
 //     K/V tile is fetched once per group; for MHA they take consecutive query
 //     blocks of one head.
@@ -54,6 +58,13 @@
 #endif
 #ifndef PREFILL_PIPE
 #define PREFILL_PIPE 1
+#endif
+// Wave priority while a wave issues its MFMA blocks (bit 0: QK^T, bit 1: PV).
+// The wave that reaches the matrix core first finishes its block first and
+// moves on to the softmax VALU work while the other wave on the SIMD gets
+// the matrix core, so the two waves fall out of lock-step.
+#ifndef PREFILL_PRIO
+#define PREFILL_PRIO 1
 #endif
 
 namespace attn {
@@ -96,19 +107,25 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
-// Copy keys [k0, k0+64) of one head into a swizzled LDS tile.  The tile is 16
-// pieces of 1 KB (4 rows); each wave issues 16 / NW of them.  Rows past the end
-// repeat the last row; the mask gives them zero weight.
-__device__ __forceinline__ void load_tile(const __bf16* head, int k0, int S, char* tile, int w,
-                                          int lane) {
+// Copy keys [k0, k0+64) of one head (a buffer resource over the head) into a
+// swizzled LDS tile.  The tile is 16 pieces of 1 KB (4 rows); each wave issues
+// 16 / NW of them.  The whole offset is in the per-lane operand, which the
+// buffer range check covers: rows past the end of the head read as zero.
+struct HeadRef {
+  __amdgpu_buffer_rsrc_t rs;
+};
+__device__ __forceinline__ HeadRef head_ref(const __bf16* head, int S) {
+  return HeadRef{__builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, S * D * 2, 0x00020000)};
+}
+__device__ __forceinline__ void load_tile(HeadRef h, int k0, int S, char* tile, int w, int lane) {
+  (void)S;
 #pragma unroll
   for (int j = 0; j < 16 / NW; ++j) {
     const int piece = w * (16 / NW) + j;
     const int r = piece * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
-    const int row = min(k0 + r, S - 1);
-    __builtin_amdgcn_global_load_lds(head + (size_t)row * D + c * 8,
-                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
+    const int voff = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
+                                             voff + k0 * (D * 2), 0, 0, 0);
   }
 }
 
@@ -124,6 +141,7 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 template <int QB_>
 __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
                                         const bf16x8 (&qf)[QB_][8], f32x16 (&s)[QB_][2]) {
+  if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int qb = 0; qb < QB_; ++qb)
 #pragma unroll
@@ -137,11 +155,13 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
       for (int qb = 0; qb < QB_; ++qb)
         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
     }
+  if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(0);
 }
 
 template <int QB_>
 __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
                                         const bf16x8 (&pf)[QB_][4], f32x16 (&o)[QB_][4]) {
+  if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -155,6 +175,7 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
       for (int qb = 0; qb < QB_; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][db], 0, 0, 0);
     }
+  if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(0);
 }
 
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
@@ -189,8 +210,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int wq1 = min(p.S, qa + QW);
   const bool wave_live = qa < p.S;
 
-  const __bf16* Kh = p.K + ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
-  const __bf16* Vh = p.V + ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
+  const HeadRef Kh = head_ref(p.K + ((size_t)b * p.Nkv + g) * (size_t)p.S * D, p.S);
+  const HeadRef Vh = head_ref(p.V + ((size_t)b * p.Nkv + g) * (size_t)p.S * D, p.S);
   const size_t q_base = ((size_t)b * p.Nq + head) * (size_t)p.S * D;
 
   // key range of the workgroup
@@ -305,7 +326,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
           s[qb][kb][r] = e;
           rs += e;
         }
-      l_run[qb] += rs;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -316,6 +336,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
             pk[j] = pack_bf16x2(s[qb][kb][kk * 8 + 2 * j], s[qb][kb][kk * 8 + 2 * j + 1]);
           pf[qb][kb * 2 + kk] = __builtin_bit_cast(bf16x8, pk);
         }
+      l_run[qb] += rs;
     }
     pv_tile<QB>(Vt, voff, pf, oacc);
   };
@@ -396,6 +417,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
                                     float* LSE, int B, int Nq, int Nkv, int S, int causal,
                                     int window, float scale, hipStream_t stream) {
+  // one head of K (or V) is addressed through a 31-bit buffer range
+  if ((long long)S * D * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
   Params p;
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
