@@ -66,6 +66,13 @@
 #ifndef PREFILL_PRIO
 #define PREFILL_PRIO 1
 #endif
+// LDS read-ahead inside the MFMA blocks: with it, the K fragments of QK^T
+// run six reads ahead of their MFMAs and the V^T fragments of PV four
+// MFMAs ahead, instead of the compiler's one or two, so the LDS latency is
+// hidden behind the matrix core.
+#ifndef PREFILL_RA
+#define PREFILL_RA 1
+#endif
 
 namespace attn {
 
@@ -108,8 +115,8 @@ __device__ __forceinline__ void wait_dma() {
 }
 
 // Copy keys [k0, k0+64) of one head (a buffer resource over the head) into a
-// swizzled LDS tile.  The tile is 16 pieces of 1 KB (4 rows); each wave issues
-// 16 / NW of them.  The whole offset is in the per-lane operand, which the
+// swizzled LDS tile.  The tile is 16 pieces of 1 KB (4 rows); wave w issues
+// pieces w, w + NW, ...  The whole offset is in the per-lane operand, which the
 // buffer range check covers: rows past the end of the head read as zero.
 struct HeadRef {
   __amdgpu_buffer_rsrc_t rs;
@@ -120,8 +127,9 @@ __device__ __forceinline__ HeadRef head_ref(const __bf16* head, int S) {
 __device__ __forceinline__ void load_tile(HeadRef h, int k0, int S, char* tile, int w, int lane) {
   (void)S;
 #pragma unroll
-  for (int j = 0; j < 16 / NW; ++j) {
-    const int piece = w * (16 / NW) + j;
+  for (int j = 0; j < (16 + NW - 1) / NW; ++j) {
+    const int piece = w + j * NW;  // wave-uniform
+    if (piece >= 16) break;
     const int r = piece * 4 + (lane >> 4);
     const int voff = r * 256 + (((lane & 15) ^ swz(r)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
@@ -155,6 +163,15 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
       for (int qb = 0; qb < QB_; ++qb)
         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
     }
+  if (PREFILL_RA && QB_ == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
+#pragma unroll
+    for (int k = 0; k < 10; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  }
   if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(0);
 }
 
@@ -175,6 +192,15 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
       for (int qb = 0; qb < QB_; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][db], 0, 0, 0);
     }
+  if (PREFILL_RA && QB_ == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 transposing reads
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
   if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(0);
 }
 
