@@ -37,16 +37,19 @@ DECODE = "decode_bf16_b64_h32kv8_t32768_d128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
-# HBM traffic of one prefill launch measured with rocprofv3 --pmc FETCH_SIZE /
-# WRITE_SIZE, scaled by the same counters on a copy of known size; valid only
-# for the kernel source it was taken on (sha256 of prefill_bf16.hip).
+# HBM traffic of one launch measured with rocprofv3 --pmc FETCH_SIZE /
+# WRITE_SIZE, scaled by the same counters on a copy of known size (one
+# FETCH_SIZE unit = 2047.9 bytes, one WRITE_SIZE unit = 1024 bytes); valid only
+# for the kernel source it was taken on (sha256[:16] of the .hip file).
 TRAFFIC = {
-    "4090374a486bc0de": 5490646586,  # 5.218e9 fetched + 2.726e8 written
+    "prefill_bf16.hip": {"f884b453a75b2b3a": 5297900052},  # 5.025e9 fetched + 2.726e8 written
+    # partial + merge kernels: 4.553e9 fetched + 3.685e7 written
+    "decode_bf16.hip": {"4878594e859d9824": 4589605918},
 }
 
 
-def _kernel_sha():
-    p = os.path.join(ROOT, "transformer_causal_head_amd", "csrc", "prefill_bf16.hip")
+def _kernel_sha(name):
+    p = os.path.join(ROOT, "transformer_causal_head_amd", "csrc", name)
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -76,6 +79,43 @@ def _cpu_baseline(q, k, v, cfg, budget_s=12.0):
                       f"float64 NumPy full score rows"}
 
 
+def _read_ceiling(torch, dev, gib=4.5, reps=5):
+    """Streaming-read rate of the device (libhbm_probe.so) for a few launch shapes."""
+    import ctypes
+    path = os.path.join(ROOT, "transformer_causal_head_amd", "libhbm_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the package first")
+    L = ctypes.CDLL(path)
+    L.hbm_read_probe.restype = ctypes.c_int
+    L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for blocks, unroll in ((1024, 4), (2048, 4), (4096, 4), (8192, 4), (16384, 4),
+                           (32768, 4), (8192, 8), (16384, 8)):
+        def launch():
+            rc = L.hbm_read_probe(buf.data_ptr(), nbytes, blocks, unroll, sink.data_ptr(),
+                                  ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"hbm_read_probe returned {rc}")
+        launch()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            launch()
+        b.record(stream)
+        b.synchronize()
+        gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        rows.append({"blocks": blocks, "threads": 256, "loads_in_flight": unroll,
+                     "GB/s": round(gbs, 1)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"read_bytes": nbytes, "reps": reps, "sweep": rows,
+                      "best_GBs": max(r["GB/s"] for r in rows)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="run only the streaming-read probe over 4.5 GB (HBM reference point)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -101,6 +143,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 2}))
+        return
+    if args.read_ceiling:
+        _read_ceiling(torch, dev)
         return
 
     pc = workloads.WORKLOADS[PREFILL]
@@ -153,8 +198,10 @@ def main():
     tflops = pflops / (pre_ms * 1e-3) / 1e12
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
-    sha = _kernel_sha()
-    traffic = TRAFFIC.get(sha)
+    sha = _kernel_sha("prefill_bf16.hip")
+    traffic = TRAFFIC["prefill_bf16.hip"].get(sha)
+    dsha = _kernel_sha("decode_bf16.hip")
+    dtraffic = TRAFFIC["decode_bf16.hip"].get(dsha)
     cpu = None
     if not args.no_cpu_baseline:
         print("timing the oracle on the host", file=sys.stderr, flush=True)
@@ -183,7 +230,7 @@ def main():
                     "algorithmic_flop": pflops},
         "decode": {"ms": round(dec_ms, 4), "value": round(gbs, 1), "unit": "GB/s",
                    "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                   "algorithmic_bytes": dbytes},
+                   "algorithmic_bytes": dbytes, "traffic": dtraffic, "kernel_sha": dsha},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill_kernel", "kernel_sha": sha},
