@@ -49,7 +49,7 @@ def test_workspace_query():
     n = tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_BF16)
     # one (m, l, o[128]) fp32 record per (sequence, query head, key chunk)
     rec = 64 * 32 * (128 + 2) * 4
-    assert n > 0 and n % rec == 0 and 32768 % (n // rec) == 0
+    assert n > 0 and n % rec == 0 and 1 <= n // rec <= 32768 // 32
     assert tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_F32) == 0
     assert tch.attn_decode_workspace_bytes(64, 30, 8, 128, 32768, tch.ATTN_BF16) == 0
     assert tch.attn_decode_workspace_bytes(0, 32, 8, 128, 32768, tch.ATTN_BF16) == 0

@@ -231,6 +231,43 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
     check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, Tcap, lens), storage_allowance=True)
 
 
+def _decode_chunk(B, Nkv, Tcap):
+    # the host's choice of keys per chunk, restated: the longest candidate that
+    # gives at least 4096 (sequence, K/V head, chunk) items at full length
+    for ch in (1792, 1152, 896, 640, 384, 224, 160, 96):
+        if B * Nkv * -(-Tcap // ch) >= 4096:
+            return ch
+    return 96
+
+
+@pytest.mark.parametrize("B,Nkv,Tcap,ch", [
+    (16, 8, 8192, 224),
+    (16, 8, 16384, 384),
+    (24, 8, 16384, 640),
+    (32, 8, 16384, 896),
+])
+def test_decode_chunk_sizes(B, Nkv, Tcap, ch):
+    # every chunk length the host can pick, with lengths on and around chunk
+    # edges; the workspace size shows which chunk length was taken
+    Nq = 32
+    assert _decode_chunk(B, Nkv, Tcap) == ch
+    ws = tch.attn_decode_workspace_bytes(B, Nq, Nkv, 128, Tcap, tch.ATTN_BF16)
+    assert ws == B * Nq * -(-Tcap // ch) * (128 + 2) * 4
+    rng = np.random.default_rng(Tcap + B)
+    lens = rng.integers(1, Tcap, B, endpoint=True)
+    lens[:8] = [1, 31, 32, 33, ch - 1, ch, ch + 1, Tcap]
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, 128, Tcap, 1, Tcap, seed=ch,
+                                                lens=lens)
+    O, L = run_decode(q, kc, vc, lens_a, "bf16")
+    rows = [(b, h) for b in range(8) for h in (0, Nq - 1)]
+    rows += [(int(b), int(h)) for b, h in zip(rng.integers(8, B, 32), rng.integers(0, Nq, 32))]
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), _LazyF64(kc), _LazyF64(vc), lens_a,
+                               rows=rows)
+    Os = np.stack([O[b, h] for b, h in rows])
+    Ls = np.array([L[b, h] for b, h in rows])
+    say(f"chunk {ch}: errors {check(Os, Ls, Or, Lr, 'bf16', (B, Nkv, Tcap, ch), storage_allowance=True)}")
+
+
 @pytest.mark.parametrize("Dh", [4, 64, 128])
 def test_decode_fp32(Dh):
     lens_a, q, kc, vc = workloads.decode_inputs(3, 4, 2, Dh, 50, 1, 50, dtype="f32", seed=Dh,

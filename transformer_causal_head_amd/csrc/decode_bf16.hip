@@ -3,28 +3,38 @@
 // The step is one query row per sequence against its cached keys (textbook
 // attention chapter, "KV-кэш" and "Prefill и decode": a 1 x t score row;
 // decode is bound by reading the cache).  The key axis of every (sequence,
-// K/V head) is cut into chunks of kDecodeChunk keys; each chunk yields a
-// partial (running max m, running sum l, unnormalised output o) for the G
-// query heads that share the K/V head, and a second kernel merges the
-// partials with the same rescaling identity the online softmax uses (the
-// Chinese post's Flash Attention section: rescale by exp(m_old - m_new)).
+// K/V head) is cut into chunks; each chunk yields a partial (running max m,
+// running sum l, unnormalised output o) for the G query heads that share the
+// K/V head, and a second kernel merges the partials with the same rescaling
+// identity the online softmax uses (the Chinese post's Flash Attention
+// section: rescale by exp(m_old - m_new)).
 //
 // gfx950 design
 //   * One wavefront per (sequence, K/V head, chunk); chunks past a sequence's
-//     length exit at once, so the work follows the ragged lengths and fills
-//     the chip with thousands of small workgroups.
-//   * The chunk streams in steps of 32 keys.  K rows are loaded into VGPRs two
-//     steps ahead; V rows are copied HBM -> LDS by the DMA path
-//     (global_load_lds_dwordx4) into a wave-private double buffer, also two
-//     steps ahead, so ~16 KB per wave stay in flight without VGPR cost.
+//     length exit at once, so the work follows the ragged lengths.
+//   * The chunk length is chosen on the host: as long as the grid still has
+//     thousands of work items (long chunks mean fewer partials and longer
+//     sequential streams), and never a power of two: chunks whose starts sit
+//     on 128 KB multiples made concurrently running waves collide in the
+//     memory system and cost ~10% of the bandwidth.
+//   * The chunk streams in steps of 32 keys.  K and V rows are both copied
+//     HBM -> LDS by the DMA path (global_load_lds_dwordx4) with the
+//     non-temporal hint: each copy instruction moves 4 whole 256-byte rows,
+//     i.e. 1 KB of contiguous memory, and nothing is staged in VGPRs.
+//     Loading K straight into MFMA operand registers instead touches 16 rows
+//     x 64 bytes per instruction and tops out ~12% lower.
+//   * Two LDS stages per tensor; the copies for step s + 2 are issued as soon
+//     as step s has read its stage, so two steps (32 KB) stay in flight per
+//     wave.  The step loop is unrolled by two so every stage is a distinct LDS
+//     object and every wait count is a compile-time constant.
 //   * Both products run on v_mfma_f32_16x16x32_bf16 in the transposed form of
 //     the prefill kernel: S^T = K q^T (keys on M, the G query heads on N), and
-//     O^T = V^T P^T, whose B operand is the S^T accumulator layout.  V is
-//     transposed on its way out of LDS by ds_read_b64_tr_b16; a row-bit
-//     rotation swizzle keeps those reads bank-conflict free.
+//     O^T = V^T P^T, whose B operand is the S^T accumulator layout.  K is read
+//     from LDS in operand layout (a row-XOR swizzle keeps the 16-row reads
+//     conflict free); V is transposed on its way out by ds_read_b64_tr_b16.
 //   * Every K and V byte is read once per K/V head and shared by its G query
-//     heads.  Rows at or past the length are never read: addresses clamp to
-//     the last valid row and those keys get probability 0.
+//     heads.  Rows at or past the length are never used: copy addresses clamp
+//     to the last valid row and those keys get probability 0.
 
 #include "common.h"
 #include "kernels.h"
@@ -34,19 +44,16 @@ namespace attn {
 namespace {
 
 constexpr int D = 128;
-constexpr int CH = kDecodeChunk;  // keys per workgroup (one wavefront)
-constexpr int STEP = 32;          // keys per pipeline step
-constexpr int NS = CH / STEP;     // steps per chunk (fully unrolled)
-#ifndef DECODE_DIST
-#define DECODE_DIST 2
-#endif
-constexpr int DIST = DECODE_DIST;  // steps of K and V in flight ahead of the math
-static_assert(DIST == 2 || DIST == 3, "prefetch distance");
-constexpr int STAGE = STEP * D * 2;  // bytes of V per step
+constexpr int STEP = 32;             // keys per pipeline step
+constexpr int STAGE = STEP * D * 2;  // bytes of K (or V) per step
 constexpr float TAU = 8.f;
+constexpr int kNonTemporal = 2;      // cache-policy bit of the copy instructions
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
 struct DecParams {
   const __bf16* q;
@@ -58,36 +65,29 @@ struct DecParams {
   float* ws_o;    // [B, Nkv, n_chunks, G, D] unnormalised partial outputs
   float* ws_ml;   // [B, Nkv, n_chunks, G, 2]  (m in log2 units, l)
   int B, Nq, Nkv, G, Tcap, n_chunks;
+  int ch;         // keys per chunk (a multiple of STEP)
   float c;        // scale * log2(e)
 };
 
-// 16-byte chunk c of V row r sits at chunk position c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r << 1) & 14) | ((r >> 3) & 1); }
+// 16-byte chunk c of V row r sits at chunk position c ^ vswz(r) (keeps the
+// transposing reads conflict free); chunk c of K row r at c ^ (r & 15) (the
+// operand reads take one chunk of 16 consecutive rows).
+__device__ __forceinline__ int vswz(int r) { return ((r << 1) & 14) | ((r >> 3) & 1); }
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
 
-// V rows [k0, k0+32) -> one LDS stage (8 pieces of 4 rows); rows are clamped
-// to the last valid one.
-__device__ __forceinline__ void load_v(const __bf16* head, int k0, int last, char* stage,
-                                       int lane) {
+// Rows [k0, k0+32) of one head -> one LDS stage: 8 copies of 4 whole rows,
+// lane i of a copy lands at byte 16*i of its 1 KB piece.  Rows past `last`
+// are clamped to it.
+template <bool IS_K>
+__device__ __forceinline__ void load_rows(const __bf16* head, int k0, int last, lds_char* stage,
+                                          int lane) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = j * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
+    const int c = (lane & 15) ^ (IS_K ? kswz(r) : vswz(r));
     const int row = min(k0 + r, last);
     __builtin_amdgcn_global_load_lds(head + (size_t)row * D + c * 8,
-                                     (lds_void*)(stage + j * 1024), 16, 0, 0);
-  }
-}
-
-// K operand for two 16-key blocks: lane (grp, l16) holds
-// K[k0 + 16*kb + l16][32*ks + 8*grp .. +7]
-__device__ __forceinline__ void load_k(const __bf16* head, int k0, int last, int l16, int grp,
-                                       bf16x8 (&kr)[2][4]) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = min(k0 + kb * 16 + l16, last);
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(head + (size_t)row * D + grp * 8);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kr[kb][ks] = src[ks * 4];
+                                     (lds_void*)(stage + j * 1024), 16, 0, kNonTemporal);
   }
 }
 
@@ -100,22 +100,26 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
-  // two separate LDS objects, so the compiler can tell that a DMA copy into
-  // one stage never aliases the transposing reads of the other
-  __shared__ __attribute__((aligned(1024))) char vs0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char vs1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char vs2[DIST > 2 ? STAGE : 16];
+  // four separate LDS objects, so the compiler can tell that a copy into one
+  // stage never aliases the reads of another
+  __shared__ __attribute__((aligned(1024))) char k0s[STAGE];
+  __shared__ __attribute__((aligned(1024))) char k1s[STAGE];
+  __shared__ __attribute__((aligned(1024))) char v0s[STAGE];
+  __shared__ __attribute__((aligned(1024))) char v1s[STAGE];
+
+  lds_char* const K0 = (lds_char*)k0s;
+  lds_char* const K1 = (lds_char*)k1s;
+  lds_char* const V0 = (lds_char*)v0s;
+  lds_char* const V1 = (lds_char*)v1s;
 
   const int chunk = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int n = min(p.lens[b], p.Tcap);
-  const int c0 = chunk * CH;
+  const int c0 = chunk * p.ch;
   if (c0 >= n) return;
-  const int nsteps = (min(CH, n - c0) + STEP - 1) / STEP;
-  // prefetches run past the chunk's last step with addresses clamped to the
-  // chunk's last row: the loop body stays uniform and the extra copies hit L2
-  const int last = min(n, c0 + CH) - 1;
+  const int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
+  const int last = min(n, c0 + p.ch) - 1;
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15;
@@ -138,16 +142,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   }
 
-  // copies in flight, oldest first: q, then K(j), V(j) for j < DIST; each
-  // step's copies are 16 vector-memory instructions, so vmcnt(16 * k) before
-  // a step means that step's K and V have landed while k later steps fly
-  bf16x8 kr[DIST][2][4];
-  auto vstage = [&](int j) -> char* { return j == 0 ? vs0 : (j == 1 ? vs1 : vs2); };
-#pragma unroll
-  for (int j = 0; j < DIST; ++j) {
-    load_k(Kh, c0 + j * STEP, last, l16, grp, kr[j]);
-    load_v(Vh, c0 + j * STEP, last, vstage(j), lane);
-  }
+  // copies in flight, oldest first: q, then K(0), V(0), K(1), V(1).  A step's
+  // copies are 16 vector-memory instructions, so vmcnt(16) before step s means
+  // step s has landed while step s + 1 is still in flight.  Copies are issued
+  // for two steps past the chunk's end too (all rows clamp to its last row
+  // and mostly hit L2), so that count holds on every path and the compiler
+  // adds no full drain of its own.
+  load_rows<true>(Kh, c0, last, K0, lane);
+  load_rows<false>(Vh, c0, last, V0, lane);
+  load_rows<true>(Kh, c0 + STEP, last, K1, lane);
+  load_rows<false>(Vh, c0 + STEP, last, V1, lane);
 
   // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
   // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
@@ -159,16 +163,20 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       const int r = 16 * hf + 4 * grp + ip;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        voff[hf][db] = r * 256 + (((2 * db + (u >> 1)) ^ swz(r)) << 4) + (u & 1) * 8;
+        voff[hf][db] = r * 256 + (((2 * db + (u >> 1)) ^ vswz(r)) << 4) + (u & 1) * 8;
     }
   }
+  // K operand offsets: row 16*kb + l16, 16-byte chunk 4*ks + grp
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = l16 * 256 + (((4 * ks + grp) ^ kswz(l16)) << 4);
 
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto step = [&](int s, bf16x8 (&kr)[2][4], const char* vst) {
+  auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
     const int k0 = c0 + s * STEP;
     // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
     // query column l16
@@ -177,8 +185,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kb][ks], qf[ks], sc[kb], 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *(lds_bf16x8*)(kst + kb * 4096 + koff[ks]);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc[kb], 0, 0, 0);
+      }
     }
     if (k0 + STEP > n) {
 #pragma unroll
@@ -227,20 +237,18 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   };
 
-  // Fully unrolled: step s reads K registers kr[s % DIST] and V stage
-  // s % DIST, and the copies for step s + DIST go into them right after.
-  // Every copy is issued unconditionally (addresses clamp inside the chunk),
-  // so the outstanding count before each step is a compile-time constant.
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (s + 2 < NS && DIST > 2) wait_vm<32>();
-    else if (s + 1 < NS) wait_vm<16>();
-    else wait_vm<0>();
-    if (s < nsteps) step(s, kr[s % DIST], vstage(s % DIST));
-    if (s + DIST < NS) {
-      load_k(Kh, c0 + (s + DIST) * STEP, last, l16, grp, kr[s % DIST]);
-      load_v(Vh, c0 + (s + DIST) * STEP, last, vstage(s % DIST), lane);
-    }
+  // Steps in pairs: even steps use stage 0, odd steps stage 1.  Before step s
+  // the copies of steps s and s + 1 are outstanding; once step s has read its
+  // stage, the copies of step s + 2 go into it.
+  for (int s = 0; s < nsteps; s += 2) {
+    wait_vm<16>();
+    step(s, K0, V0);
+    load_rows<true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
+    load_rows<false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
+    wait_vm<16>();
+    if (s + 1 < nsteps) step(s + 1, K1, V1);
+    load_rows<true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
+    load_rows<false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
   }
   wait_vm<0>();  // no copy may still target LDS when the wave ends
 
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int g = h / G;
   const int hh = h % G;
   const int n = min(p.lens[b], p.Tcap);
-  const int nc = n > 0 ? (n + CH - 1) / CH : 0;
+  const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
   const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_chunks * G + hh;  // chunk c: part0 + c*G
 
   float M = -INFINITY;
@@ -322,8 +330,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
 
 bool decode_bf16_d128_supported(int Nq, int Nkv) { return Nq / Nkv <= 16; }
 
+// Keys per chunk: the longest candidate that still gives the grid at least
+// 4096 (sequence, K/V head, chunk) items when every sequence is Tcap long.
+// The candidates are multiples of 32 keys, none a power of two.
+int decode_bf16_d128_chunk(int B, int Nkv, int Tcap) {
+  static const int kChunks[] = {1792, 1152, 896, 640, 384, 224, 160, 96};
+  const long long heads = (long long)B * Nkv;
+  for (int ch : kChunks)
+    if (heads * ((Tcap + ch - 1) / ch) >= 4096) return ch;
+  return kChunks[sizeof(kChunks) / sizeof(kChunks[0]) - 1];
+}
+
 size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap) {
-  const size_t n_chunks = ((size_t)Tcap + CH - 1) / CH;
+  const int ch = decode_bf16_d128_chunk(B, Nkv, Tcap);
+  const size_t n_chunks = ((size_t)Tcap + ch - 1) / ch;
   const size_t parts = (size_t)B * Nq * n_chunks;  // B * Nkv * n_chunks * G
   return parts * D * sizeof(float) + parts * 2 * sizeof(float);
 }
@@ -343,12 +363,13 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
   p.Nkv = Nkv;
   p.G = Nq / Nkv;
   p.Tcap = Tcap;
-  p.n_chunks = (Tcap + CH - 1) / CH;
+  p.ch = decode_bf16_d128_chunk(B, Nkv, Tcap);
+  p.n_chunks = (Tcap + p.ch - 1) / p.ch;
   const size_t parts = (size_t)B * Nq * p.n_chunks;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * D;
   p.c = kLog2e / sqrtf((float)D);
-  if (p.n_chunks > 0x7fffffff || Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
+  if (Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_chunks, Nkv, B), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

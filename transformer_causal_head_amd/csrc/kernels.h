@@ -22,10 +22,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
                                float scale, int is_bf16, hipStream_t stream);
 
 // bf16, Dh == 128 split-K decode (partials + log-sum-exp merge).
-#ifndef DECODE_CHUNK
-#define DECODE_CHUNK 512
-#endif
-constexpr int kDecodeChunk = DECODE_CHUNK;
+int decode_bf16_d128_chunk(int B, int Nkv, int Tcap);
 size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap);
 bool decode_bf16_d128_supported(int Nq, int Nkv);
 hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
