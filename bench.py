@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # for the kernel source it was taken on (sha256[:16] of the .hip file).
 TRAFFIC = {
     "prefill_bf16.hip": {"f884b453a75b2b3a": 5297900052},  # 5.025e9 fetched + 2.726e8 written
-    # partial + merge kernels: 4.553e9 fetched + 3.685e7 written
-    "decode_bf16.hip": {"4878594e859d9824": 4589605918},
+    # partial + merge kernels: 4.529e9 fetched + 1.131e7 written
+    "decode_bf16.hip": {"bdec2559054b8cb5": 4539851941},
 }
 
 
@@ -88,16 +88,16 @@ def _read_ceiling(torch, dev, gib=4.5, reps=5):
     L = ctypes.CDLL(path)
     L.hbm_read_probe.restype = ctypes.c_int
     L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_void_p, ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     nbytes = int(gib * (1 << 30)) // 16 * 16
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     rows = []
-    for blocks, unroll in ((1024, 4), (2048, 4), (4096, 4), (8192, 4), (16384, 4),
-                           (32768, 4), (8192, 8), (16384, 8)):
+    shapes = ((1024, 4), (4096, 4), (16384, 4), (32768, 4), (8192, 8), (16384, 8))
+    for nt, (blocks, unroll) in [(nt, sh) for nt in (0, 1) for sh in shapes]:
         def launch():
-            rc = L.hbm_read_probe(buf.data_ptr(), nbytes, blocks, unroll, sink.data_ptr(),
+            rc = L.hbm_read_probe(buf.data_ptr(), nbytes, blocks, unroll, nt, sink.data_ptr(),
                                   ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"hbm_read_probe returned {rc}")
@@ -110,7 +110,7 @@ def _read_ceiling(torch, dev, gib=4.5, reps=5):
         b.synchronize()
         gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
         rows.append({"blocks": blocks, "threads": 256, "loads_in_flight": unroll,
-                     "GB/s": round(gbs, 1)})
+                     "non_temporal": bool(nt), "GB/s": round(gbs, 1)})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
     print(json.dumps({"read_bytes": nbytes, "reps": reps, "sweep": rows,
                       "best_GBs": max(r["GB/s"] for r in rows)}), flush=True)
