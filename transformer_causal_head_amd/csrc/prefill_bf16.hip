@@ -293,21 +293,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
   }
 
+  // Tile ranges of this wave, as wave-uniform integers: tiles [tl_lo, tl_hi]
+  // hold at least one visible (query, key) pair; tiles [tf_lo, tf_hi] hold
+  // only visible pairs (no mask needed).  floor division by BN = 64.
+  auto fdiv = [](int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); };
+  int tl_lo = p.window > 0 ? fdiv(qa - p.window + 1) : -1;
+  int tl_hi = p.causal ? fdiv(wq1 - 1) : (p.S - 1) / BN;
+  if (!wave_live) tl_hi = tl_lo - 1;
+  int tf_lo = p.window > 0 ? -fdiv(-(wq1 - p.window)) : 0;  // ceil((wq1 - window) / 64)
+  int tf_hi = fdiv(p.S - BN);
+  if (p.causal) tf_hi = min(tf_hi, fdiv(qa - (BN - 1)));
+  tl_lo = __builtin_amdgcn_readfirstlane(tl_lo);
+  tl_hi = __builtin_amdgcn_readfirstlane(tl_hi);
+  tf_lo = __builtin_amdgcn_readfirstlane(tf_lo);
+  tf_hi = __builtin_amdgcn_readfirstlane(tf_hi);
   // does this wave see any (query, key) pair of tile t?
-  auto live = [&](int t) {
-    const int k0 = t * BN;
-    bool ok = wave_live;
-    if (p.causal) ok = ok && (k0 <= wq1 - 1);
-    if (p.window > 0) ok = ok && (k0 + BN - 1 >= qa - p.window + 1);
-    return ok;
-  };
+  auto live = [&](int t) { return t >= tl_lo && t <= tl_hi; };
 
   auto softmax_pv = [&](int t, f32x16 (&s)[QB][2], const char* Vt) {
     const int k0 = t * BN;
-    bool need_mask = (k0 + BN > p.S);
-    if (p.causal) need_mask = need_mask || (k0 + BN - 1 > qa);
-    if (p.window > 0) need_mask = need_mask || (wq1 - 1 - k0 >= p.window);
-    if (need_mask) {
+    if (t < tf_lo || t > tf_hi) {
       // accumulator register r of key block kb holds key
       // k0 + 32*kb + 8*(r/4) + 4*hl + (r%4) for query column ln
 #pragma unroll
