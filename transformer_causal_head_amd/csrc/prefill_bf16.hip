@@ -74,6 +74,7 @@
 #define PREFILL_RA 1
 #endif
 
+
 namespace attn {
 
 namespace {
@@ -310,27 +311,36 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   // does this wave see any (query, key) pair of tile t?
   auto live = [&](int t) { return t >= tl_lo && t <= tl_hi; };
 
-  auto softmax_pv = [&](int t, f32x16 (&s)[QB][2], const char* Vt) {
-    const int k0 = t * BN;
-    if (t < tf_lo || t > tf_hi) {
-      // accumulator register r of key block kb holds key
-      // k0 + 32*kb + 8*(r/4) + 4*hl + (r%4) for query column ln
+  // --- pieces of the per-tile softmax ---
+  auto masked = [&](int t) { return t < tf_lo || t > tf_hi; };
+  // Visible keys of this lane's query qi form one interval [lo_i, hi_i]
+  // (causal: hi_i = qi; window: lo_i = qi - window + 1; keys < S), so a
+  // boundary tile's mask is two compares per score.
+  int key_lo[QB], key_hi[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qa + qb * 32 + ln;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qa + qb * 32 + ln;
+    key_hi[qb] = p.causal ? min(qi, p.S - 1) : p.S - 1;
+    key_lo[qb] = p.window > 0 ? qi - p.window + 1 : 0;
+  }
+  auto mask_tile = [&](int t, f32x16 (&s)[QB][2]) {
+    const int k0 = t * BN + hl * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      // key of register r in block kb: k0 + 32*kb + 8*(r/4) + (r%4)
+      const int hi = key_hi[qb] - k0, lo = key_lo[qb] - k0;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-            bool ok = kj < p.S;
-            if (p.causal) ok = ok && (kj <= qi);
-            if (p.window > 0) ok = ok && (qi - kj < p.window);
-            if (!ok) s[qb][kb][r] = -INFINITY;
-          }
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = kb * 32 + (r >> 2) * 8 + (r & 3);
+          if (o > hi || o < lo) s[qb][kb][r] = -INFINITY;
+        }
     }
-    bf16x8 pf[QB][4];
+  };
+  // running max over the tile's (masked) scores; rescale O and l when it
+  // moves by more than TAU
+  auto max_rescale = [&](f32x16 (&s)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -347,29 +357,40 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) oacc[qb][db] *= alpha;
       }
+    }
+  };
+  // P = exp2(S*c - m) rounded to bf16, l += row sum, O^T += V^T P^T
+  auto exp_pv = [&](f32x16 (&s)[QB][2], const char* Vt) {
+    bf16x8 pf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = exp2_fast(__builtin_fmaf(s[qb][kb][r], p.c, -m_use));
-          s[qb][kb][r] = e;
-          rs += e;
-        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           u32x4 pk;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pk[j] = pack_bf16x2(s[qb][kb][kk * 8 + 2 * j], s[qb][kb][kk * 8 + 2 * j + 1]);
+          for (int j = 0; j < 4; ++j) {
+            const float e0 = exp2_fast(__builtin_fmaf(s[qb][kb][kk * 8 + 2 * j], p.c, -m_use));
+            const float e1 = exp2_fast(__builtin_fmaf(s[qb][kb][kk * 8 + 2 * j + 1], p.c, -m_use));
+            rs += e0;
+            rs += e1;
+            pk[j] = pack_bf16x2(e0, e1);
+          }
           pf[qb][kb * 2 + kk] = __builtin_bit_cast(bf16x8, pk);
         }
       l_run[qb] += rs;
     }
     pv_tile<QB>(Vt, voff, pf, oacc);
+  };
+
+  // mask (boundary tiles only), running max / rescale, then P and PV
+  auto softmax_pv = [&](int t, f32x16 (&s)[QB][2], const char* Vt) {
+    if (masked(t)) mask_tile(t, s);
+    max_rescale(s);
+    exp_pv(s, Vt);
   };
 
   if constexpr (PIPE) {
