@@ -1,4 +1,5 @@
-"""Float64 CPU oracle of causal scaled dot-product attention (prefill + decode).
+"""Float64 CPU oracle of causal scaled dot-product attention (prefill, chunked
+prefill against a cache, decode, cache append).
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the package's smoke
 check and the benchmark's CPU-baseline leg, never by the GPU library.  It is
@@ -9,8 +10,10 @@ the source pages, closed forms, brute force and an independent library routine.
 
 from .attention import (
     allowed_mask,
+    append_ref,
     attention_ref,
     attention_rows_ref,
+    chunk_ref,
     decode_ref,
     head_attention,
     kv_head_of,
@@ -19,8 +22,10 @@ from .attention import (
 
 __all__ = [
     "allowed_mask",
+    "append_ref",
     "attention_ref",
     "attention_rows_ref",
+    "chunk_ref",
     "decode_ref",
     "head_attention",
     "kv_head_of",

@@ -35,7 +35,16 @@ Readings taken where the pages leave a choice open:
   * prefill has as many keys as queries and the causal mask is aligned at the
     top-left corner: query i sees keys j <= i;
   * a decode step's cached length counts the current token: the query row
-    sits at position lens-1 and sees keys 0..lens-1.
+    sits at position lens-1 and sees keys 0..lens-1;
+  * a chunk of Sq new queries appended to a cache of lens keys (chunked
+    prefill) is aligned at the bottom-right corner: its query i sits at
+    absolute position lens - Sq + i (the textbook's step-by-step forward pass
+    takes mask rows from start_pos on), so the chunk's queries see every
+    earlier cached key and causally each other;
+  * a rolling-buffer cache of capacity W stores position p in slot p mod W;
+    with the new token appended first, the buffer holds exactly the W
+    positions a window of W admits, in rotated order, which the softmax does
+    not see.
 """
 
 import numpy as np
@@ -172,13 +181,15 @@ def attention_rows_ref(Q, K, V, triples, causal=True, window=0, scale=None):
     return O, LSE
 
 
-def decode_ref(q, Kc, Vc, lens, scale=None, rows=None):
+def decode_ref(q, Kc, Vc, lens, scale=None, rows=None, window=0):
     """One decode step against a KV cache.
 
     q: [B,Nq,Dh], Kc, Vc: [B,Nkv,Tcap,Dh], lens: [B] with 1 <= lens[b] <= Tcap.
     Sequence b's query sees its cached keys 0..lens[b]-1 (the new token's
     key is already in the cache) -- textbook, sections "KV-кэш" and
     "Prefill и decode": a decode step is a single score row of length t.
+    With ``window`` > 0 only the keys lens[b]-window .. lens[b]-1 are visible
+    (section "Скользящее окно", in the i - j < window convention).
     Entries past lens[b] are never read.  ``scale`` defaults to 1/sqrt(Dh).
     ``rows`` optionally restricts the work to (b, h) pairs; then O is
     [len(rows), Dh] and LSE [len(rows)].  Otherwise O [B,Nq,Dh], LSE [B,Nq].
@@ -198,8 +209,82 @@ def decode_ref(q, Kc, Vc, lens, scale=None, rows=None):
         qrow = np.asarray(q[b, h], dtype=np.float64)[None, :]
         Kb = np.asarray(Kc[b, g, :n], dtype=np.float64)
         Vb = np.asarray(Vc[b, g, :n], dtype=np.float64)
-        o, lse = head_attention(qrow, [n - 1], Kb, Vb, True, 0, scale)
+        o, lse = head_attention(qrow, [n - 1], Kb, Vb, True, window, scale)
         O[t], LSE[t] = o[0], lse[0]
     if rows is None:
         return O.reshape(B, Nq, Dh), LSE.reshape(B, Nq)
     return O, LSE
+
+
+def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None):
+    """Chunked prefill: Sq new queries per sequence against a KV cache.
+
+    Q: [B,Nq,Sq,Dh]; Kc, Vc: [B,Nkv,Tcap,Dh] already holding the chunk's own
+    keys; lens: [B] cached keys per sequence including the chunk, with
+    Sq <= lens[b] <= Tcap.  Query i of sequence b sits at absolute position
+    lens[b] - Sq + i and sees keys j <= its position (and, with ``window``,
+    position - j < window).  Textbook, "Prefill и decode": a long prompt can be
+    filled chunk by chunk, with the causal mask again inside the chunk;
+    "Прямой проход по шагам" and "Типичные ошибки и тонкости": the mask rows
+    start at the first new position, not at 0.
+    ``rows`` optionally restricts the work to (b, h, i) triples; then O is
+    [len(rows), Dh] and LSE [len(rows)].  Otherwise O [B,Nq,Sq,Dh], LSE [B,Nq,Sq].
+    """
+    B, Nq, Sq, Dh = Q.shape
+    Nkv = Kc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    for b in range(B):
+        if not Sq <= int(lens[b]) <= Kc.shape[2]:
+            raise ValueError("cache length must cover the chunk and fit the cache")
+    if rows is not None:
+        O = np.empty((len(rows), Dh))
+        LSE = np.empty(len(rows))
+        for t, (b, h, i) in enumerate(rows):
+            n = int(lens[b])
+            g = kv_head_of(h, Nq, Nkv)
+            qrow = np.asarray(Q[b, h, i], dtype=np.float64)[None, :]
+            o, lse = head_attention(qrow, [n - Sq + i], np.asarray(Kc[b, g, :n], dtype=np.float64),
+                                    np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale)
+            O[t], LSE[t] = o[0], lse[0]
+        return O, LSE
+    O = np.empty((B, Nq, Sq, Dh))
+    LSE = np.empty((B, Nq, Sq))
+    for b in range(B):
+        n = int(lens[b])
+        positions = np.arange(n - Sq, n)
+        for h in range(Nq):
+            g = kv_head_of(h, Nq, Nkv)
+            O[b, h], LSE[b, h] = head_attention(
+                np.asarray(Q[b, h], dtype=np.float64), positions,
+                np.asarray(Kc[b, g, :n], dtype=np.float64),
+                np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale)
+    return O, LSE
+
+
+def append_ref(Kc, Vc, Knew, Vnew, pos, rolling=False):
+    """Write new K/V rows into a cache; returns the updated copies.
+
+    Kc, Vc: [B,Nkv,Tcap,...]; Knew, Vnew: [B,Nkv,Snew,...]; pos: [B] absolute
+    position of each sequence's first new row (its token count before the
+    append).  Row i lands in slot pos[b] + i of a linear cache (textbook,
+    "Прямой проход по шагам": the new K and V are concatenated after the
+    cached ones), or in slot (pos[b] + i) mod Tcap of a rolling buffer
+    ("Скользящее окно": only the last positions are kept; Mistral's rolling
+    buffer cache).  Rows are written in order, so when a rolling append is
+    longer than the buffer the latest rows win.  A linear append past Tcap is
+    an error.
+    """
+    Kc = np.array(Kc, copy=True)
+    Vc = np.array(Vc, copy=True)
+    B, Nkv, Tcap = Kc.shape[:3]
+    Snew = Knew.shape[2]
+    for b in range(B):
+        p0 = int(pos[b])
+        if p0 < 0 or (not rolling and p0 + Snew > Tcap):
+            raise ValueError("append outside the cache")
+        for i in range(Snew):
+            slot = (p0 + i) % Tcap if rolling else p0 + i
+            Kc[b, :, slot] = Knew[b, :, i]
+            Vc[b, :, slot] = Vnew[b, :, i]
+    return Kc, Vc
