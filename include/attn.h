@@ -3,11 +3,13 @@
  *
  * Computes causal scaled dot-product multi-head attention
  *     O = softmax(Q K^T * scale + M) V        per (batch, query head)
- * with the grouped-query K/V head map, an optional sliding window, and the
- * KV-cache decode step.  The operation is the one defined in the attention
- * chapter of the LLM-architecture textbook ("Механизм внимания", sections
- * "Scaled dot-product attention", "Маскирование", "Виды по числу голов K/V",
- * "Скользящее окно", "KV-кэш" and "Prefill и decode").
+ * with the grouped-query K/V head map, an optional sliding window, the
+ * KV-cache decode step, chunked prefill against a cache, and the cache
+ * append.  The operation is the one defined in the attention chapter of the
+ * LLM-architecture textbook ("Механизм внимания", sections "Scaled
+ * dot-product attention", "Маскирование", "Виды по числу голов K/V",
+ * "Скользящее окно", "KV-кэш", "Prefill и decode" and "Прямой проход по
+ * шагам").
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers to dense row-major (contiguous)
@@ -73,6 +75,35 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
                  int dtype, void* stream);
 
 /*
+ * attn_prefill_cache -- chunked prefill: Sq new queries per sequence against
+ * a KV cache that already holds their keys (textbook, "Prefill и decode": a
+ * long prompt filled chunk by chunk, with the causal mask inside the chunk;
+ * "Прямой проход по шагам": mask rows start at the first new position).
+ *
+ *   Q       [B, Nq, Sq, Dh]      the chunk's queries
+ *   Kcache  [B, Nkv, Tcap, Dh]   keys; rows 0 .. lens[b]-1 hold sequence b's
+ *                                keys, the chunk's own Sq keys last
+ *   Vcache  [B, Nkv, Tcap, Dh]   values, same layout
+ *   lens    [B] int32, DEVICE    keys of each sequence including the chunk;
+ *                                must satisfy Sq <= lens[b] <= Tcap
+ *   O       [B, Nq, Sq, Dh]      output, same element type as Q
+ *   LSE     [B, Nq, Sq] fp32 or NULL
+ *   window   <= 0: none; > 0: only keys with pos - j < window are visible
+ *   scale    > 0 and finite (1/sqrt(Dh) for the standard definition)
+ * Query i of sequence b sits at position lens[b] - Sq + i (the mask is aligned
+ * at the bottom-right corner) and sees keys j <= its position.  Cache rows at
+ * or past lens[b] are never read.  With Sq == lens[b] this is attn_prefill.
+ * lens lives on the device: values above Tcap are clamped to Tcap, and a
+ * value below Sq leaves rows with no visible key (NaN).
+ * Supported: as attn_prefill (bf16 Dh == 128 takes the MFMA kernel).
+ * Errors: ATTN_EINVAL (also Sq > Tcap), ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O, float* LSE,
+                       int B, int Nq, int Nkv, int Sq, int Dh, int Tcap,
+                       int window, float scale, int dtype, void* stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
  * for these dimensions (0 when the chosen kernel needs none).  Pure host
  * function; returns 0 for invalid arguments.
@@ -105,6 +136,49 @@ int attn_decode(const void* q, const void* Kcache, const void* Vcache,
                 int B, int Nq, int Nkv, int Dh, int Tcap,
                 float* LSE, void* workspace, size_t workspace_bytes,
                 int dtype, void* stream);
+
+/*
+ * attn_decode_window -- attn_decode with a sliding window and an explicit
+ * scale (textbook, "Скользящее окно": with a window the new token sees only
+ * the recent past).  Arguments as attn_decode, plus
+ *   window   <= 0: every cached key; > 0: keys lens[b]-window .. lens[b]-1
+ *   scale    > 0 and finite
+ * The workspace is sized by attn_decode_workspace_bytes, as for attn_decode.
+ * A rolling-buffer cache of capacity W (see attn_kv_append) holds exactly
+ * the last W positions in some slot order; the softmax does not depend on
+ * that order, so it is decoded with lens = min(position + 1, W) and no
+ * window.
+ * Errors: as attn_decode.
+ */
+int attn_decode_window(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O,
+                       int B, int Nq, int Nkv, int Dh, int Tcap, int window, float scale,
+                       float* LSE, void* workspace, size_t workspace_bytes,
+                       int dtype, void* stream);
+
+/*
+ * attn_kv_append -- write the new tokens' K and V rows into the caches
+ * (textbook, "Прямой проход по шагам": the new K and V follow the cached
+ * ones; "Скользящее окно": a cache bounded by the window keeps only the last
+ * positions -- Mistral's rolling buffer).
+ *
+ *   Knew, Vnew      [B, Nkv, Snew, Dh]   new rows
+ *   Kcache, Vcache  [B, Nkv, Tcap, Dh]   caches, updated in place
+ *   pos     [B] int32, DEVICE   position of each sequence's first new token
+ *                               (its token count before the append)
+ *   rolling  0: row i goes to cache row pos[b] + i, which must be < Tcap;
+ *            1: row i goes to row (pos[b] + i) mod Tcap; when Snew > Tcap
+ *            only the last Tcap new rows are written
+ *   dtype    element type of all four buffers
+ * The caller updates its own lengths afterwards.  pos lives on the device: a
+ * negative value skips that sequence, and linear rows that would land at or
+ * past Tcap are dropped.
+ * Errors: ATTN_EINVAL (also rolling == 0 with Snew > Tcap), ATTN_EUNSUPPORTED
+ * (dtype, Dh > 256), ATTN_EHIP.
+ */
+int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
+                   const int32_t* pos, int B, int Nkv, int Snew, int Dh, int Tcap,
+                   int rolling, int dtype, void* stream);
 
 /* attn_strerror -- static description of an attn_status value. */
 const char* attn_strerror(int status);

@@ -124,3 +124,84 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tch.attn_prefill(q, q, q, q.clone(), None)
+
+
+def _prefill_cache(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, lens=FAKE, O=FAKE, LSE=None, B=2, Nq=8, Nkv=2, Sq=16,
+             Dh=128, Tcap=64, window=0, scale=0.125, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_prefill_cache(a["Q"], a["K"], a["V"], a["lens"], a["O"], a["LSE"],
+                                        a["B"], a["Nq"], a["Nkv"], a["Sq"], a["Dh"], a["Tcap"],
+                                        a["window"], a["scale"], a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), tch.ATTN_EINVAL),
+    (dict(lens=None), tch.ATTN_EINVAL),
+    (dict(O=None), tch.ATTN_EINVAL),
+    (dict(B=0), tch.ATTN_EINVAL),
+    (dict(Sq=0), tch.ATTN_EINVAL),
+    (dict(Tcap=0), tch.ATTN_EINVAL),
+    (dict(Sq=65), tch.ATTN_EINVAL),
+    (dict(Nq=6, Nkv=4), tch.ATTN_EGQA),
+    (dict(Dh=257), tch.ATTN_EUNSUPPORTED),
+    (dict(dtype=3), tch.ATTN_EUNSUPPORTED),
+    (dict(scale=0.0), tch.ATTN_EINVAL),
+    (dict(scale=float("nan")), tch.ATTN_EINVAL),
+])
+def test_prefill_cache_rejects(kw, code):
+    assert _prefill_cache(**kw) == code
+
+
+def _decode_window(**kw):
+    a = dict(q=FAKE, K=FAKE, V=FAKE, lens=FAKE, O=FAKE, B=2, Nq=8, Nkv=2, Dh=128, Tcap=64,
+             window=16, scale=0.1, LSE=None, ws=FAKE, ws_bytes=1 << 30, dtype=tch.ATTN_BF16,
+             stream=None)
+    a.update(kw)
+    return tch.lib().attn_decode_window(a["q"], a["K"], a["V"], a["lens"], a["O"], a["B"],
+                                        a["Nq"], a["Nkv"], a["Dh"], a["Tcap"], a["window"],
+                                        a["scale"], a["LSE"], a["ws"], a["ws_bytes"],
+                                        a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), tch.ATTN_EINVAL),
+    (dict(lens=None), tch.ATTN_EINVAL),
+    (dict(Tcap=0), tch.ATTN_EINVAL),
+    (dict(scale=-1.0), tch.ATTN_EINVAL),
+    (dict(scale=float("inf")), tch.ATTN_EINVAL),
+    (dict(Nq=8, Nkv=3), tch.ATTN_EGQA),
+    (dict(Dh=300), tch.ATTN_EUNSUPPORTED),
+    (dict(ws=None), tch.ATTN_EWORKSPACE),
+    (dict(ws_bytes=16), tch.ATTN_EWORKSPACE),
+])
+def test_decode_window_rejects(kw, code):
+    assert _decode_window(**kw) == code
+
+
+def _append(**kw):
+    a = dict(Kn=FAKE, Vn=FAKE, K=FAKE, V=FAKE, pos=FAKE, B=2, Nkv=2, Snew=4, Dh=128, Tcap=64,
+             rolling=0, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_kv_append(a["Kn"], a["Vn"], a["K"], a["V"], a["pos"], a["B"],
+                                    a["Nkv"], a["Snew"], a["Dh"], a["Tcap"], a["rolling"],
+                                    a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(Kn=None), tch.ATTN_EINVAL),
+    (dict(V=None), tch.ATTN_EINVAL),
+    (dict(pos=None), tch.ATTN_EINVAL),
+    (dict(B=0), tch.ATTN_EINVAL),
+    (dict(Snew=0), tch.ATTN_EINVAL),
+    (dict(Tcap=-1), tch.ATTN_EINVAL),
+    (dict(rolling=2), tch.ATTN_EINVAL),
+    (dict(Snew=65), tch.ATTN_EINVAL),
+    (dict(dtype=9), tch.ATTN_EUNSUPPORTED),
+    (dict(Dh=257), tch.ATTN_EUNSUPPORTED),
+])
+def test_kv_append_rejects(kw, code):
+    assert _append(**kw) == code

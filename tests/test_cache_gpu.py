@@ -1,0 +1,182 @@
+"""GPU parity of the cache-side entry points against the float64 oracle:
+chunked prefill against a cache (attn_prefill_cache), windowed decode
+(attn_decode_window), the cache append (attn_kv_append, linear and rolling),
+and generation end to end (chunked prefill, then appends and decode steps over
+a window-bounded rolling cache, against the one-pass oracle)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_causal_head_amd as tch
+import workloads
+from helpers import check, device, say
+
+pytestmark = pytest.mark.gpu
+
+
+class _Lazy:
+    """Widens cache slices to float64 on access (the caches can be large)."""
+
+    def __init__(self, arr, dtype):
+        self.arr, self.dtype, self.shape = arr, dtype, arr.shape
+
+    def __getitem__(self, idx):
+        return workloads.to_f64(self.arr[idx], self.dtype)
+
+
+def _run_chunk(Q, kc, vc, lens, dtype, window, scale=None):
+    dev = device()
+    tQ, tk, tv = (workloads.to_torch(x, dtype, dev) for x in (Q, kc, vc))
+    tl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(dev)
+    O, L = tch.prefill_cache(tQ, tk, tv, tl, window=window, scale=scale)
+    torch.cuda.synchronize()
+    return workloads.to_f64(workloads.from_torch(O, dtype), dtype), L.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,Sq,Tcap,lens,window", [
+    (2, 8, 2, 64, 300, [64, 300], 0),          # chunk of exactly one tile, ragged caches
+    (2, 8, 2, 100, 700, [100, 613], 0),
+    (3, 4, 4, 1, 257, [1, 2, 257], 0),         # one-row chunks
+    (2, 8, 2, 130, 1000, [130, 999], 64),      # window
+    (1, 32, 8, 257, 2048, [2048], 300),        # GQA 4, window, chunk past a query tile
+    (2, 4, 1, 300, 600, [300, 600], 0),        # MQA; sequence 0 is a plain prefill
+    (1, 8, 8, 40, 5000, [4321], 1),            # window 1: only the diagonal
+])
+def test_prefill_cache_bf16(B, Nq, Nkv, Sq, Tcap, lens, window):
+    lens_a, Q, kc, vc = workloads.chunk_inputs(B, Nq, Nkv, Sq, 128, Tcap, lens, "bf16", seed=Sq)
+    O, L = _run_chunk(Q, kc, vc, lens_a, "bf16", window)
+    Or, Lr = oracle.chunk_ref(workloads.to_f64(Q, "bf16"), _Lazy(kc, "bf16"), _Lazy(vc, "bf16"),
+                              lens_a, window=window)
+    say(f"prefill_cache {B, Nq, Nkv, Sq, Tcap, lens, window}: "
+        f"{check(O, L, Or, Lr, 'bf16', (Sq, lens, window), storage_allowance=True)}")
+
+
+@pytest.mark.parametrize("Dh,dtype,window", [(64, "f32", 0), (80, "bf16", 9), (128, "f32", 20)])
+def test_prefill_cache_general(Dh, dtype, window):
+    lens_a, Q, kc, vc = workloads.chunk_inputs(2, 4, 2, 33, Dh, 200, [33, 180], dtype, seed=Dh)
+    O, L = _run_chunk(Q, kc, vc, lens_a, dtype, window, scale=0.3)
+    Or, Lr = oracle.chunk_ref(workloads.to_f64(Q, dtype), workloads.to_f64(kc, dtype),
+                              workloads.to_f64(vc, dtype), lens_a, window=window, scale=0.3)
+    check(O, L, Or, Lr, dtype, (Dh, dtype, window), storage_allowance=True)
+
+
+@pytest.mark.parametrize("window", [0, 200])
+def test_chunked_prefill_pieces(window):
+    # a 1000-token prompt filled in four chunks equals the one-pass prefill
+    B, Nq, Nkv, S = 2, 8, 2, 1000
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, 128, "bf16", seed=77)
+    dev = device()
+    tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (k, v))
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
+                                  causal=True, window=window)
+    cuts = [0, 300, 301, 700, 1000]
+    for s0, s1 in zip(cuts[:-1], cuts[1:]):
+        tq = workloads.to_torch(np.ascontiguousarray(q[:, :, s0:s1]), "bf16", dev)
+        tl = torch.full((B,), s1, dtype=torch.int32, device=dev)
+        O, L = tch.prefill_cache(tq, tk, tv, tl, window=window)
+        torch.cuda.synchronize()
+        Og = workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16")
+        check(Og, L.cpu().numpy().astype(np.float64), Or[:, :, s0:s1], Lr[:, :, s0:s1], "bf16",
+              (s0, s1, window), storage_allowance=True)
+
+
+def _run_decode(q, kc, vc, lens, dtype, window, scale=None):
+    dev = device()
+    tq, tk, tv = (workloads.to_torch(x, dtype, dev) for x in (q, kc, vc))
+    tl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(dev)
+    O, L = tch.decode(tq, tk, tv, tl, window=window, scale=scale)
+    torch.cuda.synchronize()
+    return workloads.to_f64(workloads.from_torch(O, dtype), dtype), L.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,Tcap,lens,window", [
+    (6, 32, 8, 3000, [1, 31, 32, 33, 2000, 3000], 1),
+    (6, 32, 8, 3000, [1, 31, 32, 33, 2000, 3000], 32),
+    (6, 32, 8, 3000, [1, 31, 32, 33, 2000, 3000], 100),
+    (4, 16, 2, 5000, [4097, 5000, 97, 1000], 4096),
+    (3, 8, 8, 2100, [1024, 1025, 2048], 5000),          # window past every length
+    (16, 32, 8, 16384, None, 1000),                     # 384-key chunks, windows across them
+])
+def test_decode_window_bf16(B, Nq, Nkv, Tcap, lens, window):
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, 128, Tcap, 1, Tcap, seed=window,
+                                                lens=lens)
+    O, L = _run_decode(q, kc, vc, lens_a, "bf16", window)
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), _Lazy(kc, "bf16"), _Lazy(vc, "bf16"),
+                               lens_a, window=window)
+    say(f"decode window {window}: {check(O, L, Or, Lr, 'bf16', window, storage_allowance=True)}")
+
+
+@pytest.mark.parametrize("Dh,dtype,Nq,Nkv", [(64, "f32", 4, 2), (128, "bf16", 6, 2)])
+def test_decode_window_general(Dh, dtype, Nq, Nkv):
+    lens_a, q, kc, vc = workloads.decode_inputs(3, Nq, Nkv, Dh, 400, 1, 400, dtype, seed=Dh,
+                                                lens=[400, 17, 250])
+    O, L = _run_decode(q, kc, vc, lens_a, dtype, 40, scale=0.2)
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, dtype), workloads.to_f64(kc, dtype),
+                               workloads.to_f64(vc, dtype), lens_a, window=40, scale=0.2)
+    check(O, L, Or, Lr, dtype, (Dh, dtype), storage_allowance=True)
+
+
+@pytest.mark.parametrize("dtype,Dh,Snew,Tcap,pos,rolling", [
+    ("bf16", 128, 3, 50, [0, 47], 0),
+    ("bf16", 128, 7, 20, [15, 0], 1),
+    ("bf16", 128, 45, 20, [3, 40], 1),       # longer than the buffer: last 20 rows win
+    ("f32", 64, 5, 16, [11, 2], 0),
+    ("bf16", 3, 4, 9, [2, 8], 1),            # odd row length: 2-byte copies
+])
+def test_kv_append(dtype, Dh, Snew, Tcap, pos, rolling):
+    B, Nkv = 2, 3
+    dev = device()
+    kc = workloads.draw((B, Nkv, Tcap, Dh), dtype, 5, 1)
+    vc = workloads.draw((B, Nkv, Tcap, Dh), dtype, 5, 2)
+    kn = workloads.draw((B, Nkv, Snew, Dh), dtype, 5, 3)
+    vn = workloads.draw((B, Nkv, Snew, Dh), dtype, 5, 4)
+    tk, tv, tkn, tvn = (workloads.to_torch(x, dtype, dev) for x in (kc, vc, kn, vn))
+    tpos = torch.tensor(pos, dtype=torch.int32, device=dev)
+    tch.attn_kv_append(tkn, tvn, tk, tv, tpos, rolling=rolling)
+    torch.cuda.synchronize()
+    Kr, Vr = oracle.append_ref(kc, vc, kn, vn, pos, rolling=bool(rolling))
+    assert np.array_equal(workloads.from_torch(tk, dtype), Kr)  # bit-exact copy
+    assert np.array_equal(workloads.from_torch(tv, dtype), Vr)
+
+
+@pytest.mark.parametrize("mode", ["rolling", "linear"])
+def test_generation_over_window_cache(mode):
+    # the textbook's walk-through at attention-kernel scale: a 200-token prompt
+    # by chunked prefill, then 40 tokens one at a time, window 64; each output
+    # row must match the one-pass oracle
+    Nq, Nkv, Dh, T, P, W = 32, 8, 128, 240, 200, 64
+    q, k, v = workloads.prefill_inputs(1, Nq, Nkv, T, Dh, "bf16", seed=91)
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
+                                  causal=True, window=W)
+    dev = device()
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+    # prompt: its K/V form a linear cache, the chunk is the whole prompt
+    O, L = tch.prefill_cache(tq[:, :, :P].contiguous(), tk[:, :, :P].contiguous(),
+                             tv[:, :, :P].contiguous(),
+                             torch.tensor([P], dtype=torch.int32, device=dev), window=W)
+    torch.cuda.synchronize()
+    check(workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16"),
+          L.cpu().numpy().astype(np.float64), Or[:, :, :P], Lr[:, :, :P], "bf16", "prompt",
+          storage_allowance=True)
+    cap = W if mode == "rolling" else T
+    Kc = torch.full((1, Nkv, cap, Dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    Vc = torch.full((1, Nkv, cap, Dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    tch.attn_kv_append(tk[:, :, :P].contiguous(), tv[:, :, :P].contiguous(), Kc, Vc, zero,
+                       rolling=int(mode == "rolling"))
+    for t in range(P, T):
+        pos = torch.tensor([t], dtype=torch.int32, device=dev)
+        tch.attn_kv_append(tk[:, :, t:t + 1].contiguous(), tv[:, :, t:t + 1].contiguous(), Kc, Vc,
+                           pos, rolling=int(mode == "rolling"))
+        qt = tq[:, :, t].contiguous()
+        if mode == "rolling":   # the buffer holds exactly the window: attend to all of it
+            O, L = tch.decode(qt, Kc, Vc, torch.tensor([min(t + 1, W)], dtype=torch.int32,
+                                                       device=dev))
+        else:
+            O, L = tch.decode(qt, Kc, Vc, pos + 1, window=W)
+        torch.cuda.synchronize()
+        check(workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16"),
+              L.cpu().numpy().astype(np.float64), Or[:, :, t], Lr[:, :, t], "bf16", (mode, t),
+              storage_allowance=True)

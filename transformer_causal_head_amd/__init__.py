@@ -7,12 +7,17 @@ library is missing, every call raises.
 
 Entry points (same names as the C ABI):
     attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None)
+    attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, stream=None)
     attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=None)
+    attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None,
+                       window=0, scale=None, stream=None)
     attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype)
+    attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None)
     attn_strerror(status)
 Conveniences that allocate outputs with torch:
     prefill(q, k, v, causal=True, window=0, scale=None) -> (O, LSE)
-    decode(q, Kcache, Vcache, lens) -> (O, LSE)
+    prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
+    decode(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
 """
 
 import ctypes
@@ -31,7 +36,8 @@ ATTN_EHIP = -5
 ATTN_BF16 = 0
 ATTN_F32 = 1
 
-EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_workspace_bytes", "attn_strerror")
+EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
+           "attn_decode_workspace_bytes", "attn_kv_append", "attn_strerror")
 
 _lib = None
 
@@ -60,6 +66,14 @@ def lib():
         L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                   ctypes.c_size_t, i32, vp]
         L.attn_decode.restype = i32
+        L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, f32, i32, vp]
+        L.attn_prefill_cache.restype = i32
+        L.attn_decode_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                         vp, vp, ctypes.c_size_t, i32, vp]
+        L.attn_decode_window.restype = i32
+        L.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        L.attn_kv_append.restype = i32
         L.attn_strerror.argtypes = [i32]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -119,8 +133,7 @@ def attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype):
     return int(lib().attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype))
 
 
-def attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=None):
-    """q [B,Nq,Dh], caches [B,Nkv,Tcap,Dh], lens int32 [B] on the GPU, O like q."""
+def _check_decode(q, Kcache, Vcache, lens, O, LSE):
     import torch
     B, Nq, Dh = q.shape
     Nkv, Tcap = Kcache.shape[1], Kcache.shape[2]
@@ -130,12 +143,73 @@ def attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=Non
         raise ValueError("O must match q; lens must be int32 [B]")
     if LSE is not None and (tuple(LSE.shape) != (B, Nq) or LSE.dtype.itemsize != 4):
         raise ValueError("LSE must be fp32 [B, Nq]")
+    return B, Nq, Nkv, Dh, Tcap
+
+
+def attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=None):
+    """q [B,Nq,Dh], caches [B,Nkv,Tcap,Dh], lens int32 [B] on the GPU, O like q."""
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().attn_decode(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O), B, Nq,
                            Nkv, Dh, Tcap, _ptr(LSE), _ptr(workspace), ws_bytes,
                            _dtype_code(q), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+
+
+def attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, window=0,
+                       scale=None, stream=None):
+    """attn_decode with a sliding window (keys lens-window .. lens-1) and a scale."""
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_window(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O), B,
+                                  Nq, Nkv, Dh, Tcap, int(window), float(scale), _ptr(LSE),
+                                  _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_window")
+
+
+def attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, stream=None):
+    """Q [B,Nq,Sq,Dh] against caches [B,Nkv,Tcap,Dh]; lens int32 [B] on the GPU."""
+    import torch
+    B, Nq, Sq, Dh = Q.shape
+    Nkv, Tcap = Kcache.shape[1], Kcache.shape[2]
+    if tuple(Kcache.shape) != (B, Nkv, Tcap, Dh) or Kcache.shape != Vcache.shape:
+        raise ValueError("cache shapes must be [B, Nkv, Tcap, Dh]")
+    if O.shape != Q.shape or lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+        raise ValueError("O must match Q; lens must be int32 [B]")
+    if not (Q.dtype == Kcache.dtype == Vcache.dtype == O.dtype):
+        raise ValueError("Q, caches and O must share one dtype")
+    if LSE is not None and (tuple(LSE.shape) != (B, Nq, Sq) or LSE.dtype.itemsize != 4):
+        raise ValueError("LSE must be fp32 [B, Nq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    st = lib().attn_prefill_cache(_ptr(Q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O),
+                                  _ptr(LSE), B, Nq, Nkv, Sq, Dh, Tcap, int(window), float(scale),
+                                  _dtype_code(Q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill_cache")
+
+
+def attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None):
+    """New rows [B,Nkv,Snew,Dh] into caches [B,Nkv,Tcap,Dh] at pos (int32 [B], GPU)."""
+    import torch
+    B, Nkv, Snew, Dh = Knew.shape
+    Tcap = Kcache.shape[2]
+    if Knew.shape != Vnew.shape or tuple(Kcache.shape) != (B, Nkv, Tcap, Dh) \
+            or Kcache.shape != Vcache.shape:
+        raise ValueError("new rows must be [B, Nkv, Snew, Dh] and caches [B, Nkv, Tcap, Dh]")
+    if not (Knew.dtype == Vnew.dtype == Kcache.dtype == Vcache.dtype):
+        raise ValueError("all four buffers must share one dtype")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be int32 [B]")
+    st = lib().attn_kv_append(_ptr(Knew), _ptr(Vnew), _ptr(Kcache), _ptr(Vcache), _ptr(pos), B,
+                              Nkv, Snew, Dh, Tcap, int(rolling), _dtype_code(Knew),
+                              _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_append")
 
 
 def prefill(q, k, v, causal=True, window=0, scale=None):
@@ -147,8 +221,18 @@ def prefill(q, k, v, causal=True, window=0, scale=None):
     return O, LSE
 
 
-def decode(q, Kcache, Vcache, lens):
-    """Allocate O, LSE and the workspace with torch and run attn_decode."""
+def prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None):
+    """Allocate O and LSE with torch and run attn_prefill_cache."""
+    import torch
+    O = torch.empty_like(q)
+    LSE = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_prefill_cache(q, Kcache, Vcache, lens, O, LSE, window=window, scale=scale)
+    return O, LSE
+
+
+def decode(q, Kcache, Vcache, lens, window=0, scale=None):
+    """Allocate O, LSE and the workspace with torch and run attn_decode (or, with a
+    window or an explicit scale, attn_decode_window)."""
     import torch
     B, Nq, Dh = q.shape
     O = torch.empty_like(q)
@@ -156,5 +240,8 @@ def decode(q, Kcache, Vcache, lens):
     nbytes = attn_decode_workspace_bytes(B, Nq, Kcache.shape[1], Dh, Kcache.shape[2],
                                          _dtype_code(q))
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
-    attn_decode(q, Kcache, Vcache, lens, O, LSE, ws)
+    if window or scale is not None:
+        attn_decode_window(q, Kcache, Vcache, lens, O, LSE, ws, window=window, scale=scale)
+    else:
+        attn_decode(q, Kcache, Vcache, lens, O, LSE, ws)
     return O, LSE

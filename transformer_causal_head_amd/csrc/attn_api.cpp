@@ -38,10 +38,28 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
   if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && Dh == 128)
-    return from_hip(attn::launch_prefill_bf16_d128(Q, K, V, O, LSE, B, Nq, Nkv, S, causal,
-                                                   window, scale, s));
+    return from_hip(attn::launch_prefill_bf16_d128(Q, K, V, O, LSE, B, Nq, Nkv, S, S, nullptr,
+                                                   causal, window, scale, s));
   return from_hip(attn::launch_rows_general(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
                                             causal, window, scale, dtype == ATTN_BF16, s));
+}
+
+int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O, float* LSE, int B, int Nq, int Nkv,
+                       int Sq, int Dh, int Tcap, int window, float scale, int dtype,
+                       void* stream) {
+  if (!Q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
+  int st = validate_common(B, Nq, Nkv, Dh, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive(Sq) || !positive(Tcap) || Sq > Tcap) return ATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  if (window < 0) window = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16 && Dh == 128)
+    return from_hip(attn::launch_prefill_bf16_d128(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq,
+                                                   Tcap, lens, 1, window, scale, s));
+  return from_hip(attn::launch_rows_general(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
+                                            lens, 1, window, scale, dtype == ATTN_BF16, s));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int dtype) {
@@ -51,23 +69,56 @@ size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int
   return 0;
 }
 
-int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
-                void* O, int B, int Nq, int Nkv, int Dh, int Tcap, float* LSE, void* workspace,
-                size_t workspace_bytes, int dtype, void* stream) {
+static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                       int window, float scale, float* LSE, void* workspace,
+                       size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
   if (!positive(Tcap)) return ATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t need = attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
     return from_hip(attn::launch_decode_bf16_d128(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv,
-                                                  Tcap, workspace, s));
+                                                  Tcap, window, scale, workspace, s));
   }
   return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap,
-                                            lens, 1, 0, 1.0f / sqrtf((float)Dh),
-                                            dtype == ATTN_BF16, s));
+                                            lens, 1, window, scale, dtype == ATTN_BF16, s));
+}
+
+int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
+                void* O, int B, int Nq, int Nkv, int Dh, int Tcap, float* LSE, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  const float scale = Dh > 0 ? 1.0f / sqrtf((float)Dh) : 1.0f;
+  return decode_impl(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, 0, scale, LSE, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int attn_decode_window(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                       int window, float scale, float* LSE, void* workspace,
+                       size_t workspace_bytes, int dtype, void* stream) {
+  return decode_impl(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, window, scale, LSE,
+                     workspace, workspace_bytes, dtype, stream);
+}
+
+int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
+                   const int32_t* pos, int B, int Nkv, int Snew, int Dh, int Tcap, int rolling,
+                   int dtype, void* stream) {
+  if (!Knew || !Vnew || !Kcache || !Vcache || !pos) return ATTN_EINVAL;
+  if (!positive(B) || !positive(Nkv) || !positive(Snew) || !positive(Dh) || !positive(Tcap))
+    return ATTN_EINVAL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_EUNSUPPORTED;
+  if (Dh > 256) return ATTN_EUNSUPPORTED;
+  if (rolling != 0 && rolling != 1) return ATTN_EINVAL;
+  if (!rolling && Snew > Tcap) return ATTN_EINVAL;
+  return from_hip(attn::launch_kv_append(Knew, Vnew, Kcache, Vcache, pos, B, Nkv, Snew, Dh, Tcap,
+                                         rolling, dtype == ATTN_BF16 ? 2 : 4,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 const char* attn_strerror(int status) {

@@ -2,7 +2,9 @@
 //
 // The step is one query row per sequence against its cached keys (textbook
 // attention chapter, "KV-кэш" and "Prefill и decode": a 1 x t score row;
-// decode is bound by reading the cache).  The key axis of every (sequence,
+// decode is bound by reading the cache).  With a window the query sees only
+// the last `window` keys (section "Скользящее окно", i - j < window); chunks
+// wholly before that range do nothing.  The key axis of every (sequence,
 // K/V head) is cut into chunks; each chunk yields a partial (running max m,
 // running sum l, unnormalised output o) for the G query heads that share the
 // K/V head, and a second kernel merges the partials with the same rescaling
@@ -66,6 +68,7 @@ struct DecParams {
   float* ws_ml;   // [B, Nkv, n_chunks, G, 2]  (m in log2 units, l)
   int B, Nq, Nkv, G, Tcap, n_chunks;
   int ch;         // keys per chunk (a multiple of STEP)
+  int window;     // > 0: only keys lens[b] - window .. lens[b] - 1 are visible
   float c;        // scale * log2(e)
 };
 
@@ -116,8 +119,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int n = min(p.lens[b], p.Tcap);
+  const int lo = p.window > 0 ? max(0, n - p.window) : 0;  // first visible key
   const int c0 = chunk * p.ch;
-  if (c0 >= n) return;
+  if (c0 >= n || c0 + p.ch <= lo) return;
+  const int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
   const int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
   const int last = min(n, c0 + p.ch) - 1;
 
@@ -148,10 +153,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // for two steps past the chunk's end too (all rows clamp to its last row
   // and mostly hit L2), so that count holds on every path and the compiler
   // adds no full drain of its own.
-  load_rows<true>(Kh, c0, last, K0, lane);
-  load_rows<false>(Vh, c0, last, V0, lane);
-  load_rows<true>(Kh, c0 + STEP, last, K1, lane);
-  load_rows<false>(Vh, c0 + STEP, last, V1, lane);
+  load_rows<true>(Kh, c0 + s0 * STEP, last, K0, lane);
+  load_rows<false>(Vh, c0 + s0 * STEP, last, V0, lane);
+  load_rows<true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
+  load_rows<false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
 
   // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
   // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
@@ -190,18 +195,20 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc[kb], 0, 0, 0);
       }
     }
-    if (k0 + STEP > n) {
+    if (k0 + STEP > n || k0 < lo) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (k0 + kb * 16 + grp * 4 + r >= n) sc[kb][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kb * 16 + grp * 4 + r;
+          if (key >= n || key < lo) sc[kb][r] = -INFINITY;
+        }
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_cand = mx * p.c;  // the step's first key is valid: finite
+    const float m_cand = mx * p.c;  // every step run holds a visible key: finite
     if (__builtin_amdgcn_ballot_w64(m_cand > m_run + TAU)) {
       const float m_new = fmaxf(m_run, m_cand);
       const float alpha = exp2_fast(m_run - m_new);
@@ -237,10 +244,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   };
 
-  // Steps in pairs: even steps use stage 0, odd steps stage 1.  Before step s
-  // the copies of steps s and s + 1 are outstanding; once step s has read its
-  // stage, the copies of step s + 2 go into it.
-  for (int s = 0; s < nsteps; s += 2) {
+  // Steps in pairs from s0: the first of a pair uses stage 0, the second stage
+  // 1.  Before step s the copies of steps s and s + 1 are outstanding; once
+  // step s has read its stage, the copies of step s + 2 go into it.
+  for (int s = s0; s < nsteps; s += 2) {
     wait_vm<16>();
     step(s, K0, V0);
     load_rows<true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
@@ -283,13 +290,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int hh = h % G;
   const int n = min(p.lens[b], p.Tcap);
   const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
+  const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;  // first chunk with a partial
   const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_chunks * G + hh;  // chunk c: part0 + c*G
 
   float M = -INFINITY;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)c * G) * 2]);
+  for (int c = c_lo + lane; c < nc; c += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)c * G) * 2]);
   M = wave_max(M);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int cb = 0; cb < nc; cb += 64) {
+  for (int cb = c_lo; cb < nc; cb += 64) {
     // lane j of this batch holds chunk cb + j's weight
     float wgt = 0.f;
     if (cb + lane < nc) {
@@ -350,7 +358,8 @@ size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap) {
 
 hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
                                    const int32_t* lens, void* O, float* LSE, int B, int Nq,
-                                   int Nkv, int Tcap, void* ws, hipStream_t stream) {
+                                   int Nkv, int Tcap, int window, float scale, void* ws,
+                                   hipStream_t stream) {
   DecParams p;
   p.q = static_cast<const __bf16*>(q);
   p.K = static_cast<const __bf16*>(Kc);
@@ -368,7 +377,8 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
   const size_t parts = (size_t)B * Nq * p.n_chunks;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * D;
-  p.c = kLog2e / sqrtf((float)D);
+  p.window = window;
+  p.c = kLog2e * scale;
   if (Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_chunks, Nkv, B), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();

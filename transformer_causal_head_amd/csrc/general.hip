@@ -7,8 +7,11 @@
 // Definition followed: softmax(q K^T * scale + M) V for one query row
 // (textbook attention chapter, "Scaled dot-product attention"), with the
 // causal / window visibility of sections "Маскирование" and "Скользящее окно"
-// (visible iff j <= i and i - j < window), and the decode row of section
-// "Prefill и decode" (the new query sees every cached key).
+// (visible iff j <= i and i - j < window).  Query row i of a head sits at
+// position i in a plain prefill, and at position n - S + i when S rows are
+// the newest tokens of a cache of n keys (chunked prefill; a decode step is
+// the case S = 1, whose query sees every cached key -- section
+// "Prefill и decode").
 
 #include <math.h>
 
@@ -25,8 +28,8 @@ struct RowParams {
   const void* V;
   void* O;
   float* LSE;
-  int B, Nq, Nkv, S, Dh, kv_rows;
-  const int32_t* lens;
+  int B, Nq, Nkv, S, Dh, kv_rows;  // S: query rows per head
+  const int32_t* lens;              // keys per sequence in a cache, or null
   int causal, window;
   float scale;
   long long n_rows;
@@ -44,23 +47,17 @@ __global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
   T* O = static_cast<T*>(p.O);
   const int G = p.Nq / p.Nkv;
 
-  int b, h, i, lo, hi;
-  if (p.lens == nullptr) {  // prefill row (b, h, i)
-    i = (int)(row % p.S);
-    const long long bh = row / p.S;
-    h = (int)(bh % p.Nq);
-    b = (int)(bh / p.Nq);
-    hi = p.causal ? i + 1 : p.S;
-    lo = (p.causal && p.window > 0) ? max(0, i - p.window + 1) : 0;
-  } else {  // decode row (b, h): keys 0 .. lens[b]-1
-    i = 0;
-    h = (int)(row % p.Nq);
-    b = (int)(row / p.Nq);
-    lo = 0;
-    hi = min(p.lens[b], p.kv_rows);
-  }
+  // row (b, h, i); n keys; query position pos; visible keys [lo, hi)
+  const int i = (int)(row % p.S);
+  const long long bh = row / p.S;
+  const int h = (int)(bh % p.Nq);
+  const int b = (int)(bh / p.Nq);
+  const int n = p.lens ? max(0, min(p.lens[b], p.kv_rows)) : p.S;
+  const int pos = p.lens ? n - p.S + i : i;
+  const int hi = p.causal ? min(pos + 1, n) : n;
+  const int lo = (p.causal && p.window > 0) ? max(0, pos - p.window + 1) : 0;
   const int g = h / G;
-  const size_t qoff = (((size_t)b * p.Nq + h) * (p.lens ? 1 : p.S) + i) * p.Dh;
+  const size_t qoff = (size_t)row * p.Dh;
   const size_t kvoff = ((size_t)b * p.Nkv + g) * (size_t)p.kv_rows * p.Dh;
 
   float q[4], o[4];
@@ -124,7 +121,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
   p.causal = causal;
   p.window = window;
   p.scale = scale;
-  p.n_rows = (long long)B * Nq * (lens ? 1 : S);
+  p.n_rows = (long long)B * Nq * S;
   const long long nblocks = (p.n_rows + 3) / 4;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (is_bf16)

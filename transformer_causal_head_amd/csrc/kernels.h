@@ -7,26 +7,40 @@
 
 namespace attn {
 
-// bf16, Dh == 128 MFMA prefill.
+// bf16, Dh == 128 MFMA prefill.  S query rows per head; K/V heads of
+// kv_rows rows.  lens == nullptr: plain prefill (S keys, query i at position
+// i).  Otherwise sequence b has lens[b] keys and query i sits at position
+// lens[b] - S + i (chunked prefill against a cache).
 hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
-                                    float* LSE, int B, int Nq, int Nkv, int S, int causal,
-                                    int window, float scale, hipStream_t stream);
+                                    float* LSE, int B, int Nq, int Nkv, int S, int kv_rows,
+                                    const int32_t* lens, int causal, int window, float scale,
+                                    hipStream_t stream);
 
-// General row kernel: one wavefront per output row, any Dh in 1..256,
-// bf16 (is_bf16 = 1) or fp32.  Prefill when lens == nullptr (rows (b,h,i),
-// K/V heads of S rows); decode otherwise (rows (b,h), K/V heads of kv_rows
-// rows, sequence b reads keys 0..lens[b]-1).
+// General row kernel: one wavefront per output row (b, h, i), any Dh in
+// 1..256, bf16 (is_bf16 = 1) or fp32.  Same row/key convention as the MFMA
+// prefill; a decode step is S = 1 with lens (its query sees keys
+// lens[b] - window .. lens[b] - 1, or all of them without a window).
 hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void* O,
                                float* LSE, int B, int Nq, int Nkv, int S, int Dh,
                                int kv_rows, const int32_t* lens, int causal, int window,
                                float scale, int is_bf16, hipStream_t stream);
 
-// bf16, Dh == 128 split-K decode (partials + log-sum-exp merge).
+// bf16, Dh == 128 split-K decode (partials + log-sum-exp merge).  The query
+// of sequence b sees keys max(0, lens[b] - window) .. lens[b] - 1 (window 0:
+// all of them).
 int decode_bf16_d128_chunk(int B, int Nkv, int Tcap);
 size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap);
 bool decode_bf16_d128_supported(int Nq, int Nkv);
 hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
                                    const int32_t* lens, void* O, float* LSE, int B, int Nq,
-                                   int Nkv, int Tcap, void* ws, hipStream_t stream);
+                                   int Nkv, int Tcap, int window, float scale, void* ws,
+                                   hipStream_t stream);
+
+// Copy Snew new K and V rows per (sequence, K/V head) into the caches at
+// positions pos[b] .. pos[b] + Snew - 1, or at those positions modulo Tcap
+// (rolling buffer).  elem_bytes: 2 (bf16) or 4 (fp32).
+hipError_t launch_kv_append(const void* Knew, const void* Vnew, void* Kc, void* Vc,
+                            const int32_t* pos, int B, int Nkv, int Snew, int Dh, int Tcap,
+                            int rolling, int elem_bytes, hipStream_t stream);
 
 }  // namespace attn

@@ -96,7 +96,9 @@ struct Params {
   const __bf16* V;
   __bf16* O;
   float* LSE;
-  int B, Nq, Nkv, S;
+  const int32_t* lens;  // keys per sequence in a cache (chunked prefill), or null
+  int B, Nq, Nkv, S;    // S: query rows per head
+  int kv_rows;          // rows per K/V head in memory (S, or the cache capacity)
   int causal, window;
   float c;        // scale * log2(e)
   int G;          // query heads per K/V head
@@ -230,19 +232,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int g = rest % p.Nkv;
   const int b = rest / p.Nkv;
 
-  const int head = g * p.G + hsub * p.hp + (w % p.hp);
-  const int qa = qt * p.qspan + (w / p.hp) * QW;  // first query of this wave
-  const int q0 = qt * p.qspan;
-  const int q1 = min(p.S, q0 + p.qspan);
-  const int wq1 = min(p.S, qa + QW);
-  const bool wave_live = qa < p.S;
+  // Keys of this sequence and the absolute position of query row 0: a plain
+  // prefill has S keys and starts at 0; a chunk of S queries against a cache
+  // of lens[b] keys sits at the cache's end (positions lens[b] - S ..).
+  const int n_keys = p.lens ? max(0, min(p.lens[b], p.kv_rows)) : p.S;
+  const int q_off = p.lens ? n_keys - p.S : 0;
 
-  const HeadRef Kh = head_ref(p.K + ((size_t)b * p.Nkv + g) * (size_t)p.S * D, p.S);
-  const HeadRef Vh = head_ref(p.V + ((size_t)b * p.Nkv + g) * (size_t)p.S * D, p.S);
+  const int head = g * p.G + hsub * p.hp + (w % p.hp);
+  const int qa_row = qt * p.qspan + (w / p.hp) * QW;  // first query row of this wave
+  const int qa = q_off + qa_row;                      // ... and its position
+  const int q0 = q_off + qt * p.qspan;
+  const int q1 = q_off + min(p.S, qt * p.qspan + p.qspan);
+  const int wq1 = q_off + min(p.S, qa_row + QW);
+  const bool wave_live = qa_row < p.S;
+
+  const size_t kv_base = ((size_t)b * p.Nkv + g) * (size_t)p.kv_rows * D;
+  const HeadRef Kh = head_ref(p.K + kv_base, n_keys);
+  const HeadRef Vh = head_ref(p.V + kv_base, n_keys);
   const size_t q_base = ((size_t)b * p.Nq + head) * (size_t)p.S * D;
 
   // key range of the workgroup
-  const int hi_key = p.causal ? q1 : p.S;
+  const int hi_key = p.causal ? q1 : n_keys;
   const int lo_key = (p.causal && p.window > 0) ? max(0, q0 - p.window + 1) : 0;
   const int t_lo = lo_key / BN;
   const int nt = (hi_key + BN - 1) / BN - t_lo;
@@ -253,15 +263,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   char* const V1 = v1s;
 
   // start the copies first, they overlap the set-up below
-  load_tile(Kh, t_lo * BN, p.S, K0, w, lane);
-  load_tile(Vh, t_lo * BN, p.S, V0, w, lane);
-  if (PIPE && nt > 1) load_tile(Kh, (t_lo + 1) * BN, p.S, K1, w, lane);
+  load_tile(Kh, t_lo * BN, n_keys, K0, w, lane);
+  load_tile(Vh, t_lo * BN, n_keys, V0, w, lane);
+  if (PIPE && nt > 1) load_tile(Kh, (t_lo + 1) * BN, n_keys, K1, w, lane);
 
   // Q^T operand fragments: query column ln of block qb, d = 16*ks + 8*hl + i
   bf16x8 qf[QB][8];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = min(qa + qb * 32 + ln, p.S - 1);
+    const int qrow = min(qa_row + qb * 32 + ln, p.S - 1);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.Q + q_base + (size_t)qrow * D + hl * 8);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = src[ks * 2];
@@ -299,10 +309,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   // only visible pairs (no mask needed).  floor division by BN = 64.
   auto fdiv = [](int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); };
   int tl_lo = p.window > 0 ? fdiv(qa - p.window + 1) : -1;
-  int tl_hi = p.causal ? fdiv(wq1 - 1) : (p.S - 1) / BN;
+  int tl_hi = p.causal ? fdiv(wq1 - 1) : fdiv(n_keys - 1);
   if (!wave_live) tl_hi = tl_lo - 1;
   int tf_lo = p.window > 0 ? -fdiv(-(wq1 - p.window)) : 0;  // ceil((wq1 - window) / 64)
-  int tf_hi = fdiv(p.S - BN);
+  int tf_hi = fdiv(n_keys - BN);
   if (p.causal) tf_hi = min(tf_hi, fdiv(qa - (BN - 1)));
   tl_lo = __builtin_amdgcn_readfirstlane(tl_lo);
   tl_hi = __builtin_amdgcn_readfirstlane(tl_hi);
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = qa + qb * 32 + ln;
-    key_hi[qb] = p.causal ? min(qi, p.S - 1) : p.S - 1;
+    key_hi[qb] = p.causal ? min(qi, n_keys - 1) : n_keys - 1;
     key_lo[qb] = p.window > 0 ? qi - p.window + 1 : 0;
   }
   auto mask_tile = [&](int t, f32x16 (&s)[QB][2]) {
@@ -409,8 +419,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
       char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
       wait_dma();
       __syncthreads();
-      if (i + 2 < nt) load_tile(Kh, (t + 2) * BN, p.S, Kcur, w, lane);
-      if (i + 1 < nt) load_tile(Vh, (t + 1) * BN, p.S, Vnext, w, lane);
+      if (i + 2 < nt) load_tile(Kh, (t + 2) * BN, n_keys, Kcur, w, lane);
+      if (i + 1 < nt) load_tile(Vh, (t + 1) * BN, n_keys, Vnext, w, lane);
       if (i + 1 < nt && live(t + 1)) qk_tile<QB>(Knext, koff, qf, s_next);
       if (live(t)) softmax_pv(t, s_cur, Vcur);
     };
@@ -430,8 +440,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
       wait_dma();
       __syncthreads();
       if (i + 1 < nt) {
-        load_tile(Kh, (t + 1) * BN, p.S, (i & 1) ? K0 : K1, w, lane);
-        load_tile(Vh, (t + 1) * BN, p.S, (i & 1) ? V0 : V1, w, lane);
+        load_tile(Kh, (t + 1) * BN, n_keys, (i & 1) ? K0 : K1, w, lane);
+        load_tile(Vh, (t + 1) * BN, n_keys, (i & 1) ? V0 : V1, w, lane);
       }
       if (live(t)) {
         qk_tile<QB>((i & 1) ? K1 : K0, koff, qf, s);
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   // epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qa + qb * 32 + ln;
+    const int qi = qa_row + qb * 32 + ln;  // query row
     const float l_tot = xhalf_sum(l_run[qb]);
     if (qi >= p.S) continue;
     const float inv = 1.f / l_tot;
@@ -467,20 +477,24 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
-                                    float* LSE, int B, int Nq, int Nkv, int S, int causal,
-                                    int window, float scale, hipStream_t stream) {
+                                    float* LSE, int B, int Nq, int Nkv, int S, int kv_rows,
+                                    const int32_t* lens, int causal, int window, float scale,
+                                    hipStream_t stream) {
   // one head of K (or V) is addressed through a 31-bit buffer range
-  if ((long long)S * D * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
+  if ((long long)kv_rows * D * 2 > 0x7fffffffLL || (long long)S * D * 2 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
   Params p;
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
   p.V = static_cast<const __bf16*>(V);
   p.O = static_cast<__bf16*>(O);
   p.LSE = LSE;
+  p.lens = lens;
   p.B = B;
   p.Nq = Nq;
   p.Nkv = Nkv;
   p.S = S;
+  p.kv_rows = kv_rows;
   p.causal = causal;
   p.window = window;
   p.c = scale * kLog2e;

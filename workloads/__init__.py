@@ -168,6 +168,17 @@ def decode_inputs(B, Nq, Nkv, Dh, Tcap, len_lo, len_hi, dtype="bf16", seed=0,
     return lens.astype(np.int32), q, kc, vc
 
 
+def chunk_inputs(B, Nq, Nkv, Sq, Dh, Tcap, lens, dtype="bf16", seed=0):
+    """lens, Q [B,Nq,Sq,Dh], Kcache, Vcache for a chunk of Sq queries per
+    sequence whose keys are the last Sq of lens[b] cached rows (caches drawn as
+    in decode_inputs, NaN past each length; Q is stream 11)."""
+    lens, _, kc, vc = decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, dtype, seed, lens=lens)
+    if int(np.min(lens)) < Sq:
+        raise ValueError("every length must cover the chunk")
+    Q = draw((B, Nq, Sq, Dh), dtype, seed, 11)
+    return lens, Q, kc, vc
+
+
 def sample_rows(B, Nq, S, n, seed=1, forced_rows=()):
     """Seeded (b, h, i) output rows to check on a long workload."""
     rng = np.random.default_rng(seed)
