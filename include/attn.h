@@ -143,7 +143,8 @@ int attn_decode(const void* q, const void* Kcache, const void* Vcache,
  * the recent past).  Arguments as attn_decode, plus
  *   window   <= 0: every cached key; > 0: keys lens[b]-window .. lens[b]-1
  *   scale    > 0 and finite
- * The workspace is sized by attn_decode_workspace_bytes, as for attn_decode.
+ * The workspace must hold attn_decode_window_workspace_bytes(..., window, ...)
+ * bytes (a short window splits into shorter chunks, so the size depends on it).
  * A rolling-buffer cache of capacity W (see attn_kv_append) holds exactly
  * the last W positions in some slot order; the softmax does not depend on
  * that order, so it is decoded with lens = min(position + 1, W) and no
@@ -155,6 +156,15 @@ int attn_decode_window(const void* q, const void* Kcache, const void* Vcache,
                        int B, int Nq, int Nkv, int Dh, int Tcap, int window, float scale,
                        float* LSE, void* workspace, size_t workspace_bytes,
                        int dtype, void* stream);
+
+/*
+ * attn_decode_window_workspace_bytes -- bytes of device workspace
+ * attn_decode_window needs for these dimensions and this window (0 when the
+ * chosen kernel needs none; window <= 0 gives attn_decode_workspace_bytes).
+ * Pure host function; returns 0 for invalid arguments.
+ */
+size_t attn_decode_window_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int window,
+                                          int dtype);
 
 /*
  * attn_kv_append -- write the new tokens' K and V rows into the caches

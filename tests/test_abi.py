@@ -53,6 +53,13 @@ def test_workspace_query():
     assert tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_F32) == 0
     assert tch.attn_decode_workspace_bytes(64, 30, 8, 128, 32768, tch.ATTN_BF16) == 0
     assert tch.attn_decode_workspace_bytes(0, 32, 8, 128, 32768, tch.ATTN_BF16) == 0
+    # a window shorter than the cache: shorter chunks, and only the chunks a
+    # window can touch get a slot
+    assert tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 0, tch.ATTN_BF16) == n
+    nw = tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 1024, tch.ATTN_BF16)
+    assert nw > 0 and nw % rec == 0 and nw // rec <= 32
+    assert tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 40000,
+                                                  tch.ATTN_BF16) == n
 
 
 FAKE = ctypes.c_void_p(0x1000)

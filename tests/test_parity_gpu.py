@@ -233,18 +233,20 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
 
 def _decode_chunk(B, Nkv, Tcap):
     # the host's choice of keys per chunk, restated: the longest candidate that
-    # gives at least 4096 (sequence, K/V head, chunk) items at full length
+    # gives at least 2048 (sequence, K/V head, chunk) items at full length
     for ch in (1792, 1152, 896, 640, 384, 224, 160, 96):
-        if B * Nkv * -(-Tcap // ch) >= 4096:
+        if B * Nkv * -(-Tcap // ch) >= 2048:
             return ch
     return 96
 
 
 @pytest.mark.parametrize("B,Nkv,Tcap,ch", [
-    (16, 8, 8192, 224),
-    (16, 8, 16384, 384),
-    (24, 8, 16384, 640),
-    (32, 8, 16384, 896),
+    (16, 8, 3000, 160),
+    (16, 8, 4000, 224),
+    (16, 8, 8192, 384),
+    (16, 8, 12000, 640),
+    (16, 8, 16384, 896),
+    (24, 8, 16384, 1152),
 ])
 def test_decode_chunk_sizes(B, Nkv, Tcap, ch):
     # every chunk length the host can pick, with lengths on and around chunk

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None,
                        window=0, scale=None, stream=None)
     attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype)
+    attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype)
     attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None)
     attn_strerror(status)
 Conveniences that allocate outputs with torch:
@@ -37,7 +38,8 @@ ATTN_BF16 = 0
 ATTN_F32 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
-           "attn_decode_workspace_bytes", "attn_kv_append", "attn_strerror")
+           "attn_decode_workspace_bytes", "attn_decode_window_workspace_bytes",
+           "attn_kv_append", "attn_strerror")
 
 _lib = None
 
@@ -63,6 +65,8 @@ def lib():
         L.attn_prefill.restype = i32
         L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_decode_window_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.attn_decode_window_workspace_bytes.restype = ctypes.c_size_t
         L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                   ctypes.c_size_t, i32, vp]
         L.attn_decode.restype = i32
@@ -131,6 +135,10 @@ def attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None):
 
 def attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype):
     return int(lib().attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype))
+
+
+def attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype):
+    return int(lib().attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, int(window), dtype))
 
 
 def _check_decode(q, Kcache, Vcache, lens, O, LSE):
@@ -237,8 +245,8 @@ def decode(q, Kcache, Vcache, lens, window=0, scale=None):
     B, Nq, Dh = q.shape
     O = torch.empty_like(q)
     LSE = torch.empty((B, Nq), dtype=torch.float32, device=q.device)
-    nbytes = attn_decode_workspace_bytes(B, Nq, Kcache.shape[1], Dh, Kcache.shape[2],
-                                         _dtype_code(q))
+    nbytes = attn_decode_window_workspace_bytes(B, Nq, Kcache.shape[1], Dh, Kcache.shape[2],
+                                                window, _dtype_code(q))
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
     if window or scale is not None:
         attn_decode_window(q, Kcache, Vcache, lens, O, LSE, ws, window=window, scale=scale)

@@ -62,11 +62,16 @@ int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
                                             lens, 1, window, scale, dtype == ATTN_BF16, s));
 }
 
-size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int dtype) {
+size_t attn_decode_window_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int window,
+                                          int dtype) {
   if (validate_common(B, Nq, Nkv, Dh, dtype) != ATTN_OK || !positive(Tcap)) return 0;
   if (dtype == ATTN_BF16 && Dh == 128 && attn::decode_bf16_d128_supported(Nq, Nkv))
-    return attn::decode_bf16_d128_workspace(B, Nq, Nkv, Tcap);
+    return attn::decode_bf16_d128_workspace(B, Nq, Nkv, Tcap, window > 0 ? window : 0);
   return 0;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int dtype) {
+  return attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, 0, dtype);
 }
 
 static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
@@ -80,7 +85,7 @@ static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t need = attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype);
+  const size_t need = attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
     return from_hip(attn::launch_decode_bf16_d128(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv,

@@ -38,6 +38,8 @@
 //     heads.  Rows at or past the length are never used: copy addresses clamp
 //     to the last valid row and those keys get probability 0.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -64,9 +66,10 @@ struct DecParams {
   const int32_t* lens;
   __bf16* O;
   float* LSE;
-  float* ws_o;    // [B, Nkv, n_chunks, G, D] unnormalised partial outputs
-  float* ws_ml;   // [B, Nkv, n_chunks, G, 2]  (m in log2 units, l)
-  int B, Nq, Nkv, G, Tcap, n_chunks;
+  float* ws_o;    // [B, Nkv, n_slots, G, D] unnormalised partial outputs
+  float* ws_ml;   // [B, Nkv, n_slots, G, 2]  (m in log2 units, l)
+  int B, Nq, Nkv, G, Tcap;
+  int n_slots;    // chunks that can hold visible keys, per (sequence, K/V head)
   int ch;         // keys per chunk (a multiple of STEP)
   int window;     // > 0: only keys lens[b] - window .. lens[b] - 1 are visible
   float c;        // scale * log2(e)
@@ -115,13 +118,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   lds_char* const V0 = (lds_char*)v0s;
   lds_char* const V1 = (lds_char*)v1s;
 
-  const int chunk = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int n = min(p.lens[b], p.Tcap);
   const int lo = p.window > 0 ? max(0, n - p.window) : 0;  // first visible key
+  // workgroup x takes the x-th chunk from the one holding key lo
+  const int chunk = lo / p.ch + blockIdx.x;
   const int c0 = chunk * p.ch;
-  if (c0 >= n || c0 + p.ch <= lo) return;
+  if (c0 >= n) return;
   const int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
   const int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
   const int last = min(n, c0 + p.ch) - 1;
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (l16 < G) {
-    const size_t part = (((size_t)b * p.Nkv + g) * p.n_chunks + chunk) * G + l16;
+    const size_t part = (((size_t)b * p.Nkv + g) * p.n_slots + blockIdx.x) * G + l16;
     float* dst = p.ws_o + part * D + 4 * grp;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db];
@@ -290,22 +294,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int hh = h % G;
   const int n = min(p.lens[b], p.Tcap);
   const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
-  const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;  // first chunk with a partial
-  const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_chunks * G + hh;  // chunk c: part0 + c*G
+  // partial slot x holds chunk c_lo + x; chunks c_lo .. nc-1 wrote one
+  const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
+  const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_slots * G + hh;  // slot x: part0 + x*G
 
   float M = -INFINITY;
-  for (int c = c_lo + lane; c < nc; c += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)c * G) * 2]);
+  const int ns = max(0, nc - c_lo);  // slots written
+  for (int x = lane; x < ns; x += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)x * G) * 2]);
   M = wave_max(M);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int cb = c_lo; cb < nc; cb += 64) {
-    // lane j of this batch holds chunk cb + j's weight
+  for (int cb = 0; cb < ns; cb += 64) {
+    // lane j of this batch holds slot cb + j's weight
     float wgt = 0.f;
-    if (cb + lane < nc) {
+    if (cb + lane < ns) {
       const size_t part = part0 + (size_t)(cb + lane) * G;
       wgt = exp2_fast(p.ws_ml[part * 2] - M);
       L = __builtin_fmaf(wgt, p.ws_ml[part * 2 + 1], L);
     }
-    const int cnt = min(64, nc - cb);
+    const int cnt = min(64, ns - cb);
     int j = 0;
     for (; j + 4 <= cnt; j += 4) {
       f32x2 ov[4];
@@ -339,20 +345,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
 bool decode_bf16_d128_supported(int Nq, int Nkv) { return Nq / Nkv <= 16; }
 
 // Keys per chunk: the longest candidate that still gives the grid at least
-// 4096 (sequence, K/V head, chunk) items when every sequence is Tcap long.
-// The candidates are multiples of 32 keys, none a power of two.
-int decode_bf16_d128_chunk(int B, int Nkv, int Tcap) {
+// 2048 (sequence, K/V head, chunk) items when every sequence has L visible
+// keys (L = Tcap, or the window when it is shorter).  The candidates are
+// multiples of 32 keys, none a power of two.
+int decode_bf16_d128_chunk(int B, int Nkv, int L) {
   static const int kChunks[] = {1792, 1152, 896, 640, 384, 224, 160, 96};
   const long long heads = (long long)B * Nkv;
   for (int ch : kChunks)
-    if (heads * ((Tcap + ch - 1) / ch) >= 4096) return ch;
+    if (heads * ((L + ch - 1) / ch) >= 2048) return ch;
   return kChunks[sizeof(kChunks) / sizeof(kChunks[0]) - 1];
 }
 
-size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap) {
-  const int ch = decode_bf16_d128_chunk(B, Nkv, Tcap);
-  const size_t n_chunks = ((size_t)Tcap + ch - 1) / ch;
-  const size_t parts = (size_t)B * Nq * n_chunks;  // B * Nkv * n_chunks * G
+namespace {
+// visible keys at most, chunk length, and partial slots per (sequence, K/V head)
+struct DecodePlan {
+  int ch, n_slots;
+};
+DecodePlan decode_plan(int B, int Nkv, int Tcap, int window) {
+  const int L = (window > 0 && window < Tcap) ? window : Tcap;
+  DecodePlan d;
+  d.ch = decode_bf16_d128_chunk(B, Nkv, L);
+  const int all = (Tcap + d.ch - 1) / d.ch;
+  // a window of L keys starting anywhere touches at most ceil(L / ch) + 1 chunks
+  d.n_slots = L < Tcap ? std::min(all, (L + d.ch - 1) / d.ch + 1) : all;
+  return d;
+}
+}  // namespace
+
+size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap, int window) {
+  const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
+  const size_t parts = (size_t)B * Nq * d.n_slots;  // B * Nkv * n_slots * G
   return parts * D * sizeof(float) + parts * 2 * sizeof(float);
 }
 
@@ -360,6 +382,7 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
                                    const int32_t* lens, void* O, float* LSE, int B, int Nq,
                                    int Nkv, int Tcap, int window, float scale, void* ws,
                                    hipStream_t stream) {
+  const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
   DecParams p;
   p.q = static_cast<const __bf16*>(q);
   p.K = static_cast<const __bf16*>(Kc);
@@ -372,15 +395,15 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
   p.Nkv = Nkv;
   p.G = Nq / Nkv;
   p.Tcap = Tcap;
-  p.ch = decode_bf16_d128_chunk(B, Nkv, Tcap);
-  p.n_chunks = (Tcap + p.ch - 1) / p.ch;
-  const size_t parts = (size_t)B * Nq * p.n_chunks;
+  p.ch = d.ch;
+  p.n_slots = d.n_slots;
+  const size_t parts = (size_t)B * Nq * p.n_slots;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * D;
   p.window = window;
   p.c = kLog2e * scale;
   if (Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_chunks, Nkv, B), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_slots, Nkv, B), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = B * Nq;

@@ -28,8 +28,8 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
 // bf16, Dh == 128 split-K decode (partials + log-sum-exp merge).  The query
 // of sequence b sees keys max(0, lens[b] - window) .. lens[b] - 1 (window 0:
 // all of them).
-int decode_bf16_d128_chunk(int B, int Nkv, int Tcap);
-size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap);
+int decode_bf16_d128_chunk(int B, int Nkv, int L);
+size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap, int window);
 bool decode_bf16_d128_supported(int Nq, int Nkv);
 hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
                                    const int32_t* lens, void* O, float* LSE, int B, int Nq,
