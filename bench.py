@@ -116,6 +116,81 @@ def _read_ceiling(torch, dev, gib=4.5, reps=5):
                       "best_GBs": max(r["GB/s"] for r in rows)}), flush=True)
 
 
+def _time(torch, fn, steps, warmup):
+    """Mean ms per call, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def _cache_paths(torch, dev, tch, steps, warmup):
+    """One JSON line per cache-side entry point, on the shapes of the main workloads."""
+    # chunked prefill: the last 2048 tokens of a 32768-token context, GQA 32/8
+    B, Nq, Nkv, Sq, T, Dh = 1, 32, 8, 2048, 32768, 128
+    lens, Q, kc, vc = workloads.chunk_inputs(B, Nq, Nkv, Sq, Dh, T, [T], "bf16", seed=0)
+    tQ, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (Q, kc, vc))
+    tl = torch.from_numpy(lens).to(dev)
+    O = torch.empty_like(tQ)
+    L = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
+    ms = _time(torch, lambda: tch.attn_prefill_cache(tQ, tk, tv, tl, O, L), steps, warmup)
+    flop = 4 * Dh * Nq * B * sum(T - Sq + i + 1 for i in range(Sq))
+    tf = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({"path": "attn_prefill_cache", "workload": f"B={B} Nq={Nq} Nkv={Nkv} "
+                      f"Sq={Sq} lens={T} Dh={Dh} bf16 causal", "ms": round(ms, 4),
+                      "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "algorithmic_flop": flop}), flush=True)
+    del tQ, tk, tv, O, L
+
+    # decode workload with a 4096-key window: linear cache, then a rolling buffer
+    dc = workloads.WORKLOADS[DECODE]
+    B, Nq, Nkv, Dh, T, W = dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"], dc["Tcap"], 4096
+    lens, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, T, dc["len_lo"], dc["len_hi"])
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+    tl = torch.from_numpy(lens).to(dev)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, T, W,
+                                                                   tch.ATTN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    vis = np.minimum(lens, W).astype(np.int64)
+    nbytes = int(2 * vis.sum() * Nkv * Dh * 2 + 2 * B * Nq * Dh * 2 + 4 * B)
+    ms = _time(torch, lambda: tch.attn_decode_window(tq, tk, tv, tl, O, L, ws, window=W),
+               steps, warmup)
+    print(json.dumps({"path": "attn_decode_window", "workload": f"{DECODE} window={W}",
+                      "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": nbytes}), flush=True)
+    # rolling buffer of W slots holding each sequence's last min(len, W) keys
+    rk = tk[:, :, :W].contiguous()
+    rv = tv[:, :, :W].contiguous()
+    rl = torch.from_numpy(vis.astype(np.int32)).to(dev)
+    wsr = torch.empty(max(1, tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, W, tch.ATTN_BF16)),
+                      dtype=torch.uint8, device=dev)
+    ms = _time(torch, lambda: tch.attn_decode(tq, rk, rv, rl, O, L, wsr), steps, warmup)
+    print(json.dumps({"path": "attn_decode (rolling buffer)", "workload":
+                      f"B={B} Nq={Nq} Nkv={Nkv} Dh={Dh} buffer={W} slots, lens=min(len, {W})",
+                      "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": nbytes}), flush=True)
+    # append of one token per sequence into the rolling buffer
+    kn = torch.randn(B, Nkv, 1, Dh, device=dev, dtype=torch.bfloat16)
+    vn = torch.randn_like(kn)
+    ms = _time(torch, lambda: tch.attn_kv_append(kn, vn, rk, rv, tl, rolling=1), steps, warmup)
+    abytes = 2 * 2 * B * Nkv * Dh * 2
+    print(json.dumps({"path": "attn_kv_append", "workload": f"B={B} Nkv={Nkv} Snew=1 Dh={Dh} "
+                      f"rolling buffer of {W}", "ms": round(ms, 4),
+                      "GB/s": round(abytes / ms / 1e6, 1), "algorithmic_bytes": abytes}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +201,9 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run only the streaming-read probe over 4.5 GB (HBM reference point)")
+    ap.add_argument("--cache-paths", action="store_true",
+                    help="time the cache-side entry points (chunked prefill, windowed and "
+                         "rolling-buffer decode, append) instead of the main step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -146,6 +224,9 @@ def main():
         return
     if args.read_ceiling:
         _read_ceiling(torch, dev)
+        return
+    if args.cache_paths:
+        _cache_paths(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
 
     pc = workloads.WORKLOADS[PREFILL]
