@@ -65,8 +65,8 @@ typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
  *   scale    multiplier of Q K^T; > 0 and finite.  The standard definition
  *            uses 1/sqrt(Dh) (the head size).
  *   dtype    attn_dtype of Q, K, V and O.
- * Supported: Dh in 1..256 for both dtypes; bf16 with Dh == 128 takes the
- * MFMA kernel, the rest a general kernel.  B, Nq, Nkv, S >= 1.
+ * Supported: Dh in 1..256 for both dtypes; bf16 with Dh in {64, 128, 256}
+ * takes the MFMA kernel, the rest a general kernel.  B, Nq, Nkv, S >= 1.
  * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -95,7 +95,7 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
  * or past lens[b] are never read.  With Sq == lens[b] this is attn_prefill.
  * lens lives on the device: values above Tcap are clamped to Tcap, and a
  * value below Sq leaves rows with no visible key (NaN).
- * Supported: as attn_prefill (bf16 Dh == 128 takes the MFMA kernel).
+ * Supported: as attn_prefill (bf16 Dh in {64, 128, 256} takes the MFMA kernel).
  * Errors: ATTN_EINVAL (also Sq > Tcap), ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,

@@ -53,8 +53,9 @@ def test_prefill_cache_bf16(B, Nq, Nkv, Sq, Tcap, lens, window):
         f"{check(O, L, Or, Lr, 'bf16', (Sq, lens, window), storage_allowance=True)}")
 
 
-@pytest.mark.parametrize("Dh,dtype,window", [(64, "f32", 0), (80, "bf16", 9), (128, "f32", 20)])
-def test_prefill_cache_general(Dh, dtype, window):
+@pytest.mark.parametrize("Dh,dtype,window", [(64, "f32", 0), (80, "bf16", 9), (128, "f32", 20),
+                                              (64, "bf16", 0), (256, "bf16", 30)])
+def test_prefill_cache_other_head_sizes(Dh, dtype, window):
     lens_a, Q, kc, vc = workloads.chunk_inputs(2, 4, 2, 33, Dh, 200, [33, 180], dtype, seed=Dh)
     O, L = _run_chunk(Q, kc, vc, lens_a, dtype, window, scale=0.3)
     Or, Lr = oracle.chunk_ref(workloads.to_f64(Q, dtype), workloads.to_f64(kc, dtype),

@@ -120,6 +120,26 @@ def test_prefill_edge_cases_bf16(B, Nq, Nkv, S, causal, window):
     check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, S, causal, window), storage_allowance=True)
 
 
+@pytest.mark.parametrize("Dh", [64, 256])
+@pytest.mark.parametrize("B,Nq,Nkv,S,causal,window", [
+    (1, 2, 2, 1, True, 0),
+    (2, 4, 4, 65, True, 0),       # one key past a tile
+    (1, 8, 2, 300, True, 0),      # GQA 4, ragged
+    (1, 6, 3, 257, True, 0),      # GQA 2, past a query tile
+    (1, 4, 1, 200, True, 0),      # MQA
+    (2, 8, 2, 600, True, 100),    # window not aligned to tiles
+    (1, 4, 4, 700, True, 1),      # window 1
+    (1, 4, 2, 130, False, 0),     # non-causal
+])
+def test_prefill_mfma_head_sizes(Dh, B, Nq, Nkv, S, causal, window):
+    # the MFMA kernel at head sizes 64 and 256 (same cases as at 128)
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=S + Dh)
+    O, L = run_prefill(q, k, v, "bf16", causal, window, None)
+    Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
+                                  causal=causal, window=window)
+    check(O, L, Or, Lr, "bf16", (Dh, B, Nq, Nkv, S, causal, window), storage_allowance=True)
+
+
 @pytest.mark.parametrize("Dh,S,Nq,Nkv,window,dtype", [
     (4, 5, 2, 2, 0, "f32"),
     (64, 100, 4, 2, 0, "f32"),

@@ -37,9 +37,9 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == ATTN_BF16 && Dh == 128)
-    return from_hip(attn::launch_prefill_bf16_d128(Q, K, V, O, LSE, B, Nq, Nkv, S, S, nullptr,
-                                                   causal, window, scale, s));
+  if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
+    return from_hip(attn::launch_prefill_bf16(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
+                                              causal, window, scale, s));
   return from_hip(attn::launch_rows_general(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
                                             causal, window, scale, dtype == ATTN_BF16, s));
 }
@@ -55,9 +55,9 @@ int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == ATTN_BF16 && Dh == 128)
-    return from_hip(attn::launch_prefill_bf16_d128(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq,
-                                                   Tcap, lens, 1, window, scale, s));
+  if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
+    return from_hip(attn::launch_prefill_bf16(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh,
+                                              Tcap, lens, 1, window, scale, s));
   return from_hip(attn::launch_rows_general(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
                                             lens, 1, window, scale, dtype == ATTN_BF16, s));
 }

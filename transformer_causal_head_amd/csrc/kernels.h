@@ -7,14 +7,15 @@
 
 namespace attn {
 
-// bf16, Dh == 128 MFMA prefill.  S query rows per head; K/V heads of
-// kv_rows rows.  lens == nullptr: plain prefill (S keys, query i at position
-// i).  Otherwise sequence b has lens[b] keys and query i sits at position
-// lens[b] - S + i (chunked prefill against a cache).
-hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
-                                    float* LSE, int B, int Nq, int Nkv, int S, int kv_rows,
-                                    const int32_t* lens, int causal, int window, float scale,
-                                    hipStream_t stream);
+// bf16 MFMA prefill, head size 64, 128 or 256.  S query rows per head; K/V
+// heads of kv_rows rows.  lens == nullptr: plain prefill (S keys, query i at
+// position i).  Otherwise sequence b has lens[b] keys and query i sits at
+// position lens[b] - S + i (chunked prefill against a cache).
+bool prefill_bf16_supported(int Dh);
+hipError_t launch_prefill_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int Nq, int Nkv, int S, int Dh, int kv_rows,
+                               const int32_t* lens, int causal, int window, float scale,
+                               hipStream_t stream);
 
 // General row kernel: one wavefront per output row (b, h, i), any Dh in
 // 1..256, bf16 (is_bf16 = 1) or fp32.  Same row/key convention as the MFMA

@@ -79,13 +79,28 @@ namespace attn {
 
 namespace {
 
-constexpr int D = 128;         // head size
-constexpr int NW = PREFILL_NW; // waves per workgroup
 constexpr int QB = PREFILL_QB; // 32-query blocks per wave
 constexpr bool PIPE = PREFILL_PIPE != 0;
 constexpr int BN = 64;         // keys per K/V tile
-constexpr int TILE = BN * D * 2;
 constexpr float TAU = 8.f;
+
+// Tile geometry for head size D (64, 128 or 256).  A K/V row is RB = 2*D
+// bytes = NC 16-byte chunks; a tile of BN rows is NP pieces of 1 KB, RP rows
+// each.  QK^T takes KS 16-wide slices of the head; PV yields DB 32-wide
+// output blocks.
+template <int D>
+struct Geo {
+  static constexpr int RB = 2 * D;
+  static constexpr int NC = D / 8;
+  static constexpr int TILE = BN * RB;
+  static constexpr int NP = TILE / 1024;
+  static constexpr int RP = 1024 / RB;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+};
+// waves per workgroup: two per SIMD while the registers allow it
+template <int D>
+constexpr int waves_for() { return D == 128 ? PREFILL_NW : (D < 128 ? 8 : 4); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -108,9 +123,18 @@ struct Params {
   int n_hsub;     // G / hp
 };
 
-// 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
+// 16-byte chunk c of tile row r is stored at chunk position c ^ swz<D>(r).
+// Both are GF(2)-linear in the row bits, chosen (by exhaustive check of
+// every read instruction's lanes) so that the 16-byte K operand reads and
+// the transposing V reads hit distinct banks: row bits 0..3 map to chunk
+// bits 4, 10, 1, 8 for 256- and 512-byte rows, and to 2, 4, 1, 2 for 128-byte
+// rows.
+template <int D>
 __device__ __forceinline__ int swz(int r) {
-  return ((r & 1) << 2) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (r & 8);
+  if constexpr (D == 64)
+    return ((r & 1) << 1) ^ (((r >> 1) & 1) << 2) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+  else
+    return ((r & 1) << 2) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (r & 8);
 }
 
 __device__ __forceinline__ void wait_dma() {
@@ -118,25 +142,27 @@ __device__ __forceinline__ void wait_dma() {
 }
 
 // Copy keys [k0, k0+64) of one head (a buffer resource over the head) into a
-// swizzled LDS tile.  The tile is 16 pieces of 1 KB (4 rows); wave w issues
+// swizzled LDS tile.  The tile is NP pieces of 1 KB (RP rows); wave w issues
 // pieces w, w + NW, ...  The whole offset is in the per-lane operand, which the
 // buffer range check covers: rows past the end of the head read as zero.
 struct HeadRef {
   __amdgpu_buffer_rsrc_t rs;
 };
-__device__ __forceinline__ HeadRef head_ref(const __bf16* head, int S) {
-  return HeadRef{__builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, S * D * 2, 0x00020000)};
+template <int D>
+__device__ __forceinline__ HeadRef head_ref(const __bf16* head, int rows) {
+  return HeadRef{__builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, rows * D * 2, 0x00020000)};
 }
-__device__ __forceinline__ void load_tile(HeadRef h, int k0, int S, char* tile, int w, int lane) {
-  (void)S;
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(HeadRef h, int k0, char* tile, int w, int lane) {
+  using g = Geo<D>;
 #pragma unroll
-  for (int j = 0; j < (16 + NW - 1) / NW; ++j) {
+  for (int j = 0; j < (g::NP + NW - 1) / NW; ++j) {
     const int piece = w + j * NW;  // wave-uniform
-    if (piece >= 16) break;
-    const int r = piece * 4 + (lane >> 4);
-    const int voff = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+    if (piece >= g::NP) break;
+    const int r = piece * g::RP + lane / g::NC;
+    const int voff = r * g::RB + (((lane % g::NC) ^ swz<D>(r)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
-                                             voff + k0 * (D * 2), 0, 0, 0);
+                                             voff + k0 * g::RB, 0, 0, 0);
   }
 }
 
@@ -149,19 +175,21 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int QB_>
-__device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
-                                        const bf16x8 (&qf)[QB_][8], f32x16 (&s)[QB_][2]) {
+template <int D, int QB_>
+__device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>::KS],
+                                        const bf16x8 (&qf)[QB_][Geo<D>::KS],
+                                        f32x16 (&s)[QB_][2]) {
+  constexpr int KS = Geo<D>::KS;
   if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int qb = 0; qb < QB_; ++qb)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + kb * 8192 + koff[ks]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * Geo<D>::RB + koff[ks]);
 #pragma unroll
       for (int qb = 0; qb < QB_; ++qb)
         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
@@ -169,7 +197,7 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
   if (PREFILL_RA && QB_ == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
 #pragma unroll
-    for (int k = 0; k < 10; ++k) {
+    for (int k = 0; k < 2 * KS - 6; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
@@ -178,18 +206,20 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[8],
   if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(0);
 }
 
-template <int QB_>
-__device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
-                                        const bf16x8 (&pf)[QB_][4], f32x16 (&o)[QB_][4]) {
+template <int D, int QB_>
+__device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo<D>::DB],
+                                        const bf16x8 (&pf)[QB_][4],
+                                        f32x16 (&o)[QB_][Geo<D>::DB]) {
+  constexpr int DB = Geo<D>::DB;
   if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 4096 + voff[0][db]));
+          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 16 * Geo<D>::RB + voff[0][db]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 4096 + voff[1][db]));
+          (__attribute__((address_space(3))) i16x4*)(Vt + kk * 16 * Geo<D>::RB + voff[1][db]));
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int qb = 0; qb < QB_; ++qb)
@@ -198,7 +228,7 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
   if (PREFILL_RA && QB_ == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 transposing reads
 #pragma unroll
-    for (int k = 0; k < 12; ++k) {
+    for (int k = 0; k < 4 * DB - 4; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 reads
     }
@@ -207,7 +237,12 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][4],
   if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(0);
 }
 
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
+  using geo = Geo<D>;
+  constexpr int TILE = geo::TILE;
+  constexpr int KS = geo::KS;
+  constexpr int DB = geo::DB;
   constexpr int QW = 32 * QB;  // queries per wave
   // four separate LDS objects, so the compiler can tell that the DMA copies
   // into one stage never alias reads of another
@@ -247,8 +282,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const bool wave_live = qa_row < p.S;
 
   const size_t kv_base = ((size_t)b * p.Nkv + g) * (size_t)p.kv_rows * D;
-  const HeadRef Kh = head_ref(p.K + kv_base, n_keys);
-  const HeadRef Vh = head_ref(p.V + kv_base, n_keys);
+  const HeadRef Kh = head_ref<D>(p.K + kv_base, n_keys);
+  const HeadRef Vh = head_ref<D>(p.V + kv_base, n_keys);
   const size_t q_base = ((size_t)b * p.Nq + head) * (size_t)p.S * D;
 
   // key range of the workgroup
@@ -263,25 +298,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   char* const V1 = v1s;
 
   // start the copies first, they overlap the set-up below
-  load_tile(Kh, t_lo * BN, n_keys, K0, w, lane);
-  load_tile(Vh, t_lo * BN, n_keys, V0, w, lane);
-  if (PIPE && nt > 1) load_tile(Kh, (t_lo + 1) * BN, n_keys, K1, w, lane);
+  load_tile<D, NW>(Kh, t_lo * BN, K0, w, lane);
+  load_tile<D, NW>(Vh, t_lo * BN, V0, w, lane);
+  if (PIPE && nt > 1) load_tile<D, NW>(Kh, (t_lo + 1) * BN, K1, w, lane);
 
   // Q^T operand fragments: query column ln of block qb, d = 16*ks + 8*hl + i
-  bf16x8 qf[QB][8];
+  bf16x8 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = min(qa_row + qb * 32 + ln, p.S - 1);
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.Q + q_base + (size_t)qrow * D + hl * 8);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[qb][ks] = src[ks * 2];
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = src[ks * 2];
   }
 
   // LDS byte offsets inside a tile
-  int koff[8];  // K operand: row ln (+32*kb), chunk 2*ks + hl
+  int koff[KS];  // K operand: row ln (+32*kb), chunk 2*ks + hl
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koff[ks] = ln * 256 + (((2 * ks + hl) ^ swz(ln)) << 4);
-  int voff[2][4];  // V^T operand through the transposing read
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = ln * geo::RB + (((2 * ks + hl) ^ swz<D>(ln)) << 4);
+  int voff[2][DB];  // V^T operand through the transposing read
   {
     const int gq = lane >> 4, j = lane & 15;
     const int h = gq >> 1, dpart = gq & 1, ip = j >> 2, u = j & 3;
@@ -289,19 +324,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     for (int ih = 0; ih < 2; ++ih) {
       const int r = 8 * ih + 4 * h + ip;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        voff[ih][db] = r * 256 + (((4 * db + 2 * dpart + (u >> 1)) ^ swz(r)) << 4) + (u & 1) * 8;
+      for (int db = 0; db < DB; ++db)
+        voff[ih][db] = r * geo::RB + (((4 * db + 2 * dpart + (u >> 1)) ^ swz<D>(r)) << 4) + (u & 1) * 8;
     }
   }
 
-  f32x16 oacc[QB][4];
+  f32x16 oacc[QB][DB];
   float m_run[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
   }
 
   // Tile ranges of this wave, as wave-uniform integers: tiles [tl_lo, tl_hi]
@@ -365,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
         m_run[qb] = m_new;
         l_run[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[qb][db] *= alpha;
+        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
       }
     }
   };
@@ -393,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
         }
       l_run[qb] += rs;
     }
-    pv_tile<QB>(Vt, voff, pf, oacc);
+    pv_tile<D, QB>(Vt, voff, pf, oacc);
   };
 
   // mask (boundary tiles only), running max / rescale, then P and PV
@@ -407,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     f32x16 sa[QB][2], sb[QB][2];
     wait_dma();
     __syncthreads();
-    if (live(t_lo)) qk_tile<QB>(K0, koff, qf, sa);
+    if (live(t_lo)) qk_tile<D, QB>(K0, koff, qf, sa);
 
     // iteration i (tile t = t_lo + i): S(t) is in registers, K(t+1) and V(t)
     // are in LDS; the copies of K(t+2) and V(t+1) are issued at the top.
@@ -419,9 +454,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
       char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
       wait_dma();
       __syncthreads();
-      if (i + 2 < nt) load_tile(Kh, (t + 2) * BN, n_keys, Kcur, w, lane);
-      if (i + 1 < nt) load_tile(Vh, (t + 1) * BN, n_keys, Vnext, w, lane);
-      if (i + 1 < nt && live(t + 1)) qk_tile<QB>(Knext, koff, qf, s_next);
+      if (i + 2 < nt) load_tile<D, NW>(Kh, (t + 2) * BN, Kcur, w, lane);
+      if (i + 1 < nt) load_tile<D, NW>(Vh, (t + 1) * BN, Vnext, w, lane);
+      if (i + 1 < nt && live(t + 1)) qk_tile<D, QB>(Knext, koff, qf, s_next);
       if (live(t)) softmax_pv(t, s_cur, Vcur);
     };
 
@@ -440,11 +475,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
       wait_dma();
       __syncthreads();
       if (i + 1 < nt) {
-        load_tile(Kh, (t + 1) * BN, n_keys, (i & 1) ? K0 : K1, w, lane);
-        load_tile(Vh, (t + 1) * BN, n_keys, (i & 1) ? V0 : V1, w, lane);
+        load_tile<D, NW>(Kh, (t + 1) * BN, (i & 1) ? K0 : K1, w, lane);
+        load_tile<D, NW>(Vh, (t + 1) * BN, (i & 1) ? V0 : V1, w, lane);
       }
       if (live(t)) {
-        qk_tile<QB>((i & 1) ? K1 : K0, koff, qf, s);
+        qk_tile<D, QB>((i & 1) ? K1 : K0, koff, qf, s);
         softmax_pv(t, s, (i & 1) ? V1 : V0);
       }
     }
@@ -460,7 +495,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     const float inv = 1.f / l_tot;
     __bf16* orow = p.O + q_base + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = db * 32 + a4 * 8 + hl * 4;
@@ -474,12 +509,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V, void* O,
-                                    float* LSE, int B, int Nq, int Nkv, int S, int kv_rows,
-                                    const int32_t* lens, int causal, int window, float scale,
-                                    hipStream_t stream) {
+template <int D>
+hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          int B, int Nq, int Nkv, int S, int kv_rows, const int32_t* lens,
+                          int causal, int window, float scale, hipStream_t stream) {
+  constexpr int NW = waves_for<D>();
   // one head of K (or V) is addressed through a 31-bit buffer range
   if ((long long)kv_rows * D * 2 > 0x7fffffffLL || (long long)S * D * 2 > 0x7fffffffLL)
     return hipErrorInvalidValue;
@@ -499,14 +533,37 @@ hipError_t launch_prefill_bf16_d128(const void* Q, const void* K, const void* V,
   p.window = window;
   p.c = scale * kLog2e;
   p.G = Nq / Nkv;
-  p.hp = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+  p.hp = (p.G % 4 == 0 && NW % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
   p.n_hsub = p.G / p.hp;
   p.qspan = (NW / p.hp) * 32 * QB;
   p.n_qtiles = (S + p.qspan - 1) / p.qspan;
   const long long nblocks = (long long)p.n_qtiles * B * Nkv * p.n_hsub;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_bf16_supported(int Dh) { return Dh == 64 || Dh == 128 || Dh == 256; }
+
+hipError_t launch_prefill_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int Nq, int Nkv, int S, int Dh, int kv_rows,
+                               const int32_t* lens, int causal, int window, float scale,
+                               hipStream_t stream) {
+  switch (Dh) {
+    case 64:
+      return launch_prefill<64>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
+                                scale, stream);
+    case 128:
+      return launch_prefill<128>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
+                                 scale, stream);
+    case 256:
+      return launch_prefill<256>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
+                                 scale, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn
