@@ -126,7 +126,9 @@ size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int
  *                                attn_decode_workspace_bytes(...) bytes
  *                                (may be NULL when that is 0)
  * The scale is 1/sqrt(Dh).  No mask applies beyond the length; cache rows at
- * or past lens[b] are never read.
+ * or past lens[b] are never read.  bf16 with Dh in {64, 128, 256} and at most
+ * 32 query heads per K/V head takes the split-K MFMA kernels (and needs the
+ * workspace); other shapes take a general kernel.
  * lens lives on the device, so the host cannot check it: a value above Tcap
  * is clamped to Tcap, and a value below 1 yields a NaN output row.
  * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP.

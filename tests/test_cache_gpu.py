@@ -109,8 +109,9 @@ def test_decode_window_bf16(B, Nq, Nkv, Tcap, lens, window):
     say(f"decode window {window}: {check(O, L, Or, Lr, 'bf16', window, storage_allowance=True)}")
 
 
-@pytest.mark.parametrize("Dh,dtype,Nq,Nkv", [(64, "f32", 4, 2), (128, "bf16", 6, 2)])
-def test_decode_window_general(Dh, dtype, Nq, Nkv):
+@pytest.mark.parametrize("Dh,dtype,Nq,Nkv", [(64, "f32", 4, 2), (128, "bf16", 6, 2),
+                                             (64, "bf16", 4, 2), (256, "bf16", 32, 1)])
+def test_decode_window_other_shapes(Dh, dtype, Nq, Nkv):
     lens_a, q, kc, vc = workloads.decode_inputs(3, Nq, Nkv, Dh, 400, 1, 400, dtype, seed=Dh,
                                                 lens=[400, 17, 250])
     O, L = _run_decode(q, kc, vc, lens_a, dtype, 40, scale=0.2)

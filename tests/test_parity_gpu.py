@@ -290,6 +290,24 @@ def test_decode_chunk_sizes(B, Nkv, Tcap, ch):
     say(f"chunk {ch}: errors {check(Os, Ls, Or, Lr, 'bf16', (B, Nkv, Tcap, ch), storage_allowance=True)}")
 
 
+@pytest.mark.parametrize("Dh,B,Nq,Nkv,Tcap,lens", [
+    (64, 4, 16, 4, 3000, [1, 33, 2999, 3000]),
+    (256, 4, 16, 4, 3000, [1, 33, 2999, 3000]),
+    (128, 3, 32, 1, 2500, [2500, 97, 1]),        # MQA with 32 query heads: two head blocks
+    (128, 2, 24, 1, 700, [700, 300]),            # 24 heads: second block partly empty
+    (64, 2, 32, 1, 900, [900, 450]),
+    (256, 2, 64, 2, 900, [1, 900]),              # G = 32 at head size 256
+])
+def test_decode_mfma_head_sizes_and_groups(Dh, B, Nq, Nkv, Tcap, lens):
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, seed=Dh + Nq,
+                                                lens=lens)
+    O, L = run_decode(q, kc, vc, lens_a, "bf16")
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), workloads.to_f64(kc, "bf16"),
+                               workloads.to_f64(vc, "bf16"), lens_a)
+    check(O, L, Or, Lr, "bf16", (Dh, B, Nq, Nkv, Tcap, lens), storage_allowance=True)
+    assert tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, tch.ATTN_BF16) > 0
+
+
 @pytest.mark.parametrize("Dh", [4, 64, 128])
 def test_decode_fp32(Dh):
     lens_a, q, kc, vc = workloads.decode_inputs(3, 4, 2, Dh, 50, 1, 50, dtype="f32", seed=Dh,

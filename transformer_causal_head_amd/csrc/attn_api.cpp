@@ -65,8 +65,8 @@ int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
 size_t attn_decode_window_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int window,
                                           int dtype) {
   if (validate_common(B, Nq, Nkv, Dh, dtype) != ATTN_OK || !positive(Tcap)) return 0;
-  if (dtype == ATTN_BF16 && Dh == 128 && attn::decode_bf16_d128_supported(Nq, Nkv))
-    return attn::decode_bf16_d128_workspace(B, Nq, Nkv, Tcap, window > 0 ? window : 0);
+  if (dtype == ATTN_BF16 && attn::decode_bf16_supported(Nq, Nkv, Dh))
+    return attn::decode_bf16_workspace(B, Nq, Nkv, Dh, Tcap, window > 0 ? window : 0);
   return 0;
 }
 
@@ -88,8 +88,8 @@ static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
   const size_t need = attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
-    return from_hip(attn::launch_decode_bf16_d128(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv,
-                                                  Tcap, window, scale, workspace, s));
+    return from_hip(attn::launch_decode_bf16(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv, Dh,
+                                             Tcap, window, scale, workspace, s));
   }
   return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap,
                                             lens, 1, window, scale, dtype == ATTN_BF16, s));

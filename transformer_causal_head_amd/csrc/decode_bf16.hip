@@ -1,4 +1,5 @@
-// KV-cache decode step, bf16 cache, head size 128, split over the key axis.
+// KV-cache decode step, bf16 cache, head size 64, 128 or 256, split over the
+// key axis.
 //
 // The step is one query row per sequence against its cached keys (textbook
 // attention chapter, "KV-кэш" and "Prefill и decode": a 1 x t score row;
@@ -30,10 +31,12 @@
 //     wave.  The step loop is unrolled by two so every stage is a distinct LDS
 //     object and every wait count is a compile-time constant.
 //   * Both products run on v_mfma_f32_16x16x32_bf16 in the transposed form of
-//     the prefill kernel: S^T = K q^T (keys on M, the G query heads on N), and
-//     O^T = V^T P^T, whose B operand is the S^T accumulator layout.  K is read
-//     from LDS in operand layout (a row-XOR swizzle keeps the 16-row reads
-//     conflict free); V is transposed on its way out by ds_read_b64_tr_b16.
+//     the prefill kernel: S^T = K q^T (keys on M, up to 16 query heads on N),
+//     and O^T = V^T P^T, whose B operand is the S^T accumulator layout.  K is
+//     read from LDS in operand layout and V is transposed on its way out by
+//     ds_read_b64_tr_b16; row-XOR swizzles keep both conflict free.  More than
+//     16 query heads per K/V head (up to 32: MQA) take a second N block that
+//     reuses every K and V fragment.
 //   * Every K and V byte is read once per K/V head and shared by its G query
 //     heads.  Rows at or past the length are never used: copy addresses clamp
 //     to the last valid row and those keys get probability 0.
@@ -47,17 +50,28 @@ namespace attn {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int STEP = 32;             // keys per pipeline step
-constexpr int STAGE = STEP * D * 2;  // bytes of K (or V) per step
 constexpr float TAU = 8.f;
 constexpr int kNonTemporal = 2;      // cache-policy bit of the copy instructions
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// Geometry for head size D: a row is RB = 2*D bytes (NC 16-byte chunks); a
+// step's rows fill STAGE bytes = NPIECE copies of 1 KB (RP rows each); QK^T
+// takes KS 32-wide slices of the head, PV yields DB 16-wide output blocks.
+template <int D>
+struct DGeo {
+  static constexpr int RB = 2 * D;
+  static constexpr int NC = D / 8;
+  static constexpr int STAGE = STEP * RB;
+  static constexpr int NPIECE = STAGE / 1024;
+  static constexpr int RP = 1024 / RB;
+  static constexpr int KS = D / 32;
+  static constexpr int DB = D / 16;
+};
 
 struct DecParams {
   const __bf16* q;
@@ -75,22 +89,32 @@ struct DecParams {
   float c;        // scale * log2(e)
 };
 
-// 16-byte chunk c of V row r sits at chunk position c ^ vswz(r) (keeps the
-// transposing reads conflict free); chunk c of K row r at c ^ (r & 15) (the
-// operand reads take one chunk of 16 consecutive rows).
-__device__ __forceinline__ int vswz(int r) { return ((r << 1) & 14) | ((r >> 3) & 1); }
-__device__ __forceinline__ int kswz(int r) { return r & 15; }
+// 16-byte chunk c of K row r sits at chunk position c ^ kswz(r) (the operand
+// reads take one chunk of 16 consecutive rows), of V row r at c ^ vswz(r)
+// (keeps the transposing reads conflict free).  GF(2)-linear in the row bits,
+// checked exhaustively against both read patterns under 32 and 64 banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return r & 15;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 64) return ((r & 1) << 1) ^ (((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) << 1);
+  else return ((r << 1) & 14) | ((r >> 3) & 1);
+}
 
-// Rows [k0, k0+32) of one head -> one LDS stage: 8 copies of 4 whole rows,
-// lane i of a copy lands at byte 16*i of its 1 KB piece.  Rows past `last`
-// are clamped to it.
-template <bool IS_K>
+// Rows [k0, k0+32) of one head -> one LDS stage: NPIECE copies of RP whole
+// rows, lane i of a copy landing at byte 16*i of its 1 KB piece.  Rows past
+// `last` are clamped to it.
+template <int D, bool IS_K>
 __device__ __forceinline__ void load_rows(const __bf16* head, int k0, int last, lds_char* stage,
                                           int lane) {
+  using g = DGeo<D>;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = j * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (IS_K ? kswz(r) : vswz(r));
+  for (int j = 0; j < g::NPIECE; ++j) {
+    const int r = j * g::RP + lane / g::NC;
+    const int c = (lane % g::NC) ^ (IS_K ? kswz<D>(r) : vswz<D>(r));
     const int row = min(k0 + r, last);
     __builtin_amdgcn_global_load_lds(head + (size_t)row * D + c * 8,
                                      (lds_void*)(stage + j * 1024), 16, 0, kNonTemporal);
@@ -105,7 +129,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
+// NB blocks of 16 query heads per K/V head (G <= 16 * NB).
+template <int D, int NB>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
+  using geo = DGeo<D>;
+  constexpr int STAGE = geo::STAGE;
+  constexpr int KS = geo::KS;
+  constexpr int DB = geo::DB;
+  constexpr int PER_STEP = 2 * geo::NPIECE;  // copy instructions per step (K and V)
   // four separate LDS objects, so the compiler can tell that a copy into one
   // stage never aliases the reads of another
   __shared__ __attribute__((aligned(1024))) char k0s[STAGE];
@@ -139,64 +170,78 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   const __bf16* Kh = p.K + kvh;
   const __bf16* Vh = p.V + kvh;
 
-  // q^T operand: lane (grp, l16) holds q[head g*G + l16][32*ks + 8*grp + i]
-  bf16x8 qf[4];
+  // q^T operand: lane (grp, l16) of block nb holds
+  // q[head g*G + 16*nb + l16][32*ks + 8*grp + i]
+  bf16x8 qf[NB][KS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (l16 < G) {
-      const __bf16* src = p.q + ((size_t)b * p.Nq + (size_t)g * G + l16) * D + ks * 32 + grp * 8;
-      qf[ks] = *reinterpret_cast<const bf16x8*>(src);
-    } else {
-      qf[ks] = bf16x8{};
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int hh = 16 * nb + l16;
+      if (hh < G) {
+        const __bf16* src = p.q + ((size_t)b * p.Nq + (size_t)g * G + hh) * D + ks * 32 + grp * 8;
+        qf[nb][ks] = *reinterpret_cast<const bf16x8*>(src);
+      } else {
+        qf[nb][ks] = bf16x8{};
+      }
     }
-  }
 
   // copies in flight, oldest first: q, then K(0), V(0), K(1), V(1).  A step's
-  // copies are 16 vector-memory instructions, so vmcnt(16) before step s means
-  // step s has landed while step s + 1 is still in flight.  Copies are issued
-  // for two steps past the chunk's end too (all rows clamp to its last row
-  // and mostly hit L2), so that count holds on every path and the compiler
-  // adds no full drain of its own.
-  load_rows<true>(Kh, c0 + s0 * STEP, last, K0, lane);
-  load_rows<false>(Vh, c0 + s0 * STEP, last, V0, lane);
-  load_rows<true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
-  load_rows<false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
+  // copies are PER_STEP vector-memory instructions, so vmcnt(PER_STEP) before
+  // step s means step s has landed while step s + 1 is still in flight.
+  // Copies are issued for two steps past the chunk's end too (all rows clamp
+  // to its last row and mostly hit L2), so that count holds on every path and
+  // the compiler adds no full drain of its own.
+  load_rows<D, true>(Kh, c0 + s0 * STEP, last, K0, lane);
+  load_rows<D, false>(Vh, c0 + s0 * STEP, last, V0, lane);
+  load_rows<D, true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
+  load_rows<D, false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
 
   // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
   // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
-  int voff[2][8];
+  int voff[2][DB];
   {
     const int ip = l16 >> 2, u = l16 & 3;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int r = 16 * hf + 4 * grp + ip;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        voff[hf][db] = r * 256 + (((2 * db + (u >> 1)) ^ vswz(r)) << 4) + (u & 1) * 8;
+      for (int db = 0; db < DB; ++db)
+        voff[hf][db] = r * geo::RB + (((2 * db + (u >> 1)) ^ vswz<D>(r)) << 4) + (u & 1) * 8;
     }
   }
-  // K operand offsets: row 16*kb + l16, 16-byte chunk 4*ks + grp
-  int koff[4];
+  // K operand offsets: row 16*kb + l16, 16-byte chunk 4*ks + grp (the K
+  // swizzle does not depend on row bit 4, so one offset serves both kb)
+  int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) koff[ks] = l16 * 256 + (((4 * ks + grp) ^ kswz(l16)) << 4);
+  for (int ks = 0; ks < KS; ++ks)
+    koff[ks] = l16 * geo::RB + (((4 * ks + grp) ^ kswz<D>(l16)) << 4);
 
-  f32x4 o[8];
+  f32x4 o[NB][DB];
+  float m_run[NB], l_run[NB];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
+  }
 
   auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
     const int k0 = c0 + s * STEP;
     // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
-    // query column l16
-    f32x4 sc[2];
+    // query column l16 of head block nb
+    f32x4 sc[NB][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *(lds_bf16x8*)(kst + kb * 4096 + koff[ks]);
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sc[kb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) sc[nb][kb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(lds_bf16x8*)(kst + kb * 16 * geo::RB + koff[ks]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], sc[nb][kb], 0, 0, 0);
       }
     }
     if (k0 + STEP > n || k0 < lo) {
@@ -205,46 +250,56 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + kb * 16 + grp * 4 + r;
-          if (key >= n || key < lo) sc[kb][r] = -INFINITY;
+          if (key >= n || key < lo) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sc[nb][kb][r] = -INFINITY;
+          }
         }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_cand = mx * p.c;  // every step run holds a visible key: finite
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + TAU)) {
-      const float m_new = fmaxf(m_run, m_cand);
-      const float alpha = exp2_fast(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    bf16x8 pf[NB];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) o[db] *= alpha;
-    }
-    float rs = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 (&t)[2] = sc[nb];
+      float mx = fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
+                       fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_cand = mx * p.c;  // every step run holds a visible key: finite
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + TAU)) {
+        const float m_new = fmaxf(m_run[nb], m_cand);
+        const float alpha = exp2_fast(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = exp2_fast(__builtin_fmaf(sc[kb][r], p.c, -m_run));
-        sc[kb][r] = e;
-        rs += e;
+        for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
       }
-    l_run += rs;
-    u32x4 pk;
-    pk[0] = pack_bf16x2(sc[0][0], sc[0][1]);
-    pk[1] = pack_bf16x2(sc[0][2], sc[0][3]);
-    pk[2] = pack_bf16x2(sc[1][0], sc[1][1]);
-    pk[3] = pack_bf16x2(sc[1][2], sc[1][3]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+      float rs = 0.f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2_fast(__builtin_fmaf(t[kb][r], p.c, -m_run[nb]));
+          t[kb][r] = e;
+          rs += e;
+        }
+      l_run[nb] += rs;
+      u32x4 pk;
+      pk[0] = pack_bf16x2(t[0][0], t[0][1]);
+      pk[1] = pack_bf16x2(t[0][2], t[0][3]);
+      pk[2] = pack_bf16x2(t[1][0], t[1][1]);
+      pk[3] = pack_bf16x2(t[1][2], t[1][3]);
+      pf[nb] = __builtin_bit_cast(bf16x8, pk);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[db], 0, 0, 0);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
     }
   };
 
@@ -252,38 +307,46 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // 1.  Before step s the copies of steps s and s + 1 are outstanding; once
   // step s has read its stage, the copies of step s + 2 go into it.
   for (int s = s0; s < nsteps; s += 2) {
-    wait_vm<16>();
+    wait_vm<PER_STEP>();
     step(s, K0, V0);
-    load_rows<true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
-    load_rows<false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
-    wait_vm<16>();
+    load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
+    load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
+    wait_vm<PER_STEP>();
     if (s + 1 < nsteps) step(s + 1, K1, V1);
-    load_rows<true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
-    load_rows<false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
+    load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
+    load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
   }
   wait_vm<0>();  // no copy may still target LDS when the wave ends
 
   // partial of this chunk: O^T register r of block db is d = 16*db + 4*grp + r
   // of query column l16
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (l16 < G) {
-    const size_t part = (((size_t)b * p.Nkv + g) * p.n_slots + blockIdx.x) * G + l16;
-    float* dst = p.ws_o + part * D + 4 * grp;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db];
-    if (grp == 0) {
-      p.ws_ml[part * 2 + 0] = m_run;
-      p.ws_ml[part * 2 + 1] = l_run;
+  for (int nb = 0; nb < NB; ++nb) {
+    float l_tot = l_run[nb];
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int hh = 16 * nb + l16;
+    if (hh < G) {
+      const size_t part = (((size_t)b * p.Nkv + g) * p.n_slots + blockIdx.x) * G + hh;
+      float* dst = p.ws_o + part * D + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[nb][db];
+      if (grp == 0) {
+        p.ws_ml[part * 2 + 0] = m_run[nb];
+        p.ws_ml[part * 2 + 1] = l_tot;
+      }
     }
   }
 }
 
 // One wavefront per (sequence, query head): merge the chunk partials.  Lanes
 // first read the chunks' (m, l) side by side and reduce them across the
-// wavefront; then each lane accumulates two head-dims over the chunks, with
+// wavefront; then each lane accumulates D/64 head-dims over the chunks, with
 // the chunk weights broadcast from the lane that computed them.
+template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
+  constexpr int PL = D / 64;  // head-dims per lane
+  typedef float fvec __attribute__((ext_vector_type(PL)));
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.B * p.Nq) return;
@@ -298,11 +361,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
   const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_slots * G + hh;  // slot x: part0 + x*G
 
-  float M = -INFINITY;
   const int ns = max(0, nc - c_lo);  // slots written
+  float M = -INFINITY;
   for (int x = lane; x < ns; x += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)x * G) * 2]);
   M = wave_max(M);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  float L = 0.f;
+  fvec acc = {};
   for (int cb = 0; cb < ns; cb += 64) {
     // lane j of this batch holds slot cb + j's weight
     float wgt = 0.f;
@@ -314,41 +378,44 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     const int cnt = min(64, ns - cb);
     int j = 0;
     for (; j + 4 <= cnt; j += 4) {
-      f32x2 ov[4];
+      fvec ov[4];
       float wj[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        ov[u] = *reinterpret_cast<const f32x2*>(p.ws_o + (part0 + (size_t)(cb + j + u) * G) * D + lane * 2);
+        ov[u] = *reinterpret_cast<const fvec*>(p.ws_o + (part0 + (size_t)(cb + j + u) * G) * D + lane * PL);
         wj[u] = __shfl(wgt, j + u, 64);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o0 = __builtin_fmaf(wj[u], ov[u][0], o0);
-        o1 = __builtin_fmaf(wj[u], ov[u][1], o1);
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wj[u], ov[u][e], acc[e]);
     }
     for (; j < cnt; ++j) {
-      const f32x2 ov = *reinterpret_cast<const f32x2*>(p.ws_o + (part0 + (size_t)(cb + j) * G) * D + lane * 2);
+      const fvec ov = *reinterpret_cast<const fvec*>(p.ws_o + (part0 + (size_t)(cb + j) * G) * D + lane * PL);
       const float wj = __shfl(wgt, j, 64);
-      o0 = __builtin_fmaf(wj, ov[0], o0);
-      o1 = __builtin_fmaf(wj, ov[1], o1);
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wj, ov[e], acc[e]);
     }
   }
   L = wave_sum(L);
   const float inv = 1.f / L;  // n < 1 leaves L = 0: NaN row
-  *reinterpret_cast<uint32_t*>(p.O + (size_t)row * D + lane * 2) = pack_bf16x2(o0 * inv, o1 * inv);
+  __bf16* dst = p.O + (size_t)row * D + lane * PL;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) dst[e] = (__bf16)(acc[e] * inv);
   if (p.LSE != nullptr && lane == 0) p.LSE[row] = (M + __log2f(L)) * kLn2;
 }
 
 }  // namespace
 
-bool decode_bf16_d128_supported(int Nq, int Nkv) { return Nq / Nkv <= 16; }
+bool decode_bf16_supported(int Nq, int Nkv, int Dh) {
+  return (Dh == 64 || Dh == 128 || Dh == 256) && Nq / Nkv <= 32;
+}
 
 // Keys per chunk: the longest candidate that still gives the grid at least
 // 2048 (sequence, K/V head, chunk) items when every sequence has L visible
 // keys (L = Tcap, or the window when it is shorter).  The candidates are
 // multiples of 32 keys, none a power of two.
-int decode_bf16_d128_chunk(int B, int Nkv, int L) {
+int decode_bf16_chunk(int B, int Nkv, int L) {
   static const int kChunks[] = {1792, 1152, 896, 640, 384, 224, 160, 96};
   const long long heads = (long long)B * Nkv;
   for (int ch : kChunks)
@@ -357,31 +424,41 @@ int decode_bf16_d128_chunk(int B, int Nkv, int L) {
 }
 
 namespace {
-// visible keys at most, chunk length, and partial slots per (sequence, K/V head)
+// chunk length and partial slots per (sequence, K/V head)
 struct DecodePlan {
   int ch, n_slots;
 };
 DecodePlan decode_plan(int B, int Nkv, int Tcap, int window) {
   const int L = (window > 0 && window < Tcap) ? window : Tcap;
   DecodePlan d;
-  d.ch = decode_bf16_d128_chunk(B, Nkv, L);
+  d.ch = decode_bf16_chunk(B, Nkv, L);
   const int all = (Tcap + d.ch - 1) / d.ch;
   // a window of L keys starting anywhere touches at most ceil(L / ch) + 1 chunks
   d.n_slots = L < Tcap ? std::min(all, (L + d.ch - 1) / d.ch + 1) : all;
   return d;
 }
+
+template <int D, int NB>
+hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_partial_kernel<D, NB>), dim3(p.n_slots, p.Nkv, p.B), dim3(64), 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = p.B * p.Nq;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 }  // namespace
 
-size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap, int window) {
+size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
   const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
   const size_t parts = (size_t)B * Nq * d.n_slots;  // B * Nkv * n_slots * G
-  return parts * D * sizeof(float) + parts * 2 * sizeof(float);
+  return parts * Dh * sizeof(float) + parts * 2 * sizeof(float);
 }
 
-hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
-                                   const int32_t* lens, void* O, float* LSE, int B, int Nq,
-                                   int Nkv, int Tcap, int window, float scale, void* ws,
-                                   hipStream_t stream) {
+hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
+                              void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
+                              int window, float scale, void* ws, hipStream_t stream) {
   const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
   DecParams p;
   p.q = static_cast<const __bf16*>(q);
@@ -399,16 +476,17 @@ hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc
   p.n_slots = d.n_slots;
   const size_t parts = (size_t)B * Nq * p.n_slots;
   p.ws_o = static_cast<float*>(ws);
-  p.ws_ml = p.ws_o + parts * D;
+  p.ws_ml = p.ws_o + parts * Dh;
   p.window = window;
   p.c = kLog2e * scale;
   if (Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(p.n_slots, Nkv, B), dim3(64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rows = B * Nq;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  const bool two = p.G > 16;
+  switch (Dh) {
+    case 64: return two ? launch_decode<64, 2>(p, stream) : launch_decode<64, 1>(p, stream);
+    case 128: return two ? launch_decode<128, 2>(p, stream) : launch_decode<128, 1>(p, stream);
+    case 256: return two ? launch_decode<256, 2>(p, stream) : launch_decode<256, 1>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

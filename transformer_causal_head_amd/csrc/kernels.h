@@ -26,16 +26,15 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
                                int kv_rows, const int32_t* lens, int causal, int window,
                                float scale, int is_bf16, hipStream_t stream);
 
-// bf16, Dh == 128 split-K decode (partials + log-sum-exp merge).  The query
-// of sequence b sees keys max(0, lens[b] - window) .. lens[b] - 1 (window 0:
-// all of them).
-int decode_bf16_d128_chunk(int B, int Nkv, int L);
-size_t decode_bf16_d128_workspace(int B, int Nq, int Nkv, int Tcap, int window);
-bool decode_bf16_d128_supported(int Nq, int Nkv);
-hipError_t launch_decode_bf16_d128(const void* q, const void* Kc, const void* Vc,
-                                   const int32_t* lens, void* O, float* LSE, int B, int Nq,
-                                   int Nkv, int Tcap, int window, float scale, void* ws,
-                                   hipStream_t stream);
+// bf16 split-K decode (partials + log-sum-exp merge), head size 64, 128 or
+// 256, up to 32 query heads per K/V head.  The query of sequence b sees keys
+// max(0, lens[b] - window) .. lens[b] - 1 (window 0: all of them).
+bool decode_bf16_supported(int Nq, int Nkv, int Dh);
+int decode_bf16_chunk(int B, int Nkv, int L);
+size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window);
+hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
+                              void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
+                              int window, float scale, void* ws, hipStream_t stream);
 
 // Copy Snew new K and V rows per (sequence, K/V head) into the caches at
 // positions pos[b] .. pos[b] + Snew - 1, or at those positions modulo Tcap
