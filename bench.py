@@ -191,6 +191,45 @@ def _cache_paths(torch, dev, tch, steps, warmup):
           flush=True)
 
 
+def _head_sizes(torch, dev, tch, steps, warmup):
+    """One JSON line per shape: causal MHA prefill at head sizes 64 / 128 / 256 with the same
+    32-head layout, and the batched decode workload at head sizes 64 / 256 and as MQA."""
+    for Dh, S in ((64, 32768), (128, 32768), (256, 16384)):
+        B, H = 1, 32
+        q, k, v = workloads.prefill_inputs(B, H, H, S, Dh, "bf16", seed=0)
+        tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+        del q, k, v
+        O = torch.empty_like(tq)
+        L = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        ms = _time(torch, lambda: tch.attn_prefill(tq, tk, tv, O, L, causal=1,
+                                                   scale=1.0 / math.sqrt(Dh)), steps, warmup)
+        flop, _ = workloads.prefill_work(B, H, H, S, Dh, True, 0, 2)
+        tf = flop / (ms * 1e-3) / 1e12
+        print(json.dumps({"path": "attn_prefill", "workload": f"B={B} heads={H} S={S} Dh={Dh} "
+                          "bf16 causal", "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        del tq, tk, tv, O, L
+    dc = workloads.WORKLOADS[DECODE]
+    for Dh, Nq, Nkv in ((64, 32, 8), (256, 32, 8), (128, 32, 1)):
+        B, T = dc["B"], dc["Tcap"]
+        lens, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, T, dc["len_lo"], dc["len_hi"])
+        tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+        del kc, vc
+        tl = torch.from_numpy(lens).to(dev)
+        O = torch.empty_like(tq)
+        L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, T, tch.ATTN_BF16)),
+                         dtype=torch.uint8, device=dev)
+        ms = _time(torch, lambda: tch.attn_decode(tq, tk, tv, tl, O, L, ws), steps, warmup)
+        _, nbytes = workloads.decode_work(lens, Nq, Nkv, Dh, 2)
+        gbs = nbytes / ms / 1e6
+        print(json.dumps({"path": "attn_decode", "workload": f"B={B} Nq={Nq} Nkv={Nkv} Dh={Dh} "
+                          f"Tcap={T} sum(lens)={int(lens.sum())} bf16", "ms": round(ms, 4),
+                          "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": nbytes}), flush=True)
+        del tq, tk, tv, O, L, ws
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +240,9 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run only the streaming-read probe over 4.5 GB (HBM reference point)")
+    ap.add_argument("--head-sizes", action="store_true",
+                    help="time prefill and decode at head sizes 64 / 256 and decode with 32 "
+                         "query heads per K/V head instead of the main step")
     ap.add_argument("--cache-paths", action="store_true",
                     help="time the cache-side entry points (chunked prefill, windowed and "
                          "rolling-buffer decode, append) instead of the main step")
@@ -227,6 +269,9 @@ def main():
         return
     if args.cache_paths:
         _cache_paths(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
+        return
+    if args.head_sizes:
+        _head_sizes(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
 
     pc = workloads.WORKLOADS[PREFILL]
