@@ -1,5 +1,5 @@
 """Float64 CPU oracle of causal scaled dot-product attention (prefill, chunked
-prefill against a cache, decode, cache append).
+prefill against a cache, decode, cache append, and the backward pass).
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the package's smoke
 check and the benchmark's CPU-baseline leg, never by the GPU library.  It is
@@ -13,11 +13,13 @@ from .attention import (
     append_ref,
     attention_ref,
     attention_rows_ref,
+    backward_ref,
     chunk_ref,
     decode_ref,
     head_attention,
     kv_head_of,
     softmax_rows,
+    softmax_vjp,
 )
 
 __all__ = [
@@ -25,9 +27,11 @@ __all__ = [
     "append_ref",
     "attention_ref",
     "attention_rows_ref",
+    "backward_ref",
     "chunk_ref",
     "decode_ref",
     "head_attention",
     "kv_head_of",
     "softmax_rows",
+    "softmax_vjp",
 ]

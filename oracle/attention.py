@@ -44,7 +44,11 @@ Readings taken where the pages leave a choice open:
   * a rolling-buffer cache of capacity W stores position p in slot p mod W;
     with the new token appended first, the buffer holds exactly the W
     positions a window of W admits, in rotated order, which the softmax does
-    not see.
+    not see;
+  * the backward pass differentiates the same definition: the softmax
+    Jacobian is dp_i/dz_j = p_i (delta_ij - p_j) (textbook, "Почему делить
+    на корень из d_h"), the rest is the chain rule through the two products;
+    a K/V head shared by G query heads collects the gradients of all of them.
 """
 
 import numpy as np
@@ -288,3 +292,57 @@ def append_ref(Kc, Vc, Knew, Vnew, pos, rolling=False):
             Kc[b, :, slot] = Knew[b, :, i]
             Vc[b, :, slot] = Vnew[b, :, i]
     return Kc, Vc
+
+
+def softmax_vjp(P, dP):
+    """Vector-Jacobian product of the row softmax: given P = softmax(Z) row by
+    row and dL/dP, returns dL/dZ.
+
+    Textbook, "Почему делить на корень из d_h": dp_i/dz_j = p_i (delta_ij - p_j),
+    so dL/dz_j = sum_i dL/dp_i * p_i (delta_ij - p_j) = p_j (dP_j - sum_i p_i dP_i).
+    Masked entries have p = 0 and receive 0.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    dP = np.asarray(dP, dtype=np.float64)
+    return P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
+
+
+def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
+    """Gradients of the prefill attention output with respect to Q, K and V.
+
+    Q: [B,Nq,S,Dh], K, V: [B,Nkv,S,Dh], dO = dL/dO: [B,Nq,S,Dh].  Returns
+    (dQ, dK, dV) in float64 with the shapes of Q, K, V.  Per (b, h) with
+    g = kv_head_of(h), by the chain rule through A = scale * Q K^T + M,
+    P = softmax(A) (row-wise), O = P V:
+        dV[g] += P^T dO,   dP = dO V^T,   dA = softmax_vjp(P, dP),
+        dQ     = scale * dA K,   dK[g] += scale * dA^T Q.
+    A K/V head shared by several query heads (GQA/MQA) sums their
+    contributions (textbook, "Как K/V-головы доходят до голов Q": the shared
+    head is repeated, so its gradient is the sum over the repeats).  The
+    weights are recomputed from the inputs here, as the textbook's
+    FlashAttention section says the backward pass does.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, Nq, Nkv, S, Dh = _check_prefill_shapes(Q, K, V)
+    if dO.shape != Q.shape:
+        raise ValueError("dO must have the shape of Q")
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    rows = np.arange(S)
+    for b in range(B):
+        for h in range(Nq):
+            g = kv_head_of(h, Nq, Nkv)
+            _, _, P = head_attention(Q[b, h], rows, K[b, g], V[b, g], causal, window, scale,
+                                     return_probs=True)
+            dV[b, g] += P.T @ dO[b, h]
+            dP = dO[b, h] @ V[b, g].T
+            dA = softmax_vjp(P, dP)
+            dQ[b, h] = scale * (dA @ K[b, g])
+            dK[b, g] += scale * (dA.T @ Q[b, h])
+    return dQ, dK, dV
