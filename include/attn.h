@@ -192,6 +192,39 @@ int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcach
                    const int32_t* pos, int B, int Nkv, int Snew, int Dh, int Tcap,
                    int rolling, int dtype, void* stream);
 
+/*
+ * attn_backward_workspace_bytes -- bytes of device workspace attn_backward
+ * needs (one fp32 per query row).  Pure host function; 0 for invalid arguments.
+ */
+size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int dtype);
+
+/*
+ * attn_backward -- gradients of attn_prefill's output with respect to Q, K and
+ * V (training).  The weights are recomputed from the stored LSE instead of
+ * being read (textbook, "Эффективные реализации": FlashAttention recomputes
+ * the weight matrix by blocks on the backward pass); the softmax Jacobian is
+ * p_i (delta_ij - p_j) ("Почему делить на корень из d_h").  With
+ * P = exp(scale Q K^T + M - LSE):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q;
+ * a K/V head shared by G query heads receives the sum of their gradients.
+ *
+ *   Q, O, dO, dQ  [B, Nq,  S, Dh]   forward input, forward output, dL/dO, dL/dQ
+ *   K, V, dK, dV  [B, Nkv, S, Dh]   forward inputs and their gradients
+ *   LSE           [B, Nq,  S] fp32  the LSE attn_prefill returned for this O
+ *   causal, window, scale, dtype    as passed to attn_prefill
+ *   workspace / workspace_bytes     device scratch of at least
+ *                                   attn_backward_workspace_bytes(...) bytes
+ * dQ, dK, dV are written in the element type of the inputs (accumulation in
+ * fp32); they are overwritten, not accumulated into.
+ * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP.
+ */
+int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* LSE, void* dQ, void* dK, void* dV,
+                  int B, int Nq, int Nkv, int S, int Dh,
+                  int causal, int window, float scale,
+                  void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
 /* attn_strerror -- static description of an attn_status value. */
 const char* attn_strerror(int status);
 

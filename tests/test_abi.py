@@ -212,3 +212,36 @@ def _append(**kw):
 ])
 def test_kv_append_rejects(kw, code):
     assert _append(**kw) == code
+
+
+def _backward(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, B=1,
+             Nq=4, Nkv=2, S=16, Dh=128, causal=1, window=0, scale=0.125, ws=FAKE,
+             ws_bytes=1 << 20, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_backward(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"],
+                                   a["dK"], a["dV"], a["B"], a["Nq"], a["Nkv"], a["S"], a["Dh"],
+                                   a["causal"], a["window"], a["scale"], a["ws"], a["ws_bytes"],
+                                   a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), tch.ATTN_EINVAL),
+    (dict(LSE=None), tch.ATTN_EINVAL),
+    (dict(dV=None), tch.ATTN_EINVAL),
+    (dict(S=0), tch.ATTN_EINVAL),
+    (dict(causal=0, window=3), tch.ATTN_EINVAL),
+    (dict(scale=0.0), tch.ATTN_EINVAL),
+    (dict(Nq=6, Nkv=4), tch.ATTN_EGQA),
+    (dict(Dh=512), tch.ATTN_EUNSUPPORTED),
+    (dict(ws=None), tch.ATTN_EWORKSPACE),
+    (dict(ws_bytes=4), tch.ATTN_EWORKSPACE),
+])
+def test_backward_rejects(kw, code):
+    assert _backward(**kw) == code
+
+
+def test_backward_workspace_query():
+    assert tch.attn_backward_workspace_bytes(2, 8, 2, 100, 128, tch.ATTN_BF16) == 2 * 8 * 100 * 4
+    assert tch.attn_backward_workspace_bytes(2, 8, 3, 100, 128, tch.ATTN_BF16) == 0

@@ -1,0 +1,106 @@
+"""GPU parity of attn_backward against the float64 oracle's gradients.
+
+The GPU forward produces O and LSE, as in training; the backward then takes
+dO.  The oracle computes the exact gradients of the same definition from the
+stored inputs.  Tolerance, from the arithmetic (see the backward section of
+the design notes): the gradients are stored in bf16 and Delta = dO . O uses
+the bf16-stored O, so a correct kernel differs from the exact values by up to
+~0.9 % of (1 + |ref|) and ~5e-4 on average on these inputs (an emulation of
+those roundings against the oracle); the bound is twice that.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_causal_head_amd as tch
+import workloads
+from helpers import device, say
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL = 1.6e-2   # per element: |err| <= BF16_REL * (1 + |ref|)
+BF16_MEAN = 1e-3
+F32_REL = 1e-4
+
+
+def _grads(q, k, v, dO, dtype, causal, window, scale=None):
+    dev = device()
+    tq, tk, tv, tdo = (workloads.to_torch(x, dtype, dev) for x in (q, k, v, dO))
+    O, L = tch.prefill(tq, tk, tv, causal=causal, window=window, scale=scale)
+    dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo, causal=causal, window=window, scale=scale)
+    torch.cuda.synchronize()
+    return [workloads.to_f64(workloads.from_torch(t, dtype), dtype) for t in (dQ, dK, dV)]
+
+
+def _check(got, ref, dtype, what):
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        err = np.abs(g - r)
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        rel = BF16_REL if dtype == "bf16" else F32_REL
+        worst = np.argmax(err - rel * (1 + np.abs(r)))
+        assert np.all(err <= rel * (1 + np.abs(r))), (
+            f"{what} {name}: err {err.flat[worst]:.3g} at {np.unravel_index(worst, err.shape)} "
+            f"ref {r.flat[worst]:.3g}")
+        if dtype == "bf16":
+            assert err.mean() <= BF16_MEAN, f"{what} {name}: mean err {err.mean():.3g}"
+        out.append(f"{name} {err.max():.2e}/{err.mean():.2e}")
+    say(f"backward {what}: " + " ".join(out))
+
+
+def _inputs(B, Nq, Nkv, S, Dh, dtype, seed):
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, dtype, seed=seed)
+    dO = workloads.draw((B, Nq, S, Dh), dtype, seed, 3)
+    return q, k, v, dO
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,causal,window", [
+    (1, 2, 2, 1, 128, True, 0),
+    (2, 4, 4, 63, 128, True, 0),
+    (1, 4, 2, 65, 128, True, 0),
+    (1, 8, 2, 300, 128, True, 0),       # GQA 4, ragged
+    (1, 4, 1, 257, 128, True, 0),       # MQA
+    (1, 4, 4, 700, 128, True, 100),     # window
+    (1, 4, 2, 130, 128, False, 0),      # non-causal
+    (2, 4, 1, 257, 64, True, 0),
+    (1, 2, 2, 200, 256, True, 30),
+])
+def test_backward_bf16(B, Nq, Nkv, S, Dh, causal, window):
+    q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, "bf16", seed=S + Dh)
+    got = _grads(q, k, v, dO, "bf16", causal, window)
+    ref = oracle.backward_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v, dO)),
+                              causal=causal, window=window)
+    _check(got, ref, "bf16", (B, Nq, Nkv, S, Dh, causal, window))
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window,scale", [
+    (1, 2, 2, 5, 4, 0, 0.5),            # the tiny fp32 workload's shape
+    (1, 4, 2, 100, 64, 7, 0.1),
+    (2, 2, 1, 33, 80, 0, None),
+])
+def test_backward_f32(B, Nq, Nkv, S, Dh, window, scale):
+    q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, "f32", seed=Dh)
+    got = _grads(q, k, v, dO, "f32", True, window, scale)
+    ref = oracle.backward_ref(*(workloads.to_f64(x, "f32") for x in (q, k, v, dO)),
+                              causal=True, window=window, scale=scale)
+    _check(got, ref, "f32", (B, Nq, Nkv, S, Dh, window))
+
+
+def test_backward_deterministic():
+    q, k, v, dO = _inputs(1, 8, 2, 400, 128, "bf16", seed=5)
+    a = _grads(q, k, v, dO, "bf16", True, 0)
+    b = _grads(q, k, v, dO, "bf16", True, 0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_workspace_checked():
+    dev = device()
+    t = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16, device=dev)
+    L = torch.zeros(1, 2, 16, dtype=torch.float32, device=dev)
+    small = torch.empty(8, dtype=torch.uint8, device=dev)
+    with pytest.raises(tch.AttnError) as e:
+        tch.attn_backward(t, t, t, t, t, L, t.clone(), t.clone(), t.clone(), workspace=small)
+    assert e.value.status == tch.ATTN_EWORKSPACE

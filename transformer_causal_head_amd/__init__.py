@@ -14,11 +14,15 @@ Entry points (same names as the C ABI):
     attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype)
     attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype)
     attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None)
+    attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
+                  workspace=None, stream=None)
+    attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype)
     attn_strerror(status)
 Conveniences that allocate outputs with torch:
     prefill(q, k, v, causal=True, window=0, scale=None) -> (O, LSE)
     prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
     decode(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
+    backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None) -> (dQ, dK, dV)
 """
 
 import ctypes
@@ -39,7 +43,8 @@ ATTN_F32 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
            "attn_decode_workspace_bytes", "attn_decode_window_workspace_bytes",
-           "attn_kv_append", "attn_strerror")
+           "attn_kv_append", "attn_backward", "attn_backward_workspace_bytes",
+           "attn_strerror")
 
 _lib = None
 
@@ -78,6 +83,11 @@ def lib():
         L.attn_decode_window.restype = i32
         L.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         L.attn_kv_append.restype = i32
+        L.attn_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.attn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                    i32, i32, f32, vp, ctypes.c_size_t, i32, vp]
+        L.attn_backward.restype = i32
         L.attn_strerror.argtypes = [i32]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -218,6 +228,48 @@ def attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None):
                               _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_kv_append")
+
+
+def attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype):
+    return int(lib().attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype))
+
+
+def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
+                  workspace=None, stream=None):
+    """Gradients of attn_prefill; shapes as attn_prefill, dQ like Q, dK/dV like K."""
+    B, Nq, S, Dh = Q.shape
+    Nkv = K.shape[1]
+    if tuple(K.shape) != (B, Nkv, S, Dh) or K.shape != V.shape:
+        raise ValueError("K and V must be [B, Nkv, S, Dh]")
+    if O.shape != Q.shape or dO.shape != Q.shape or dQ.shape != Q.shape:
+        raise ValueError("O, dO, dQ must have the shape of Q")
+    if dK.shape != K.shape or dV.shape != K.shape:
+        raise ValueError("dK, dV must have the shape of K")
+    if len({t.dtype for t in (Q, K, V, O, dO, dQ, dK, dV)}) != 1:
+        raise ValueError("all tensors but LSE must share one dtype")
+    if tuple(LSE.shape) != (B, Nq, S) or LSE.dtype.itemsize != 4:
+        raise ValueError("LSE must be fp32 [B, Nq, S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ),
+                             _ptr(dK), _ptr(dV), B, Nq, Nkv, S, Dh, int(causal), int(window),
+                             float(scale), _ptr(workspace), ws_bytes, _dtype_code(Q),
+                             _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_backward")
+
+
+def backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None):
+    """Allocate dQ, dK, dV and the workspace with torch and run attn_backward."""
+    import torch
+    dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    B, Nq, S, Dh = q.shape
+    n = attn_backward_workspace_bytes(B, Nq, k.shape[1], S, Dh, _dtype_code(q))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    attn_backward(q, k, v, O, dO, LSE, dQ, dK, dV, causal=int(causal), window=window, scale=scale,
+                  workspace=ws)
+    return dQ, dK, dV
 
 
 def prefill(q, k, v, causal=True, window=0, scale=None):

@@ -126,13 +126,38 @@ int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcach
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int dtype) {
+  if (validate_common(B, Nq, Nkv, Dh, dtype) != ATTN_OK || !positive(S)) return 0;
+  return attn::backward_workspace(B, Nq, S);
+}
+
+int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* LSE, void* dQ, void* dK, void* dV, int B, int Nq, int Nkv, int S,
+                  int Dh, int causal, int window, float scale, void* workspace,
+                  size_t workspace_bytes, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return ATTN_EINVAL;
+  int st = validate_common(B, Nq, Nkv, Dh, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive(S)) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (window > 0 && !causal) return ATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  if (window < 0) window = 0;
+  const size_t need = attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(attn::launch_backward_general(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S,
+                                                Dh, causal, window, scale, workspace,
+                                                dtype == ATTN_BF16, s));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null pointer, non-positive size, bad flag or scale)";
     case ATTN_EGQA: return "number of query heads is not a multiple of the number of K/V heads";
     case ATTN_EUNSUPPORTED: return "unsupported element type or head size";
-    case ATTN_EWORKSPACE: return "decode workspace missing or too small";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_EHIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }

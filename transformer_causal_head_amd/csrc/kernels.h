@@ -43,4 +43,12 @@ hipError_t launch_kv_append(const void* Knew, const void* Vnew, void* Kc, void* 
                             const int32_t* pos, int B, int Nkv, int Snew, int Dh, int Tcap,
                             int rolling, int elem_bytes, hipStream_t stream);
 
+// Backward pass of prefill attention.  The workspace holds Delta
+// [B, Nq, S] fp32 (dO . O per row).
+size_t backward_workspace(int B, int Nq, int S);
+hipError_t launch_backward_general(const void* Q, const void* K, const void* V, const void* O,
+                                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                   int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
+                                   float scale, void* ws, int is_bf16, hipStream_t stream);
+
 }  // namespace attn
