@@ -46,6 +46,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 // Variant knobs (compile-time): 32-query blocks per wave, waves per
 // workgroup, and whether the next tile's QK^T is issued before this tile's
@@ -81,29 +82,11 @@ namespace {
 
 constexpr int QB = PREFILL_QB; // 32-query blocks per wave
 constexpr bool PIPE = PREFILL_PIPE != 0;
-constexpr int BN = 64;         // keys per K/V tile
 constexpr float TAU = 8.f;
 
-// Tile geometry for head size D (64, 128 or 256).  A K/V row is RB = 2*D
-// bytes = NC 16-byte chunks; a tile of BN rows is NP pieces of 1 KB, RP rows
-// each.  QK^T takes KS 16-wide slices of the head; PV yields DB 32-wide
-// output blocks.
-template <int D>
-struct Geo {
-  static constexpr int RB = 2 * D;
-  static constexpr int NC = D / 8;
-  static constexpr int TILE = BN * RB;
-  static constexpr int NP = TILE / 1024;
-  static constexpr int RP = 1024 / RB;
-  static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
-};
 // waves per workgroup: two per SIMD while the registers allow it
 template <int D>
 constexpr int waves_for() { return D == 128 ? PREFILL_NW : (D < 128 ? 8 : 4); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
   const __bf16* Q;
@@ -122,58 +105,6 @@ struct Params {
   int n_qtiles;
   int n_hsub;     // G / hp
 };
-
-// 16-byte chunk c of tile row r is stored at chunk position c ^ swz<D>(r).
-// Both are GF(2)-linear in the row bits, chosen (by exhaustive check of
-// every read instruction's lanes) so that the 16-byte K operand reads and
-// the transposing V reads hit distinct banks: row bits 0..3 map to chunk
-// bits 4, 10, 1, 8 for 256- and 512-byte rows, and to 2, 4, 1, 2 for 128-byte
-// rows.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 64)
-    return ((r & 1) << 1) ^ (((r >> 1) & 1) << 2) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
-  else
-    return ((r & 1) << 2) ^ (((r >> 1) & 1) * 10) ^ ((r >> 2) & 1) ^ (r & 8);
-}
-
-__device__ __forceinline__ void wait_dma() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-}
-
-// Copy keys [k0, k0+64) of one head (a buffer resource over the head) into a
-// swizzled LDS tile.  The tile is NP pieces of 1 KB (RP rows); wave w issues
-// pieces w, w + NW, ...  The whole offset is in the per-lane operand, which the
-// buffer range check covers: rows past the end of the head read as zero.
-struct HeadRef {
-  __amdgpu_buffer_rsrc_t rs;
-};
-template <int D>
-__device__ __forceinline__ HeadRef head_ref(const __bf16* head, int rows) {
-  return HeadRef{__builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, rows * D * 2, 0x00020000)};
-}
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(HeadRef h, int k0, char* tile, int w, int lane) {
-  using g = Geo<D>;
-#pragma unroll
-  for (int j = 0; j < (g::NP + NW - 1) / NW; ++j) {
-    const int piece = w + j * NW;  // wave-uniform
-    if (piece >= g::NP) break;
-    const int r = piece * g::RP + lane / g::NC;
-    const int voff = r * g::RB + (((lane % g::NC) ^ swz<D>(r)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
-                                             voff + k0 * g::RB, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ float xhalf_max(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, int QB_>
 __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>::KS],
