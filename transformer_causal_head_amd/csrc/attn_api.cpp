@@ -146,6 +146,9 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
   const size_t need = attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16 && attn::backward_bf16_supported(Dh))
+    return from_hip(attn::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S, Dh,
+                                               causal, window, scale, workspace, s));
   return from_hip(attn::launch_backward_general(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S,
                                                 Dh, causal, window, scale, workspace,
                                                 dtype == ATTN_BF16, s));

@@ -207,6 +207,24 @@ hipError_t launch_general(const BwdParams& p, hipStream_t stream) {
 
 size_t backward_workspace(int B, int Nq, int S) { return (size_t)B * Nq * S * sizeof(float); }
 
+hipError_t launch_backward_delta(const void* O, const void* dO, float* delta, long long rows, int Dh,
+                                 int is_bf16, hipStream_t stream) {
+  BwdParams p{};
+  p.O = O;
+  p.dO = dO;
+  p.delta = delta;
+  p.B = 1;
+  p.Nq = 1;
+  p.S = (int)rows;
+  p.Dh = Dh;
+  if ((rows + 3) / 4 > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (is_bf16)
+    hipLaunchKernelGGL(delta_kernel<__bf16>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(delta_kernel<float>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_backward_general(const void* Q, const void* K, const void* V, const void* O,
                                    const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                    int B, int Nq, int Nkv, int S, int Dh, int causal, int window,

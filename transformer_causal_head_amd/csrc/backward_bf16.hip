@@ -1,0 +1,457 @@
+// Backward pass of prefill attention on bf16 MFMA (head size 64 or 128; at
+// 256 the K and V fragments plus both accumulators of the dK/dV kernel exceed
+// the register file, and that size takes the general kernels).  Same mathematics as the general row kernels in backward.hip (the
+// weights recomputed from the stored LSE, the softmax Jacobian p (delta - p)
+// of the textbook's "Почему делить на корень из d_h"), split into two kernels
+// so that every gradient has a single owner and no float atomics are needed
+// (the results are bitwise reproducible):
+//
+//   dq_kernel  -- one wavefront per 32 query rows of one head, streaming the
+//                 K/V tiles of its key range like the forward pass:
+//                   S^T  = K Q^T     (A: K tile rows,  B: Q in VGPRs)
+//                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
+//                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
+//                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
+//   dkv_kernel -- one wavefront per 32 keys of one K/V head, streaming the Q and
+//                 dO tiles of every query head of its group over the queries
+//                 that see those keys:
+//                   S  = Q K^T       (A: Q tile rows,  B: K in VGPRs)
+//                   dP = dO V^T      (A: dO tile rows, B: V in VGPRs)
+//                   dV^T += dO^T P   (A: dO tile read transposed, B: P)
+//                   dK^T += Q^T dS   (A: Q tile read transposed,  B: dS)
+//
+// In both, the 32x32 score accumulator is used directly (rounded to bf16) as
+// the B operand of the product that contracts over its rows; the transposing
+// LDS reads deliver the A operand in the matching row order.  Tiles are
+// copied HBM -> LDS by buffer DMA, two stages, with the swizzle of tiles.h.
+
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace attn {
+
+namespace {
+
+struct BwdMfmaParams {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  const __bf16* dO;
+  const float* LSE;
+  const float* delta;
+  __bf16* dQ;
+  __bf16* dK;
+  __bf16* dV;
+  int B, Nq, Nkv, S;
+  int causal, window;
+  float c;       // scale * log2(e)
+  float scale;
+  int G;         // query heads per K/V head
+  // dq_kernel grid
+  int hp, qspan, n_qtiles, n_hsub;
+};
+
+// Mask of one 32x32 accumulator: rows (r/4)*8 + hl*4 + r%4 of the block,
+// column ln.  Visible iff key <= query (causal), query - key < window, and
+// both below S.
+__device__ __forceinline__ bool visible(const BwdMfmaParams& p, int q, int k) {
+  bool ok = q < p.S && k < p.S;
+  if (p.causal) ok = ok && k <= q;
+  if (p.window > 0) ok = ok && q - k < p.window;
+  return ok;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one wavefront = 32 query rows of one head; workgroup as in the forward
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
+  using geo = Geo<D>;
+  constexpr int KS = geo::KS;
+  constexpr int DB = geo::DB;
+  __shared__ __attribute__((aligned(1024))) char k0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[geo::TILE];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hl = lane >> 5;
+
+  const int inner = p.B * p.Nkv * p.n_hsub;
+  const int bid = blockIdx.x;
+  const int qt = p.causal ? (p.n_qtiles - 1 - bid / inner) : (bid / inner);
+  int rest = bid % inner;
+  const int hsub = rest % p.n_hsub;
+  rest /= p.n_hsub;
+  const int g = rest % p.Nkv;
+  const int b = rest / p.Nkv;
+
+  const int head = g * p.G + hsub * p.hp + (w % p.hp);
+  const int qa = qt * p.qspan + (w / p.hp) * 32;  // first query row of this wave
+  const int q0 = qt * p.qspan;
+  const int q1 = min(p.S, q0 + p.qspan);
+  const int wq1 = min(p.S, qa + 32);
+  const bool wave_live = qa < p.S;
+
+  const size_t kv_base = ((size_t)b * p.Nkv + g) * (size_t)p.S * D;
+  const HeadRef Kh = head_ref<D>(p.K + kv_base, p.S);
+  const HeadRef Vh = head_ref<D>(p.V + kv_base, p.S);
+  const size_t q_row0 = ((size_t)b * p.Nq + head) * (size_t)p.S;
+
+  const int hi_key = p.causal ? q1 : p.S;
+  const int lo_key = (p.causal && p.window > 0) ? max(0, q0 - p.window + 1) : 0;
+  const int t_lo = lo_key / BN;
+  const int nt = (hi_key + BN - 1) / BN - t_lo;
+
+  load_tile<D, NW>(Kh, t_lo * BN, k0s, w, lane);
+  load_tile<D, NW>(Vh, t_lo * BN, v0s, w, lane);
+
+  // Q and dO as B operands: query column ln, head dims 16*ks + 8*hl + i
+  const int qi = min(qa + ln, p.S - 1);
+  bf16x8 qf[KS], df[KS];
+  {
+    const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.Q + (q_row0 + qi) * D + hl * 8);
+    const bf16x8* ds = reinterpret_cast<const bf16x8*>(p.dO + (q_row0 + qi) * D + hl * 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = qs[ks * 2];
+      df[ks] = ds[ks * 2];
+    }
+  }
+  const float lse2 = p.LSE[q_row0 + qi] * kLog2e;
+  const float dlt = p.delta[q_row0 + qi];
+
+  int roff[KS];
+  row_operand_offsets<D>(ln, hl, roff);
+  int troff[2][DB];
+  tr_operand_offsets<D>(lane, troff);
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+  // tiles with any visible pair for this wave, and with only visible pairs
+  auto fdiv = [](int a) { return a >= 0 ? a / BN : -((-a + BN - 1) / BN); };
+  int tl_lo = p.window > 0 ? fdiv(qa - p.window + 1) : -1;
+  int tl_hi = p.causal ? fdiv(wq1 - 1) : (p.S - 1) / BN;
+  if (!wave_live) tl_hi = tl_lo - 1;
+  int tf_lo = p.window > 0 ? -fdiv(-(wq1 - p.window)) : 0;
+  int tf_hi = fdiv(p.S - BN);
+  if (p.causal) tf_hi = min(tf_hi, fdiv(qa - (BN - 1)));
+  tl_lo = __builtin_amdgcn_readfirstlane(tl_lo);
+  tl_hi = __builtin_amdgcn_readfirstlane(tl_hi);
+  tf_lo = __builtin_amdgcn_readfirstlane(tf_lo);
+  tf_hi = __builtin_amdgcn_readfirstlane(tf_hi);
+
+  for (int i = 0; i < nt; ++i) {
+    const int t = t_lo + i;
+    const char* Kt = (i & 1) ? k1s : k0s;
+    const char* Vt = (i & 1) ? v1s : v0s;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this tile's copies have landed
+    __syncthreads();
+    if (i + 1 < nt) {
+      load_tile<D, NW>(Kh, (t + 1) * BN, (i & 1) ? k0s : k1s, w, lane);
+      load_tile<D, NW>(Vh, (t + 1) * BN, (i & 1) ? v0s : v1s, w, lane);
+    }
+    if (t < tl_lo || t > tl_hi) continue;
+    const bool need_mask = t < tf_lo || t > tf_hi;
+    const int k0 = t * BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * geo::RB + roff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + kb * 32 * geo::RB + roff[ks]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+      }
+      // register r: key k0 + 32*kb + 8*(r/4) + 4*hl + r%4, query qa + ln
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (!visible(p, qa + ln, key)) s[r] = -INFINITY;
+        }
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = kk * 8 + 2 * j;
+          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2));
+          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2));
+          pk[j] = pack_bf16x2(p0 * (dp[r0] - dlt), p1 * (dp[r0 + 1] - dlt));
+        }
+        dsf[kk] = __builtin_bit_cast(bf16x8, pk);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = read_tr_operand<D>(Kt, kb * 2 + kk, troff, db);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], dq[db], 0, 0, 0);
+        }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS when the wave ends
+
+  if (!wave_live || qa + ln >= p.S) return;
+  __bf16* row = p.dQ + (q_row0 + qa + ln) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d0 = db * 32 + a4 * 8 + hl * 4;
+      u32x2 st;
+      st[0] = pack_bf16x2(dq[db][a4 * 4 + 0] * p.scale, dq[db][a4 * 4 + 1] * p.scale);
+      st[1] = pack_bf16x2(dq[db][a4 * 4 + 2] * p.scale, dq[db][a4 * 4 + 3] * p.scale);
+      *reinterpret_cast<u32x2*>(row + d0) = st;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one wavefront = 32 keys of one K/V head; workgroup = NW waves of
+// consecutive keys; loops over (query head of the group, query tile).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
+  using geo = Geo<D>;
+  constexpr int KS = geo::KS;
+  constexpr int DB = geo::DB;
+  constexpr int KB = NW * 32;  // keys per workgroup
+  __shared__ __attribute__((aligned(1024))) char q0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char q1s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char o0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char o1s[geo::TILE];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hl = lane >> 5;
+
+  const int n_kb = (p.S + KB - 1) / KB;
+  const int kt = blockIdx.x % n_kb;  // key blocks in ascending order: heaviest first
+  const int bg = blockIdx.x / n_kb;
+  const int g = bg % p.Nkv;
+  const int b = bg / p.Nkv;
+
+  const int k0 = kt * KB;
+  const int k1 = min(p.S, k0 + KB);
+  const int kw0 = k0 + w * 32;          // this wave's first key
+  const int kw1 = min(p.S, kw0 + 32);
+  const bool wave_live = kw0 < p.S;
+  const size_t kv_row0 = ((size_t)b * p.Nkv + g) * (size_t)p.S;
+
+  // query range of the workgroup: queries that see any of its keys
+  const int qlo = p.causal ? k0 : 0;
+  const int qhi = (p.causal && p.window > 0) ? min(p.S, k1 - 1 + p.window) : p.S;
+  const int t_lo = qlo / BN;
+  const int n_qt = (qhi + BN - 1) / BN - t_lo;  // query tiles per head
+  const int n_items = p.G * max(n_qt, 0);
+
+  auto head_refs = [&](int item, HeadRef& hq, HeadRef& ho, int& q0) {
+    const int hh = item / n_qt;
+    q0 = (t_lo + item % n_qt) * BN;
+    const size_t base = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S * D;
+    hq = head_ref<D>(p.Q + base, p.S);
+    ho = head_ref<D>(p.dO + base, p.S);
+  };
+  if (n_items > 0) {
+    HeadRef hq, ho;
+    int q0;
+    head_refs(0, hq, ho, q0);
+    load_tile<D, NW>(hq, q0, q0s, w, lane);
+    load_tile<D, NW>(ho, q0, o0s, w, lane);
+  }
+
+  // K and V as B operands: key column ln, head dims 16*ks + 8*hl + i
+  const int kj = min(kw0 + ln, p.S - 1);
+  bf16x8 kf[KS], vf[KS];
+  {
+    const bf16x8* ks_ = reinterpret_cast<const bf16x8*>(p.K + (kv_row0 + kj) * D + hl * 8);
+    const bf16x8* vs_ = reinterpret_cast<const bf16x8*>(p.V + (kv_row0 + kj) * D + hl * 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = ks_[ks * 2];
+      vf[ks] = vs_[ks * 2];
+    }
+  }
+
+  int roff[KS];
+  row_operand_offsets<D>(ln, hl, roff);
+  int troff[2][DB];
+  tr_operand_offsets<D>(lane, troff);
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  for (int it = 0; it < n_items; ++it) {
+    const int hh = it / n_qt;
+    const int q0 = (t_lo + it % n_qt) * BN;
+    const char* Qt = (it & 1) ? q1s : q0s;
+    const char* Ot = (it & 1) ? o1s : o0s;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (it + 1 < n_items) {
+      HeadRef hq, ho;
+      int qn;
+      head_refs(it + 1, hq, ho, qn);
+      load_tile<D, NW>(hq, qn, (it & 1) ? q0s : q1s, w, lane);
+      load_tile<D, NW>(ho, qn, (it & 1) ? o0s : o1s, w, lane);
+    }
+    // does this wave see any (query, key) pair of the tile?  all of them?
+    bool live = wave_live && q0 < p.S;
+    if (p.causal) live = live && q0 + BN - 1 >= kw0;
+    if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
+    if (!live) continue;
+    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
+    if (p.causal) full = full && q0 >= kw1 - 1;
+    if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
+
+    const size_t qrow0 = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+      }
+      // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln.
+      // LSE and Delta of those query rows (clamped at the last row; rows past
+      // S are masked below)
+      float lse2[16], dlt[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = min(q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3), p.S - 1);
+        lse2[r] = p.LSE[qrow0 + q] * kLog2e;
+        dlt[r] = p.delta[qrow0 + q];
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
+        }
+      }
+      bf16x8 pf[2], sf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pp, ss;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = kk * 8 + 2 * j;
+          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0]));
+          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1]));
+          pp[j] = pack_bf16x2(p0, p1);
+          ss[j] = pack_bf16x2(p0 * (dp[r0] - dlt[r0]), p1 * (dp[r0 + 1] - dlt[r0 + 1]));
+        }
+        pf[kk] = __builtin_bit_cast(bf16x8, pp);
+        sf[kk] = __builtin_bit_cast(bf16x8, ss);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 oa = read_tr_operand<D>(Ot, mb * 2 + kk, troff, db);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[kk], dv[db], 0, 0, 0);
+          const bf16x8 qa = read_tr_operand<D>(Qt, mb * 2 + kk, troff, db);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf[kk], dk[db], 0, 0, 0);
+        }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  if (!wave_live || kw0 + ln >= p.S) return;
+  __bf16* krow = p.dK + (kv_row0 + kw0 + ln) * D;
+  __bf16* vrow = p.dV + (kv_row0 + kw0 + ln) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d0 = db * 32 + a4 * 8 + hl * 4;
+      u32x2 sk, sv;
+      sk[0] = pack_bf16x2(dk[db][a4 * 4 + 0] * p.scale, dk[db][a4 * 4 + 1] * p.scale);
+      sk[1] = pack_bf16x2(dk[db][a4 * 4 + 2] * p.scale, dk[db][a4 * 4 + 3] * p.scale);
+      sv[0] = pack_bf16x2(dv[db][a4 * 4 + 0], dv[db][a4 * 4 + 1]);
+      sv[1] = pack_bf16x2(dv[db][a4 * 4 + 2], dv[db][a4 * 4 + 3]);
+      *reinterpret_cast<u32x2*>(krow + d0) = sk;
+      *reinterpret_cast<u32x2*>(vrow + d0) = sv;
+    }
+}
+
+template <int D>
+hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
+  constexpr int NWQ = 8;  // dQ waves per workgroup
+  constexpr int NWK = 4;                 // dK/dV waves per workgroup (one per SIMD)
+  if ((long long)p.S * D * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
+  p.hp = (p.G % 4 == 0 && NWQ % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+  p.n_hsub = p.G / p.hp;
+  p.qspan = (NWQ / p.hp) * 32;
+  p.n_qtiles = (p.S + p.qspan - 1) / p.qspan;
+  const long long nq = (long long)p.n_qtiles * p.B * p.Nkv * p.n_hsub;
+  const long long nk = (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
+  if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)nq), dim3(NWQ * 64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_bf16_supported(int Dh) { return Dh == 64 || Dh == 128; }
+
+hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
+                                float scale, void* ws, hipStream_t stream) {
+  hipError_t e = launch_backward_delta(O, dO, static_cast<float*>(ws), (long long)B * Nq * S, Dh,
+                                       1, stream);
+  if (e != hipSuccess) return e;
+  BwdMfmaParams p;
+  p.Q = static_cast<const __bf16*>(Q);
+  p.K = static_cast<const __bf16*>(K);
+  p.V = static_cast<const __bf16*>(V);
+  p.dO = static_cast<const __bf16*>(dO);
+  p.LSE = LSE;
+  p.delta = static_cast<const float*>(ws);
+  p.dQ = static_cast<__bf16*>(dQ);
+  p.dK = static_cast<__bf16*>(dK);
+  p.dV = static_cast<__bf16*>(dV);
+  p.B = B;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.S = S;
+  p.causal = causal;
+  p.window = window;
+  p.c = scale * kLog2e;
+  p.scale = scale;
+  p.G = Nq / Nkv;
+  switch (Dh) {
+    case 64: return launch_bwd<64>(p, stream);
+    case 128: return launch_bwd<128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

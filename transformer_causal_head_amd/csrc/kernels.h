@@ -50,5 +50,14 @@ hipError_t launch_backward_general(const void* Q, const void* K, const void* V, 
                                    const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                    int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
                                    float scale, void* ws, int is_bf16, hipStream_t stream);
+// Delta_i = dO_i . O_i for `rows` rows of Dh elements
+hipError_t launch_backward_delta(const void* O, const void* dO, float* delta, long long rows, int Dh,
+                                 int is_bf16, hipStream_t stream);
+// bf16 MFMA backward (Dh 64 or 128): Delta, then the dQ and dK/dV kernels
+bool backward_bf16_supported(int Dh);
+hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
+                                float scale, void* ws, hipStream_t stream);
 
 }  // namespace attn
