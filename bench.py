@@ -230,6 +230,37 @@ def _head_sizes(torch, dev, tch, steps, warmup):
         del tq, tk, tv, O, L, ws
 
 
+def _backward(torch, dev, tch, steps, warmup):
+    """One JSON line per shape: attn_backward (dQ, dK, dV from O, LSE and dO) on the prefill
+    workload and on GQA / head-size-64 variants.  Algorithmic FLOPs are 2.5 times the
+    forward's: five products per visible pair (S = Q K^T, dP = dO V^T, dV, dK, dQ); the
+    kernels recompute S and dP once more (seven products), which is not counted."""
+    for B, Nq, Nkv, S, Dh in ((1, 32, 32, 32768, 128), (1, 32, 8, 32768, 128),
+                              (1, 32, 32, 32768, 64)):
+        q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
+        tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+        del q, k, v
+        tdo = torch.randn_like(tq)
+        O = torch.empty_like(tq)
+        L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(Dh)
+        tch.attn_prefill(tq, tk, tv, O, L, causal=1, scale=scale)
+        dQ, dK, dV = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+        ws = torch.empty(tch.attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, tch.ATTN_BF16),
+                         dtype=torch.uint8, device=dev)
+        ms = _time(torch, lambda: tch.attn_backward(tq, tk, tv, O, tdo, L, dQ, dK, dV,
+                                                    causal=1, scale=scale, workspace=ws),
+                   steps, warmup)
+        fwd, _ = workloads.prefill_work(B, Nq, Nkv, S, Dh, True, 0, 2)
+        flop = int(2.5 * fwd)
+        tf = flop / (ms * 1e-3) / 1e12
+        print(json.dumps({"path": "attn_backward", "workload": f"B={B} Nq={Nq} Nkv={Nkv} "
+                          f"S={S} Dh={Dh} bf16 causal", "ms": round(ms, 4),
+                          "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "algorithmic_flop": flop}), flush=True)
+        del tq, tk, tv, tdo, O, L, dQ, dK, dV, ws
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +277,8 @@ def main():
     ap.add_argument("--cache-paths", action="store_true",
                     help="time the cache-side entry points (chunked prefill, windowed and "
                          "rolling-buffer decode, append) instead of the main step")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV) instead of the main step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -272,6 +305,9 @@ def main():
         return
     if args.head_sizes:
         _head_sizes(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
+        return
+    if args.backward:
+        _backward(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
 
     pc = workloads.WORKLOADS[PREFILL]

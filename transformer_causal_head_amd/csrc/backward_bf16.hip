@@ -231,6 +231,9 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
   __shared__ __attribute__((aligned(1024))) char q1s[geo::TILE];
   __shared__ __attribute__((aligned(1024))) char o0s[geo::TILE];
   __shared__ __attribute__((aligned(1024))) char o1s[geo::TILE];
+  // LSE and Delta of the tile's 64 query rows, next to the Q / dO tile
+  __shared__ __attribute__((aligned(256))) float a0s[2 * BN];
+  __shared__ __attribute__((aligned(256))) float a1s[2 * BN];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,20 +261,24 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
   const int n_qt = (qhi + BN - 1) / BN - t_lo;  // query tiles per head
   const int n_items = p.G * max(n_qt, 0);
 
-  auto head_refs = [&](int item, HeadRef& hq, HeadRef& ho, int& q0) {
+  // copies of item `item` (query head hh of the group, query tile q0): the Q
+  // and dO tiles, and 64 LSE (wave 0) and 64 Delta (wave 1) values, which
+  // read as zero past the last row like the tile rows
+  auto issue = [&](int item, char* qdst, char* odst, float* adst) {
     const int hh = item / n_qt;
-    q0 = (t_lo + item % n_qt) * BN;
-    const size_t base = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S * D;
-    hq = head_ref<D>(p.Q + base, p.S);
-    ho = head_ref<D>(p.dO + base, p.S);
+    const int q0 = (t_lo + item % n_qt) * BN;
+    const size_t row0 = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S;
+    load_tile<D, NW>(head_ref<D>(p.Q + row0 * D, p.S), q0, qdst, w, lane);
+    load_tile<D, NW>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, w, lane);
+    if (w < 2) {
+      const float* src = (w == 0 ? p.LSE : p.delta) + row0;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.S * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(adst + w * BN), 4, (q0 + lane) * 4,
+                                               0, 0, 0);
+    }
   };
-  if (n_items > 0) {
-    HeadRef hq, ho;
-    int q0;
-    head_refs(0, hq, ho, q0);
-    load_tile<D, NW>(hq, q0, q0s, w, lane);
-    load_tile<D, NW>(ho, q0, o0s, w, lane);
-  }
+  if (n_items > 0) issue(0, q0s, o0s, a0s);
 
   // K and V as B operands: key column ln, head dims 16*ks + 8*hl + i
   const int kj = min(kw0 + ln, p.S - 1);
@@ -299,19 +306,14 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
   }
 
   for (int it = 0; it < n_items; ++it) {
-    const int hh = it / n_qt;
     const int q0 = (t_lo + it % n_qt) * BN;
     const char* Qt = (it & 1) ? q1s : q0s;
     const char* Ot = (it & 1) ? o1s : o0s;
+    const float* At = (it & 1) ? a1s : a0s;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (it + 1 < n_items) {
-      HeadRef hq, ho;
-      int qn;
-      head_refs(it + 1, hq, ho, qn);
-      load_tile<D, NW>(hq, qn, (it & 1) ? q0s : q1s, w, lane);
-      load_tile<D, NW>(ho, qn, (it & 1) ? o0s : o1s, w, lane);
-    }
+    if (it + 1 < n_items)
+      issue(it + 1, (it & 1) ? q0s : q1s, (it & 1) ? o0s : o1s, (it & 1) ? a0s : a1s);
     // does this wave see any (query, key) pair of the tile?  all of them?
     bool live = wave_live && q0 < p.S;
     if (p.causal) live = live && q0 + BN - 1 >= kw0;
@@ -321,7 +323,6 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     if (p.causal) full = full && q0 >= kw1 - 1;
     if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
 
-    const size_t qrow0 = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -335,15 +336,18 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
       }
-      // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln.
-      // LSE and Delta of those query rows (clamped at the last row; rows past
-      // S are masked below)
+      // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln;
+      // the LSE and Delta of those rows are 4 consecutive floats per r/4
       float lse2[16], dlt[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = min(q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3), p.S - 1);
-        lse2[r] = p.LSE[qrow0 + q] * kLog2e;
-        dlt[r] = p.delta[qrow0 + q];
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          lse2[a * 4 + u] = l4[u] * kLog2e;
+          dlt[a * 4 + u] = d4[u];
+        }
       }
       if (!full) {
 #pragma unroll
