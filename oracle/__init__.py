@@ -1,5 +1,6 @@
 """Float64 CPU oracle of causal scaled dot-product attention (prefill, chunked
-prefill against a cache, decode, cache append, and the backward pass).
+prefill against a cache, decode, cache append, the backward pass, rotary
+position embedding and key-padding masks).
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the package's smoke
 check and the benchmark's CPU-baseline leg, never by the GPU library.  It is
@@ -21,10 +22,12 @@ from .attention import (
     softmax_rows,
     softmax_vjp,
 )
+from .rope import append_rope_ref, rope_angles, rope_ref, rope_table_ref
 
 __all__ = [
     "allowed_mask",
     "append_ref",
+    "append_rope_ref",
     "attention_ref",
     "attention_rows_ref",
     "backward_ref",
@@ -32,6 +35,9 @@ __all__ = [
     "decode_ref",
     "head_attention",
     "kv_head_of",
+    "rope_angles",
+    "rope_ref",
+    "rope_table_ref",
     "softmax_rows",
     "softmax_vjp",
 ]

@@ -45,6 +45,14 @@ Readings taken where the pages leave a choice open:
     with the new token appended first, the buffer holds exactly the W
     positions a window of W admits, in rotated order, which the softmax does
     not see;
+  * a key-padding mask (textbook, "Паддинг" under "Прямой проход по шагам":
+    the padding's key mask is added to the causal mask and the window, one
+    mask per batch row) hides key j of sequence b wherever key_mask[b, j] is
+    false, on top of the causal mask and the window; a hidden key's weight
+    is exactly 0, so its K and V must hold finite values (0 * NaN is NaN);
+  * a query row that sees no key at all (possible only with a key-padding
+    mask, e.g. a left-pad query) gets O = 0 and LSE = -inf: an empty weighted
+    sum, where the textbook's masked_fill followed by softmax would give NaN;
   * the backward pass differentiates the same definition: the softmax
     Jacobian is dp_i/dz_j = p_i (delta_ij - p_j) (textbook, "Почему делить
     на корень из d_h"), the rest is the chain rule through the two products;
@@ -109,23 +117,31 @@ def softmax_rows(A):
 
 
 def head_attention(q_rows, row_positions, K, V, causal, window, scale,
-                   return_probs=False):
+                   return_probs=False, key_ok=None):
     """Attention of some query rows of one head against one K/V head.
 
     q_rows: [R, Dh] float64, row_positions: [R] absolute query positions,
-    K, V: [T_kv, Dh].  Returns (O [R, Dh], LSE [R]) and, if asked, P [R, T_kv].
-    Steps follow the textbook's formula softmax(QK^T / sqrt(d_h) + M) V
-    (section "Scaled dot-product attention") with the scale passed in.
+    K, V: [T_kv, Dh], key_ok: optional [T_kv] booleans (False: padding key).
+    Returns (O [R, Dh], LSE [R]) and, if asked, P [R, T_kv].  Steps follow the
+    textbook's formula softmax(QK^T / sqrt(d_h) + M) V (section "Scaled
+    dot-product attention") with the scale passed in.  A row with no visible
+    key gets O = 0, LSE = -inf (and P = 0).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     A = scale * (q_rows @ K.T)
     ok = allowed_mask(row_positions, K.shape[0], causal, window)
+    if key_ok is not None:
+        ok &= np.asarray(key_ok, dtype=bool)[None, :]
+    seen = ok.any(axis=1)
     A = np.where(ok, A, -np.inf)
+    A[~seen] = 0.0  # placeholder, overwritten below
     P, m, l = softmax_rows(A)
+    P[~seen] = 0.0
     O = P @ V
     LSE = m + np.log(l)
+    LSE[~seen] = -np.inf
     if return_probs:
         return O, LSE, P
     return O, LSE
@@ -140,11 +156,12 @@ def _check_prefill_shapes(Q, K, V):
     return B, Nq, K.shape[1], S, Dh
 
 
-def attention_ref(Q, K, V, causal=True, window=0, scale=None):
+def attention_ref(Q, K, V, causal=True, window=0, scale=None, key_mask=None):
     """Full prefill attention.  Q: [B,Nq,S,Dh], K,V: [B,Nkv,S,Dh].
 
     Returns O [B,Nq,S,Dh] and LSE [B,Nq,S], both float64.  ``scale`` defaults
     to 1/sqrt(Dh), the head size (textbook, "Почему делить на корень из d_h").
+    ``key_mask``: optional [B, S] booleans, False for padding keys.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -158,8 +175,9 @@ def attention_ref(Q, K, V, causal=True, window=0, scale=None):
     for b in range(B):
         for h in range(Nq):
             g = kv_head_of(h, Nq, Nkv)
-            O[b, h], LSE[b, h] = head_attention(Q[b, h], rows, K[b, g], V[b, g],
-                                                causal, window, scale)
+            O[b, h], LSE[b, h] = head_attention(
+                Q[b, h], rows, K[b, g], V[b, g], causal, window, scale,
+                key_ok=None if key_mask is None else key_mask[b])
     return O, LSE
 
 
@@ -185,7 +203,7 @@ def attention_rows_ref(Q, K, V, triples, causal=True, window=0, scale=None):
     return O, LSE
 
 
-def decode_ref(q, Kc, Vc, lens, scale=None, rows=None, window=0):
+def decode_ref(q, Kc, Vc, lens, scale=None, rows=None, window=0, key_mask=None):
     """One decode step against a KV cache.
 
     q: [B,Nq,Dh], Kc, Vc: [B,Nkv,Tcap,Dh], lens: [B] with 1 <= lens[b] <= Tcap.
@@ -195,6 +213,8 @@ def decode_ref(q, Kc, Vc, lens, scale=None, rows=None, window=0):
     With ``window`` > 0 only the keys lens[b]-window .. lens[b]-1 are visible
     (section "Скользящее окно", in the i - j < window convention).
     Entries past lens[b] are never read.  ``scale`` defaults to 1/sqrt(Dh).
+    ``key_mask``: optional [B, Tcap] booleans over the cache slots, False for
+    padding keys.
     ``rows`` optionally restricts the work to (b, h) pairs; then O is
     [len(rows), Dh] and LSE [len(rows)].  Otherwise O [B,Nq,Dh], LSE [B,Nq].
     """
@@ -213,14 +233,15 @@ def decode_ref(q, Kc, Vc, lens, scale=None, rows=None, window=0):
         qrow = np.asarray(q[b, h], dtype=np.float64)[None, :]
         Kb = np.asarray(Kc[b, g, :n], dtype=np.float64)
         Vb = np.asarray(Vc[b, g, :n], dtype=np.float64)
-        o, lse = head_attention(qrow, [n - 1], Kb, Vb, True, window, scale)
+        o, lse = head_attention(qrow, [n - 1], Kb, Vb, True, window, scale,
+                                key_ok=None if key_mask is None else key_mask[b][:n])
         O[t], LSE[t] = o[0], lse[0]
     if rows is None:
         return O.reshape(B, Nq, Dh), LSE.reshape(B, Nq)
     return O, LSE
 
 
-def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None):
+def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None, key_mask=None):
     """Chunked prefill: Sq new queries per sequence against a KV cache.
 
     Q: [B,Nq,Sq,Dh]; Kc, Vc: [B,Nkv,Tcap,Dh] already holding the chunk's own
@@ -233,6 +254,8 @@ def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None):
     start at the first new position, not at 0.
     ``rows`` optionally restricts the work to (b, h, i) triples; then O is
     [len(rows), Dh] and LSE [len(rows)].  Otherwise O [B,Nq,Sq,Dh], LSE [B,Nq,Sq].
+    ``key_mask``: optional [B, Tcap] booleans over the cache slots, False for
+    padding keys.
     """
     B, Nq, Sq, Dh = Q.shape
     Nkv = Kc.shape[1]
@@ -249,7 +272,8 @@ def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None):
             g = kv_head_of(h, Nq, Nkv)
             qrow = np.asarray(Q[b, h, i], dtype=np.float64)[None, :]
             o, lse = head_attention(qrow, [n - Sq + i], np.asarray(Kc[b, g, :n], dtype=np.float64),
-                                    np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale)
+                                    np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale,
+                                    key_ok=None if key_mask is None else key_mask[b][:n])
             O[t], LSE[t] = o[0], lse[0]
         return O, LSE
     O = np.empty((B, Nq, Sq, Dh))
@@ -262,7 +286,8 @@ def chunk_ref(Q, Kc, Vc, lens, window=0, scale=None, rows=None):
             O[b, h], LSE[b, h] = head_attention(
                 np.asarray(Q[b, h], dtype=np.float64), positions,
                 np.asarray(Kc[b, g, :n], dtype=np.float64),
-                np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale)
+                np.asarray(Vc[b, g, :n], dtype=np.float64), True, window, scale,
+                key_ok=None if key_mask is None else key_mask[b][:n])
     return O, LSE
 
 
