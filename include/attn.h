@@ -4,8 +4,8 @@
  * Computes causal scaled dot-product multi-head attention
  *     O = softmax(Q K^T * scale + M) V        per (batch, query head)
  * with the grouped-query K/V head map, an optional sliding window, the
- * KV-cache decode step, chunked prefill against a cache, and the cache
- * append.  The operation is the one defined in the attention chapter of the
+ * KV-cache decode step, chunked prefill against a cache, the cache append,
+ * key-padding masks, rotary position embedding and the backward pass.  The operation is the one defined in the attention chapter of the
  * LLM-architecture textbook ("Механизм внимания", sections "Scaled
  * dot-product attention", "Маскирование", "Виды по числу голов K/V",
  * "Скользящее окно", "KV-кэш", "Prefill и decode" and "Прямой проход по
@@ -224,6 +224,93 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int Nq, int Nkv, int S, int Dh,
                   int causal, int window, float scale,
                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * Key-padding masks (textbook, "Паддинг" under "Прямой проход по шагам": the
+ * padding's key mask is added to the causal mask and the window, one mask per
+ * batch row).  The attention entry points below take the mask as BITS: for a
+ * sequence of T keys (T = S for a prefill, Tcap for a cache) its row holds
+ * ceil(T / 64) uint64 words, and bit j % 64 of word j / 64 is key j's flag
+ * (1 = real token, 0 = padding).  A hidden key gets weight exactly 0, so its
+ * K and V must still hold finite values.  A query row that sees no key at all
+ * (a left-padding query, say) gets O = 0 and LSE = -inf.
+ *
+ * attn_pack_key_mask -- bytes -> bits.
+ *   mask      [B, T] uint8, DEVICE   nonzero = real token
+ *   key_bits  [B, ceil(T / 64)] uint64, DEVICE, written
+ * Errors: ATTN_EINVAL, ATTN_EHIP.
+ */
+int attn_pack_key_mask(const uint8_t* mask, int B, int T, uint64_t* key_bits, void* stream);
+
+/*
+ * attn_prefill_padded / attn_prefill_cache_padded / attn_decode_padded --
+ * attn_prefill, attn_prefill_cache and attn_decode_window with a key-padding
+ * mask, key_bits [B, ceil(S / 64)] (prefill) or [B, ceil(Tcap / 64)] (the
+ * cache forms, indexed by cache row), DEVICE.  key_bits == NULL is the
+ * unmasked call.  Every other argument, the workspace size and the errors
+ * are those of the unpadded entry point.
+ */
+int attn_prefill_padded(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                        void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh,
+                        int causal, int window, float scale, int dtype, void* stream);
+int attn_prefill_cache_padded(const void* Q, const void* Kcache, const void* Vcache,
+                              const int32_t* lens, const uint64_t* key_bits, void* O, float* LSE,
+                              int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
+                              float scale, int dtype, void* stream);
+int attn_decode_padded(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, const uint64_t* key_bits, void* O,
+                       int B, int Nq, int Nkv, int Dh, int Tcap, int window, float scale,
+                       float* LSE, void* workspace, size_t workspace_bytes,
+                       int dtype, void* stream);
+
+/*
+ * Rotary position embedding, RoPE (textbook, "Как в attention попадает
+ * позиция": q and k are rotated by a position-dependent angle so that
+ * q_i . k_j depends only on i - j, V is not; step 4 of "Прямой проход по
+ * шагам": with padding the rotation takes explicit positions; the layer-cache
+ * section: K enters the cache already rotated).  The formula is RoFormer's,
+ * which the page cites: pair m is turned by p * theta_m, theta_m =
+ * base^(-2m/Dh), (a, b) -> (a cos - b sin, a sin + b cos).
+ *
+ * attn_rope_cos_sin -- build the angle table.
+ *   table [P, Dh] fp32, DEVICE, written: column m holds cos(p theta_m),
+ *         column Dh/2 + m holds sin(p theta_m), for positions p = 0 .. P-1
+ *   base  > 1 (10000 in RoFormer and LLaMA); Dh even
+ * Computed in double precision and rounded once to fp32.
+ * Errors: ATTN_EINVAL, ATTN_EHIP.
+ */
+int attn_rope_cos_sin(float* table, int P, int Dh, double base, void* stream);
+
+/*
+ * attn_rope -- rotate X [B, H, S, Dh] into Y (Y == X allowed: in place).
+ *   positions [B, S] int32, DEVICE, or NULL: token (b, s) is at positions[b, s]
+ *   start     [B] int32, DEVICE, or NULL: with positions NULL, token (b, s) is
+ *             at start[b] + s (the first new token's position), or at s
+ *   table     from attn_rope_cos_sin with this Dh; positions are clamped to
+ *             [0, P - 1]
+ *   style     0: pairs (x[2m], x[2m+1]) (RoFormer);
+ *             1: halves (x[m], x[m + Dh/2]) (GPT-NeoX, LLaMA in the Hugging
+ *             Face layout)
+ *   dtype     of X and Y; the rotation is computed in fp32
+ * Errors: ATTN_EINVAL (also odd Dh, bad style), ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_rope(const void* X, void* Y, const int32_t* positions, const int32_t* start,
+              const float* table, int P, int B, int H, int S, int Dh, int style, int dtype,
+              void* stream);
+
+/*
+ * attn_kv_append_rope -- attn_kv_append with the new keys rotated on their
+ * way into the cache (one pass over the new rows): key row i of sequence b is
+ * rotated at positions[b, i] ([B, Snew] int32, DEVICE) or, with positions
+ * NULL, at pos[b] + i, then written where attn_kv_append writes it; V rows are
+ * copied unchanged.  table, P, style as for attn_rope; the rest as for
+ * attn_kv_append.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_kv_append_rope(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
+                        const int32_t* pos, const int32_t* positions, const float* table, int P,
+                        int B, int Nkv, int Snew, int Dh, int Tcap, int rolling, int style,
+                        int dtype, void* stream);
 
 /* attn_strerror -- static description of an attn_status value. */
 const char* attn_strerror(int status);

@@ -245,3 +245,109 @@ def test_backward_rejects(kw, code):
 def test_backward_workspace_query():
     assert tch.attn_backward_workspace_bytes(2, 8, 2, 100, 128, tch.ATTN_BF16) == 2 * 8 * 100 * 4
     assert tch.attn_backward_workspace_bytes(2, 8, 3, 100, 128, tch.ATTN_BF16) == 0
+
+
+@no_gpu
+@pytest.mark.parametrize("args,code", [
+    ((None, 2, 100, FAKE, None), tch.ATTN_EINVAL),
+    ((FAKE, 0, 100, FAKE, None), tch.ATTN_EINVAL),
+    ((FAKE, 2, 0, FAKE, None), tch.ATTN_EINVAL),
+    ((FAKE, 2, 100, None, None), tch.ATTN_EINVAL),
+])
+def test_pack_key_mask_rejects(args, code):
+    assert tch.lib().attn_pack_key_mask(*args) == code
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nkv=3), tch.ATTN_EGQA),
+    (dict(causal=0, window=4), tch.ATTN_EINVAL),
+    (dict(Dh=300), tch.ATTN_EUNSUPPORTED),
+    (dict(Q=None), tch.ATTN_EINVAL),
+    (dict(scale=0.0), tch.ATTN_EINVAL),
+])
+def test_padded_entry_points_reject(kw, code):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, B=1, Nq=4, Nkv=2, S=16, Dh=128, causal=1, window=0,
+             scale=0.125)
+    a.update(kw)
+    L = tch.lib()
+    assert L.attn_prefill_padded(a["Q"], a["K"], a["V"], FAKE, a["O"], None, a["B"], a["Nq"],
+                                 a["Nkv"], a["S"], a["Dh"], a["causal"], a["window"], a["scale"],
+                                 tch.ATTN_BF16, None) == code
+    if "causal" in kw:
+        return  # the cache forms are causal by construction
+    assert L.attn_prefill_cache_padded(a["Q"], a["K"], a["V"], FAKE, FAKE, a["O"], None, a["B"],
+                                       a["Nq"], a["Nkv"], 4, a["Dh"], a["S"], 0, a["scale"],
+                                       tch.ATTN_BF16, None) == code
+    assert L.attn_decode_padded(a["Q"], a["K"], a["V"], FAKE, FAKE, a["O"], a["B"], a["Nq"],
+                                a["Nkv"], a["Dh"], a["S"], 0, a["scale"], None, FAKE, 1 << 30,
+                                tch.ATTN_BF16, None) == code
+
+
+@no_gpu
+def test_padded_cache_forms_check_chunk_and_workspace():
+    L = tch.lib()
+    # a chunk longer than the cache
+    assert L.attn_prefill_cache_padded(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 32, 128,
+                                       16, 0, 0.125, tch.ATTN_BF16, None) == tch.ATTN_EINVAL
+    # the split-K decode needs its workspace
+    assert L.attn_decode_padded(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 128, 4096, 0, 0.1,
+                                None, None, 0, tch.ATTN_BF16, None) == tch.ATTN_EWORKSPACE
+
+
+@no_gpu
+@pytest.mark.parametrize("args,code", [
+    ((None, 16, 64, 10000.0, None), tch.ATTN_EINVAL),
+    ((FAKE, 0, 64, 10000.0, None), tch.ATTN_EINVAL),
+    ((FAKE, 16, 63, 10000.0, None), tch.ATTN_EINVAL),
+    ((FAKE, 16, 64, 1.0, None), tch.ATTN_EINVAL),
+    ((FAKE, 16, 64, float("inf"), None), tch.ATTN_EINVAL),
+])
+def test_rope_table_rejects(args, code):
+    assert tch.lib().attn_rope_cos_sin(*args) == code
+
+
+def _rope(**kw):
+    a = dict(X=FAKE, Y=FAKE, positions=None, start=None, table=FAKE, P=64, B=1, H=4, S=16, Dh=128,
+             style=0, dtype=tch.ATTN_BF16)
+    a.update(kw)
+    return tch.lib().attn_rope(a["X"], a["Y"], a["positions"], a["start"], a["table"], a["P"],
+                               a["B"], a["H"], a["S"], a["Dh"], a["style"], a["dtype"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), tch.ATTN_EINVAL),
+    (dict(table=None), tch.ATTN_EINVAL),
+    (dict(Dh=127), tch.ATTN_EINVAL),
+    (dict(style=2), tch.ATTN_EINVAL),
+    (dict(P=0), tch.ATTN_EINVAL),
+    (dict(S=0), tch.ATTN_EINVAL),
+    (dict(dtype=7), tch.ATTN_EUNSUPPORTED),
+])
+def test_rope_rejects(kw, code):
+    assert _rope(**kw) == code
+
+
+def _append_rope(**kw):
+    a = dict(Kn=FAKE, Vn=FAKE, Kc=FAKE, Vc=FAKE, pos=FAKE, positions=None, table=FAKE, P=64, B=2,
+             Nkv=2, Snew=3, Dh=128, Tcap=16, rolling=0, style=0, dtype=tch.ATTN_BF16)
+    a.update(kw)
+    return tch.lib().attn_kv_append_rope(a["Kn"], a["Vn"], a["Kc"], a["Vc"], a["pos"],
+                                         a["positions"], a["table"], a["P"], a["B"], a["Nkv"],
+                                         a["Snew"], a["Dh"], a["Tcap"], a["rolling"], a["style"],
+                                         a["dtype"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(pos=None), tch.ATTN_EINVAL),
+    (dict(table=None), tch.ATTN_EINVAL),
+    (dict(Snew=20), tch.ATTN_EINVAL),
+    (dict(Dh=7), tch.ATTN_EINVAL),
+    (dict(style=-1), tch.ATTN_EINVAL),
+    (dict(rolling=2), tch.ATTN_EINVAL),
+    (dict(dtype=3), tch.ATTN_EUNSUPPORTED),
+])
+def test_kv_append_rope_rejects(kw, code):
+    assert _append_rope(**kw) == code

@@ -17,12 +17,26 @@ Entry points (same names as the C ABI):
     attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
                   workspace=None, stream=None)
     attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype)
+    attn_pack_key_mask(mask, key_bits, stream=None)
+    attn_prefill_padded(Q, K, V, key_bits, O, LSE, causal=1, window=0, scale=None, stream=None)
+    attn_prefill_cache_padded(Q, Kcache, Vcache, lens, key_bits, O, LSE, window=0, scale=None,
+                              stream=None)
+    attn_decode_padded(q, Kcache, Vcache, lens, key_bits, O, LSE=None, workspace=None,
+                       window=0, scale=None, stream=None)
+    attn_rope_cos_sin(table, base=10000.0, stream=None)
+    attn_rope(X, Y, table, positions=None, start=None, style=0, stream=None)
+    attn_kv_append_rope(Knew, Vnew, Kcache, Vcache, pos, table, positions=None, rolling=0,
+                        style=0, stream=None)
     attn_strerror(status)
+Key bits are held in int64 tensors [B, ceil(T / 64)] (the C ABI's uint64 words).
 Conveniences that allocate outputs with torch:
-    prefill(q, k, v, causal=True, window=0, scale=None) -> (O, LSE)
-    prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
-    decode(q, Kcache, Vcache, lens, window=0, scale=None) -> (O, LSE)
+    prefill(q, k, v, causal=True, window=0, scale=None, key_mask=None) -> (O, LSE)
+    prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None, key_mask=None) -> (O, LSE)
+    decode(q, Kcache, Vcache, lens, window=0, scale=None, key_mask=None) -> (O, LSE)
     backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None) -> (dQ, dK, dV)
+    pack_key_mask(mask) -> key_bits          (mask: bool or uint8 [B, T])
+    rope_table(P, Dh, base=10000.0, device=None) -> table [P, Dh] fp32
+    rope(x, table, positions=None, start=None, style="pairs", out=None) -> rotated x
 """
 
 import ctypes
@@ -44,7 +58,10 @@ ATTN_F32 = 1
 EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
            "attn_decode_workspace_bytes", "attn_decode_window_workspace_bytes",
            "attn_kv_append", "attn_backward", "attn_backward_workspace_bytes",
+           "attn_pack_key_mask", "attn_prefill_padded", "attn_prefill_cache_padded",
+           "attn_decode_padded", "attn_rope_cos_sin", "attn_rope", "attn_kv_append_rope",
            "attn_strerror")
+ROPE_STYLES = {"pairs": 0, "half": 1}
 
 _lib = None
 
@@ -88,6 +105,24 @@ def lib():
         L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     i32, i32, f32, vp, ctypes.c_size_t, i32, vp]
         L.attn_backward.restype = i32
+        L.attn_pack_key_mask.argtypes = [vp, i32, i32, vp, vp]
+        L.attn_pack_key_mask.restype = i32
+        L.attn_prefill_padded.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, f32, i32, vp]
+        L.attn_prefill_padded.restype = i32
+        L.attn_prefill_cache_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                i32, i32, i32, f32, i32, vp]
+        L.attn_prefill_cache_padded.restype = i32
+        L.attn_decode_padded.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                         vp, vp, ctypes.c_size_t, i32, vp]
+        L.attn_decode_padded.restype = i32
+        L.attn_rope_cos_sin.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+        L.attn_rope_cos_sin.restype = i32
+        L.attn_rope.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        L.attn_rope.restype = i32
+        L.attn_kv_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, vp]
+        L.attn_kv_append_rope.restype = i32
         L.attn_strerror.argtypes = [i32]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -124,8 +159,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None):
-    """Q [B,Nq,S,Dh], K/V [B,Nkv,S,Dh], O like Q, LSE fp32 [B,Nq,S] or None."""
+def _check_bits(key_bits, B, T):
+    import torch
+    if key_bits is None:
+        return
+    if key_bits.dtype != torch.int64 or tuple(key_bits.shape) != (B, (T + 63) // 64):
+        raise ValueError(f"key_bits must be int64 [B, ceil({T} / 64)]")
+
+
+def _check_prefill(Q, K, V, O, LSE):
     B, Nq, S, Dh = Q.shape
     Nkv = K.shape[1]
     if tuple(K.shape) != (B, Nkv, S, Dh) or K.shape != V.shape or O.shape != Q.shape:
@@ -134,6 +176,12 @@ def attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None):
         raise ValueError("Q, K, V, O must share one dtype")
     if LSE is not None and (tuple(LSE.shape) != (B, Nq, S) or LSE.dtype.itemsize != 4):
         raise ValueError("LSE must be fp32 [B, Nq, S]")
+    return B, Nq, Nkv, S, Dh
+
+
+def attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None):
+    """Q [B,Nq,S,Dh], K/V [B,Nkv,S,Dh], O like Q, LSE fp32 [B,Nq,S] or None."""
+    B, Nq, Nkv, S, Dh = _check_prefill(Q, K, V, O, LSE)
     if scale is None:
         scale = 1.0 / math.sqrt(Dh)
     st = lib().attn_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, Nq, Nkv, S, Dh,
@@ -141,6 +189,19 @@ def attn_prefill(Q, K, V, O, LSE, causal=1, window=0, scale=None, stream=None):
                             _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_prefill")
+
+
+def attn_prefill_padded(Q, K, V, key_bits, O, LSE, causal=1, window=0, scale=None, stream=None):
+    """attn_prefill with a key-padding mask: key_bits int64 [B, ceil(S/64)] on the GPU."""
+    B, Nq, Nkv, S, Dh = _check_prefill(Q, K, V, O, LSE)
+    _check_bits(key_bits, B, S)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    st = lib().attn_prefill_padded(_ptr(Q), _ptr(K), _ptr(V), _ptr(key_bits), _ptr(O), _ptr(LSE),
+                                   B, Nq, Nkv, S, Dh, int(causal), int(window), float(scale),
+                                   _dtype_code(Q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill_padded")
 
 
 def attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype):
@@ -189,8 +250,10 @@ def attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, win
         raise AttnError(st, "attn_decode_window")
 
 
-def attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, stream=None):
-    """Q [B,Nq,Sq,Dh] against caches [B,Nkv,Tcap,Dh]; lens int32 [B] on the GPU."""
+def attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, stream=None,
+                       key_bits=None):
+    """Q [B,Nq,Sq,Dh] against caches [B,Nkv,Tcap,Dh]; lens int32 [B] on the GPU.
+    With key_bits (int64 [B, ceil(Tcap/64)]) it calls attn_prefill_cache_padded."""
     import torch
     B, Nq, Sq, Dh = Q.shape
     Nkv, Tcap = Kcache.shape[1], Kcache.shape[2]
@@ -204,11 +267,120 @@ def attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, st
         raise ValueError("LSE must be fp32 [B, Nq, Sq]")
     if scale is None:
         scale = 1.0 / math.sqrt(Dh)
-    st = lib().attn_prefill_cache(_ptr(Q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O),
-                                  _ptr(LSE), B, Nq, Nkv, Sq, Dh, Tcap, int(window), float(scale),
-                                  _dtype_code(Q), _stream(stream))
+    if key_bits is None:
+        st = lib().attn_prefill_cache(_ptr(Q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O),
+                                      _ptr(LSE), B, Nq, Nkv, Sq, Dh, Tcap, int(window),
+                                      float(scale), _dtype_code(Q), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_prefill_cache")
+        return
+    _check_bits(key_bits, B, Tcap)
+    st = lib().attn_prefill_cache_padded(_ptr(Q), _ptr(Kcache), _ptr(Vcache), _ptr(lens),
+                                         _ptr(key_bits), _ptr(O), _ptr(LSE), B, Nq, Nkv, Sq, Dh,
+                                         Tcap, int(window), float(scale), _dtype_code(Q),
+                                         _stream(stream))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_prefill_cache")
+        raise AttnError(st, "attn_prefill_cache_padded")
+
+
+def attn_prefill_cache_padded(Q, Kcache, Vcache, lens, key_bits, O, LSE, window=0, scale=None,
+                              stream=None):
+    """attn_prefill_cache with a key-padding mask over the cache rows."""
+    attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=window, scale=scale,
+                       stream=stream, key_bits=key_bits)
+
+
+def attn_decode_padded(q, Kcache, Vcache, lens, key_bits, O, LSE=None, workspace=None, window=0,
+                       scale=None, stream=None):
+    """attn_decode_window with a key-padding mask over the cache rows (key_bits int64
+    [B, ceil(Tcap/64)] on the GPU); same workspace as attn_decode_window."""
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
+    _check_bits(key_bits, B, Tcap)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_padded(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(lens),
+                                  _ptr(key_bits), _ptr(O), B, Nq, Nkv, Dh, Tcap, int(window),
+                                  float(scale), _ptr(LSE), _ptr(workspace), ws_bytes,
+                                  _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_padded")
+
+
+def attn_pack_key_mask(mask, key_bits, stream=None):
+    """mask bool or uint8 [B, T] (nonzero = real token) -> key_bits int64 [B, ceil(T/64)]."""
+    import torch
+    if mask.dtype not in (torch.bool, torch.uint8) or mask.dim() != 2:
+        raise ValueError("mask must be bool or uint8 [B, T]")
+    B, T = mask.shape
+    _check_bits(key_bits, B, T)
+    st = lib().attn_pack_key_mask(_ptr(mask), B, T, _ptr(key_bits), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_pack_key_mask")
+
+
+def attn_rope_cos_sin(table, base=10000.0, stream=None):
+    """Fill table fp32 [P, Dh]: cos(p theta_m) in column m, sin in column Dh/2 + m."""
+    import torch
+    if table.dtype != torch.float32 or table.dim() != 2:
+        raise ValueError("table must be fp32 [P, Dh]")
+    P, Dh = table.shape
+    st = lib().attn_rope_cos_sin(_ptr(table), P, Dh, float(base), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_rope_cos_sin")
+
+
+def _rope_style(style):
+    return ROPE_STYLES[style] if isinstance(style, str) else int(style)
+
+
+def _check_table(table, Dh):
+    import torch
+    if table.dtype != torch.float32 or table.dim() != 2 or table.shape[1] != Dh:
+        raise ValueError(f"table must be fp32 [P, {Dh}]")
+
+
+def attn_rope(X, Y, table, positions=None, start=None, style=0, stream=None):
+    """Rotate X [B,H,S,Dh] into Y (may be X) at positions (int32 [B,S]) or start (int32 [B])."""
+    import torch
+    B, H, S, Dh = X.shape
+    if Y.shape != X.shape or Y.dtype != X.dtype:
+        raise ValueError("Y must match X")
+    _check_table(table, Dh)
+    if positions is not None and (positions.dtype != torch.int32 or tuple(positions.shape) != (B, S)):
+        raise ValueError("positions must be int32 [B, S]")
+    if start is not None and (start.dtype != torch.int32 or tuple(start.shape) != (B,)):
+        raise ValueError("start must be int32 [B]")
+    st = lib().attn_rope(_ptr(X), _ptr(Y), _ptr(positions), _ptr(start), _ptr(table),
+                         table.shape[0], B, H, S, Dh, _rope_style(style), _dtype_code(X),
+                         _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_rope")
+
+
+def attn_kv_append_rope(Knew, Vnew, Kcache, Vcache, pos, table, positions=None, rolling=0,
+                        style=0, stream=None):
+    """attn_kv_append with the new keys rotated at positions (int32 [B,Snew]) or pos[b] + i."""
+    import torch
+    B, Nkv, Snew, Dh = Knew.shape
+    Tcap = Kcache.shape[2]
+    if Knew.shape != Vnew.shape or tuple(Kcache.shape) != (B, Nkv, Tcap, Dh) \
+            or Kcache.shape != Vcache.shape:
+        raise ValueError("new rows must be [B, Nkv, Snew, Dh] and caches [B, Nkv, Tcap, Dh]")
+    if not (Knew.dtype == Vnew.dtype == Kcache.dtype == Vcache.dtype):
+        raise ValueError("all four buffers must share one dtype")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be int32 [B]")
+    if positions is not None and (positions.dtype != torch.int32
+                                  or tuple(positions.shape) != (B, Snew)):
+        raise ValueError("positions must be int32 [B, Snew]")
+    _check_table(table, Dh)
+    st = lib().attn_kv_append_rope(_ptr(Knew), _ptr(Vnew), _ptr(Kcache), _ptr(Vcache), _ptr(pos),
+                                   _ptr(positions), _ptr(table), table.shape[0], B, Nkv, Snew,
+                                   Dh, Tcap, int(rolling), _rope_style(style), _dtype_code(Knew),
+                                   _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_kv_append_rope")
 
 
 def attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None):
@@ -272,27 +444,61 @@ def backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None):
     return dQ, dK, dV
 
 
-def prefill(q, k, v, causal=True, window=0, scale=None):
-    """Allocate O and LSE with torch and run attn_prefill on the current stream."""
+def pack_key_mask(mask):
+    """Key bits (int64 [B, ceil(T/64)]) of a bool / uint8 mask [B, T] on the GPU."""
+    import torch
+    B, T = mask.shape
+    bits = torch.empty((B, (T + 63) // 64), dtype=torch.int64, device=mask.device)
+    attn_pack_key_mask(mask.contiguous(), bits)
+    return bits
+
+
+def rope_table(P, Dh, base=10000.0, device=None):
+    """cos/sin table fp32 [P, Dh] for positions 0 .. P-1, built on the GPU."""
+    import torch
+    table = torch.empty((P, Dh), dtype=torch.float32, device=device or "cuda")
+    attn_rope_cos_sin(table, base)
+    return table
+
+
+def rope(x, table, positions=None, start=None, style="pairs", out=None):
+    """Rotated copy of x [B,H,S,Dh] (or rotate into `out`, which may be x itself)."""
+    import torch
+    y = torch.empty_like(x) if out is None else out
+    attn_rope(x, y, table, positions=positions, start=start, style=style)
+    return y
+
+
+def prefill(q, k, v, causal=True, window=0, scale=None, key_mask=None):
+    """Allocate O and LSE with torch and run attn_prefill (attn_prefill_padded with a
+    key_mask, bool / uint8 [B, S]) on the current stream."""
     import torch
     O = torch.empty_like(q)
     LSE = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_prefill(q, k, v, O, LSE, causal=int(causal), window=window, scale=scale)
+    if key_mask is None:
+        attn_prefill(q, k, v, O, LSE, causal=int(causal), window=window, scale=scale)
+    else:
+        attn_prefill_padded(q, k, v, pack_key_mask(key_mask), O, LSE, causal=int(causal),
+                            window=window, scale=scale)
     return O, LSE
 
 
-def prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None):
-    """Allocate O and LSE with torch and run attn_prefill_cache."""
+def prefill_cache(q, Kcache, Vcache, lens, window=0, scale=None, key_mask=None):
+    """Allocate O and LSE with torch and run attn_prefill_cache (key_mask: bool / uint8
+    [B, Tcap] over the cache rows, or None)."""
     import torch
     O = torch.empty_like(q)
     LSE = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_prefill_cache(q, Kcache, Vcache, lens, O, LSE, window=window, scale=scale)
+    bits = None if key_mask is None else pack_key_mask(key_mask)
+    attn_prefill_cache(q, Kcache, Vcache, lens, O, LSE, window=window, scale=scale,
+                       key_bits=bits)
     return O, LSE
 
 
-def decode(q, Kcache, Vcache, lens, window=0, scale=None):
+def decode(q, Kcache, Vcache, lens, window=0, scale=None, key_mask=None):
     """Allocate O, LSE and the workspace with torch and run attn_decode (or, with a
-    window or an explicit scale, attn_decode_window)."""
+    window or an explicit scale, attn_decode_window; with a key_mask, bool / uint8
+    [B, Tcap], attn_decode_padded)."""
     import torch
     B, Nq, Dh = q.shape
     O = torch.empty_like(q)
@@ -300,7 +506,10 @@ def decode(q, Kcache, Vcache, lens, window=0, scale=None):
     nbytes = attn_decode_window_workspace_bytes(B, Nq, Kcache.shape[1], Dh, Kcache.shape[2],
                                                 window, _dtype_code(q))
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if nbytes else None
-    if window or scale is not None:
+    if key_mask is not None:
+        attn_decode_padded(q, Kcache, Vcache, lens, pack_key_mask(key_mask), O, LSE, ws,
+                           window=window, scale=scale)
+    elif window or scale is not None:
         attn_decode_window(q, Kcache, Vcache, lens, O, LSE, ws, window=window, scale=scale)
     else:
         attn_decode(q, Kcache, Vcache, lens, O, LSE, ws)

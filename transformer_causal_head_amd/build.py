@@ -21,7 +21,8 @@ PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "general.hip", "cache.hip", "backward.hip", "backward_bf16.hip", "attn_api.cpp"]
+SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "general.hip", "cache.hip", "backward.hip", "backward_bf16.hip", "rope.hip", "keymask.hip",
+           "attn_api.cpp"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 
 FLAGS = [

@@ -23,11 +23,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
 }  // namespace
 
-extern "C" {
-
-int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
-                 int Nq, int Nkv, int S, int Dh, int causal, int window, float scale,
-                 int dtype, void* stream) {
+static int prefill_impl(const void* Q, const void* K, const void* V, const uint64_t* kbits,
+                        void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh, int causal,
+                        int window, float scale, int dtype, void* stream) {
   if (!Q || !K || !V || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
@@ -39,15 +37,15 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
-                                              causal, window, scale, s));
+                                              kbits, causal, window, scale, s));
   return from_hip(attn::launch_rows_general(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
-                                            causal, window, scale, dtype == ATTN_BF16, s));
+                                            kbits, causal, window, scale, dtype == ATTN_BF16, s));
 }
 
-int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
-                       const int32_t* lens, void* O, float* LSE, int B, int Nq, int Nkv,
-                       int Sq, int Dh, int Tcap, int window, float scale, int dtype,
-                       void* stream) {
+static int prefill_cache_impl(const void* Q, const void* Kcache, const void* Vcache,
+                              const int32_t* lens, const uint64_t* kbits, void* O, float* LSE,
+                              int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
+                              float scale, int dtype, void* stream) {
   if (!Q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
@@ -57,9 +55,41 @@ int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh,
-                                              Tcap, lens, 1, window, scale, s));
+                                              Tcap, lens, kbits, 1, window, scale, s));
   return from_hip(attn::launch_rows_general(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
-                                            lens, 1, window, scale, dtype == ATTN_BF16, s));
+                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s));
+}
+
+extern "C" {
+
+int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                 int Nq, int Nkv, int S, int Dh, int causal, int window, float scale,
+                 int dtype, void* stream) {
+  return prefill_impl(Q, K, V, nullptr, O, LSE, B, Nq, Nkv, S, Dh, causal, window, scale, dtype,
+                      stream);
+}
+
+int attn_prefill_padded(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                        void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh, int causal,
+                        int window, float scale, int dtype, void* stream) {
+  return prefill_impl(Q, K, V, key_bits, O, LSE, B, Nq, Nkv, S, Dh, causal, window, scale, dtype,
+                      stream);
+}
+
+int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, void* O, float* LSE, int B, int Nq, int Nkv,
+                       int Sq, int Dh, int Tcap, int window, float scale, int dtype,
+                       void* stream) {
+  return prefill_cache_impl(Q, Kcache, Vcache, lens, nullptr, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
+                            window, scale, dtype, stream);
+}
+
+int attn_prefill_cache_padded(const void* Q, const void* Kcache, const void* Vcache,
+                              const int32_t* lens, const uint64_t* key_bits, void* O, float* LSE,
+                              int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
+                              float scale, int dtype, void* stream) {
+  return prefill_cache_impl(Q, Kcache, Vcache, lens, key_bits, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
+                            window, scale, dtype, stream);
 }
 
 size_t attn_decode_window_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int window,
@@ -75,7 +105,8 @@ size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int
 }
 
 static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
-                       const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                       const int32_t* lens, const uint64_t* kbits, void* O, int B, int Nq,
+                       int Nkv, int Dh, int Tcap,
                        int window, float scale, float* LSE, void* workspace,
                        size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
@@ -89,26 +120,76 @@ static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
     return from_hip(attn::launch_decode_bf16(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv, Dh,
-                                             Tcap, window, scale, workspace, s));
+                                             Tcap, window, scale, kbits, workspace, s));
   }
   return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap,
-                                            lens, 1, window, scale, dtype == ATTN_BF16, s));
+                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s));
 }
 
 int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
                 void* O, int B, int Nq, int Nkv, int Dh, int Tcap, float* LSE, void* workspace,
                 size_t workspace_bytes, int dtype, void* stream) {
   const float scale = Dh > 0 ? 1.0f / sqrtf((float)Dh) : 1.0f;
-  return decode_impl(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, 0, scale, LSE, workspace,
-                     workspace_bytes, dtype, stream);
+  return decode_impl(q, Kcache, Vcache, lens, nullptr, O, B, Nq, Nkv, Dh, Tcap, 0, scale, LSE,
+                     workspace, workspace_bytes, dtype, stream);
 }
 
 int attn_decode_window(const void* q, const void* Kcache, const void* Vcache,
                        const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
                        int window, float scale, float* LSE, void* workspace,
                        size_t workspace_bytes, int dtype, void* stream) {
-  return decode_impl(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, window, scale, LSE,
+  return decode_impl(q, Kcache, Vcache, lens, nullptr, O, B, Nq, Nkv, Dh, Tcap, window, scale, LSE,
                      workspace, workspace_bytes, dtype, stream);
+}
+
+int attn_decode_padded(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, const uint64_t* key_bits, void* O, int B, int Nq,
+                       int Nkv, int Dh, int Tcap, int window, float scale, float* LSE,
+                       void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  return decode_impl(q, Kcache, Vcache, lens, key_bits, O, B, Nq, Nkv, Dh, Tcap, window, scale,
+                     LSE, workspace, workspace_bytes, dtype, stream);
+}
+
+int attn_pack_key_mask(const uint8_t* mask, int B, int T, uint64_t* key_bits, void* stream) {
+  if (!mask || !key_bits || !positive(B) || !positive(T)) return ATTN_EINVAL;
+  return from_hip(attn::launch_pack_key_mask(mask, B, T, key_bits,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int attn_rope_cos_sin(float* table, int P, int Dh, double base, void* stream) {
+  if (!table || !positive(P) || !positive(Dh) || Dh % 2 != 0) return ATTN_EINVAL;
+  if (!(base > 1.0) || !isfinite(base)) return ATTN_EINVAL;
+  return from_hip(attn::launch_rope_table(table, P, Dh, base, static_cast<hipStream_t>(stream)));
+}
+
+int attn_rope(const void* X, void* Y, const int32_t* positions, const int32_t* start,
+              const float* table, int P, int B, int H, int S, int Dh, int style, int dtype,
+              void* stream) {
+  if (!X || !Y || !table) return ATTN_EINVAL;
+  if (!positive(P) || !positive(B) || !positive(H) || !positive(S) || !positive(Dh))
+    return ATTN_EINVAL;
+  if (Dh % 2 != 0 || (style != 0 && style != 1)) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_EUNSUPPORTED;
+  return from_hip(attn::launch_rope(X, Y, positions, start, table, P, B, H, S, Dh, style,
+                                    dtype == ATTN_BF16 ? 2 : 4, static_cast<hipStream_t>(stream)));
+}
+
+int attn_kv_append_rope(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
+                        const int32_t* pos, const int32_t* positions, const float* table, int P,
+                        int B, int Nkv, int Snew, int Dh, int Tcap, int rolling, int style,
+                        int dtype, void* stream) {
+  if (!Knew || !Vnew || !Kcache || !Vcache || !pos || !table) return ATTN_EINVAL;
+  if (!positive(B) || !positive(Nkv) || !positive(Snew) || !positive(Dh) || !positive(Tcap) ||
+      !positive(P))
+    return ATTN_EINVAL;
+  if (Dh % 2 != 0 || (style != 0 && style != 1)) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_EUNSUPPORTED;
+  if (rolling != 0 && rolling != 1) return ATTN_EINVAL;
+  if (!rolling && Snew > Tcap) return ATTN_EINVAL;
+  return from_hip(attn::launch_kv_append_rope(Knew, Vnew, Kcache, Vcache, pos, positions, table, P,
+                                              B, Nkv, Snew, Dh, Tcap, rolling, style,
+                                              dtype == ATTN_BF16 ? 2 : 4,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,

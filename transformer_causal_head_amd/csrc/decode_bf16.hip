@@ -78,6 +78,8 @@ struct DecParams {
   const __bf16* K;
   const __bf16* V;
   const int32_t* lens;
+  const uint64_t* kbits;  // key-padding mask, one bit per cache slot (kwords words per sequence)
+  int kwords;
   __bf16* O;
   float* LSE;
   float* ws_o;    // [B, Nkv, n_slots, G, D] unnormalised partial outputs
@@ -129,8 +131,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
-// NB blocks of 16 query heads per K/V head (G <= 16 * NB).
-template <int D, int NB>
+// NB blocks of 16 query heads per K/V head (G <= 16 * NB).  KM: a key-padding
+// mask is given (p.kbits); without it the kernel is compiled as if it did not
+// exist.
+template <int D, int NB, bool KM>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   using geo = DGeo<D>;
   constexpr int STAGE = geo::STAGE;
@@ -227,8 +231,20 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
   }
 
+  // key-padding flags, read as wave-uniform scalar loads (constant address
+  // space) that stay off the vector-memory counter the copies use
+  typedef __attribute__((address_space(4))) const uint64_t const_u64;
+  const_u64* const kwrow = KM ? (const_u64*)(p.kbits + (size_t)b * p.kwords) : nullptr;
+
   auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
     const int k0 = c0 + s * STEP;
+    // flags of keys k0 .. k0 + 31 (k0 is a multiple of 32); a step of padding
+    // keys only changes nothing
+    uint32_t kw = ~0u;
+    if constexpr (KM) {
+      kw = (uint32_t)(kwrow[k0 >> 6] >> (k0 & 32));
+      if (kw == 0) return;
+    }
     // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
     // query column l16 of head block nb
     f32x4 sc[NB][2];
@@ -244,13 +260,15 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
           sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], sc[nb][kb], 0, 0, 0);
       }
     }
-    if (k0 + STEP > n || k0 < lo) {
+    if (k0 + STEP > n || k0 < lo || (KM && kw != ~0u)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + kb * 16 + grp * 4 + r;
-          if (key >= n || key < lo) {
+          bool hide = key >= n || key < lo;
+          if (KM) hide = hide || !((kw >> (kb * 16 + grp * 4 + r)) & 1);
+          if (hide) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb][kb][r] = -INFINITY;
           }
@@ -264,7 +282,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
                        fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_cand = mx * p.c;  // every step run holds a visible key: finite
+      // every step run holds a visible key unless a key-padding mask hides it
+      const float m_cand = mx * p.c;
       if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + TAU)) {
         const float m_new = fmaxf(m_run[nb], m_cand);
         const float alpha = exp2_fast(m_run[nb] - m_new);
@@ -273,12 +292,13 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
       }
+      const float m_use = (KM && m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = exp2_fast(__builtin_fmaf(t[kb][r], p.c, -m_run[nb]));
+          const float e = exp2_fast(__builtin_fmaf(t[kb][r], p.c, -m_use));
           t[kb][r] = e;
           rs += e;
         }
@@ -343,7 +363,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
 // first read the chunks' (m, l) side by side and reduce them across the
 // wavefront; then each lane accumulates D/64 head-dims over the chunks, with
 // the chunk weights broadcast from the lane that computed them.
-template <int D>
+template <int D, bool KM>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   constexpr int PL = D / 64;  // head-dims per lane
   typedef float fvec __attribute__((ext_vector_type(PL)));
@@ -365,6 +385,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
   float M = -INFINITY;
   for (int x = lane; x < ns; x += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)x * G) * 2]);
   M = wave_max(M);
+  // with a key-padding mask every chunk may hold padding only (M = -inf)
+  const float Mu = (KM && M == -INFINITY) ? 0.f : M;
   float L = 0.f;
   fvec acc = {};
   for (int cb = 0; cb < ns; cb += 64) {
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     float wgt = 0.f;
     if (cb + lane < ns) {
       const size_t part = part0 + (size_t)(cb + lane) * G;
-      wgt = exp2_fast(p.ws_ml[part * 2] - M);
+      wgt = exp2_fast(p.ws_ml[part * 2] - Mu);
       L = __builtin_fmaf(wgt, p.ws_ml[part * 2 + 1], L);
     }
     const int cnt = min(64, ns - cb);
@@ -398,7 +420,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     }
   }
   L = wave_sum(L);
-  const float inv = 1.f / L;  // n < 1 leaves L = 0: NaN row
+  // n < 1 leaves L = 0: a NaN row, or O = 0 and LSE = -inf with a key-padding mask
+  const float inv = (KM && L == 0.f) ? 0.f : 1.f / L;
   __bf16* dst = p.O + (size_t)row * D + lane * PL;
 #pragma unroll
   for (int e = 0; e < PL; ++e) dst[e] = (__bf16)(acc[e] * inv);
@@ -438,15 +461,19 @@ DecodePlan decode_plan(int B, int Nkv, int Tcap, int window) {
   return d;
 }
 
-template <int D, int NB>
-hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partial_kernel<D, NB>), dim3(p.n_slots, p.Nkv, p.B), dim3(64), 0,
+template <int D, int NB, bool KM>
+hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM>), dim3(p.n_slots, p.Nkv, p.B), dim3(64), 0,
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Nq;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D, KM>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+template <int D, int NB>
+hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
+  return p.kbits ? launch_decode_km<D, NB, true>(p, stream) : launch_decode_km<D, NB, false>(p, stream);
 }
 }  // namespace
 
@@ -458,13 +485,16 @@ size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int windo
 
 hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
                               void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
-                              int window, float scale, void* ws, hipStream_t stream) {
+                              int window, float scale, const uint64_t* kbits, void* ws,
+                              hipStream_t stream) {
   const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
   DecParams p;
   p.q = static_cast<const __bf16*>(q);
   p.K = static_cast<const __bf16*>(Kc);
   p.V = static_cast<const __bf16*>(Vc);
   p.lens = lens;
+  p.kbits = kbits;
+  p.kwords = key_mask_words(Tcap);
   p.O = static_cast<__bf16*>(O);
   p.LSE = LSE;
   p.B = B;

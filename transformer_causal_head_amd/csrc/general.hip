@@ -30,6 +30,8 @@ struct RowParams {
   float* LSE;
   int B, Nq, Nkv, S, Dh, kv_rows;  // S: query rows per head
   const int32_t* lens;              // keys per sequence in a cache, or null
+  const uint64_t* kbits;            // key-padding mask bits (kwords per sequence), or null
+  int kwords;
   int causal, window;
   float scale;
   long long n_rows;
@@ -68,7 +70,9 @@ __global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
     o[u] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  const uint64_t* kw = p.kbits ? p.kbits + (size_t)b * p.kwords : nullptr;
   for (int j = lo; j < hi; ++j) {
+    if (kw && !((kw[j >> 6] >> (j & 63)) & 1)) continue;  // padding key (uniform branch)
     const size_t r = kvoff + (size_t)j * p.Dh;
     float part = 0.f;
 #pragma unroll
@@ -89,8 +93,9 @@ __global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
     }
     m = m_new;
   }
-  // hi <= lo (decode length below 1) leaves l = 0: the row becomes 0/0 = NaN
-  const float inv = 1.f / l;
+  // no visible key leaves l = 0: the row becomes 0/0 = NaN (decode length
+  // below 1), or O = 0 and LSE = -inf when a key-padding mask hid every key
+  const float inv = (kw && l == 0.f) ? 0.f : 1.f / l;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int d = lane + 64 * u;
@@ -103,8 +108,9 @@ __global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
 
 hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void* O,
                                float* LSE, int B, int Nq, int Nkv, int S, int Dh,
-                               int kv_rows, const int32_t* lens, int causal, int window,
-                               float scale, int is_bf16, hipStream_t stream) {
+                               int kv_rows, const int32_t* lens, const uint64_t* kbits,
+                               int causal, int window, float scale, int is_bf16,
+                               hipStream_t stream) {
   RowParams p;
   p.Q = Q;
   p.K = K;
@@ -118,6 +124,8 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
   p.Dh = Dh;
   p.kv_rows = kv_rows;
   p.lens = lens;
+  p.kbits = kbits;
+  p.kwords = key_mask_words(kv_rows);
   p.causal = causal;
   p.window = window;
   p.scale = scale;

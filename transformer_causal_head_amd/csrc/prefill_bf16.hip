@@ -95,6 +95,8 @@ struct Params {
   __bf16* O;
   float* LSE;
   const int32_t* lens;  // keys per sequence in a cache (chunked prefill), or null
+  const uint64_t* kbits;  // key-padding mask, one bit per key (kwords words per sequence)
+  int kwords;
   int B, Nq, Nkv, S;    // S: query rows per head
   int kv_rows;          // rows per K/V head in memory (S, or the cache capacity)
   int causal, window;
@@ -168,7 +170,9 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
   if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int NW>
+// KM: a key-padding mask is given (p.kbits); without it the kernel is
+// compiled exactly as if the mask did not exist.
+template <int D, int NW, bool KM>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   using geo = Geo<D>;
   constexpr int TILE = geo::TILE;
@@ -284,11 +288,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   tl_hi = __builtin_amdgcn_readfirstlane(tl_hi);
   tf_lo = __builtin_amdgcn_readfirstlane(tf_lo);
   tf_hi = __builtin_amdgcn_readfirstlane(tf_hi);
-  // does this wave see any (query, key) pair of tile t?
-  auto live = [&](int t) { return t >= tl_lo && t <= tl_hi; };
+  // key-padding flags of tile t's 64 keys: one scalar load of a wave-uniform
+  // word through the constant address space (off the vector-memory counter
+  // the tile copies use)
+  typedef __attribute__((address_space(4))) const uint64_t const_u64;
+  const_u64* const kwrow = KM ? (const_u64*)(p.kbits + (size_t)b * p.kwords) : nullptr;
+  auto key_word = [&](int t) -> uint64_t { return KM ? kwrow[t] : ~0ull; };
+  // does this wave see any (query, key) pair of tile t?  (a tile of padding
+  // keys only is skipped like one the causal mask hides)
+  auto live = [&](int t) { return t >= tl_lo && t <= tl_hi && (!KM || key_word(t) != 0); };
 
   // --- pieces of the per-tile softmax ---
-  auto masked = [&](int t) { return t < tf_lo || t > tf_hi; };
+  auto masked = [&](int t) { return t < tf_lo || t > tf_hi || (KM && key_word(t) != ~0ull); };
   // Visible keys of this lane's query qi form one interval [lo_i, hi_i]
   // (causal: hi_i = qi; window: lo_i = qi - window + 1; keys < S), so a
   // boundary tile's mask is two compares per score.
@@ -301,6 +312,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   }
   auto mask_tile = [&](int t, f32x16 (&s)[QB][2]) {
     const int k0 = t * BN + hl * 4;
+    // this lane's key flags: bit o of kl is key k0 + o
+    const uint64_t kl = key_word(t) >> (hl * 4);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // key of register r in block kb: k0 + 32*kb + 8*(r/4) + (r%4)
@@ -310,7 +323,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int o = kb * 32 + (r >> 2) * 8 + (r & 3);
-          if (o > hi || o < lo) s[qb][kb][r] = -INFINITY;
+          bool hide = o > hi || o < lo;
+          if (KM) hide = hide || !((kl >> o) & 1);
+          if (hide) s[qb][kb][r] = -INFINITY;
         }
     }
   };
@@ -423,7 +438,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     const int qi = qa_row + qb * 32 + ln;  // query row
     const float l_tot = xhalf_sum(l_run[qb]);
     if (qi >= p.S) continue;
-    const float inv = 1.f / l_tot;
+    // with a key-padding mask a row may see no key at all: O = 0, LSE = -inf
+    const float inv = (KM && l_tot == 0.f) ? 0.f : 1.f / l_tot;
     __bf16* orow = p.O + q_base + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -443,7 +459,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
 template <int D>
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
                           int B, int Nq, int Nkv, int S, int kv_rows, const int32_t* lens,
-                          int causal, int window, float scale, hipStream_t stream) {
+                          const uint64_t* kbits, int causal, int window, float scale,
+                          hipStream_t stream) {
   constexpr int NW = waves_for<D>();
   // one head of K (or V) is addressed through a 31-bit buffer range
   if ((long long)kv_rows * D * 2 > 0x7fffffffLL || (long long)S * D * 2 > 0x7fffffffLL)
@@ -455,6 +472,8 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.O = static_cast<__bf16*>(O);
   p.LSE = LSE;
   p.lens = lens;
+  p.kbits = kbits;
+  p.kwords = key_mask_words(kv_rows);
   p.B = B;
   p.Nq = Nq;
   p.Nkv = Nkv;
@@ -470,7 +489,12 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.n_qtiles = (S + p.qspan - 1) / p.qspan;
   const long long nblocks = (long long)p.n_qtiles * B * Nkv * p.n_hsub;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<D, NW>), dim3((unsigned)nblocks), dim3(NW * 64), 0, stream, p);
+  if (kbits)
+    hipLaunchKernelGGL((prefill_kernel<D, NW, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, NW, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -480,18 +504,18 @@ bool prefill_bf16_supported(int Dh) { return Dh == 64 || Dh == 128 || Dh == 256;
 
 hipError_t launch_prefill_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int B, int Nq, int Nkv, int S, int Dh, int kv_rows,
-                               const int32_t* lens, int causal, int window, float scale,
-                               hipStream_t stream) {
+                               const int32_t* lens, const uint64_t* kbits, int causal, int window,
+                               float scale, hipStream_t stream) {
   switch (Dh) {
     case 64:
-      return launch_prefill<64>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
-                                scale, stream);
+      return launch_prefill<64>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
+                                window, scale, stream);
     case 128:
-      return launch_prefill<128>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
-                                 scale, stream);
+      return launch_prefill<128>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
+                                 window, scale, stream);
     case 256:
-      return launch_prefill<256>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, causal, window,
-                                 scale, stream);
+      return launch_prefill<256>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
+                                 window, scale, stream);
     default:
       return hipErrorInvalidValue;
   }

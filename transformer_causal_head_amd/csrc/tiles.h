@@ -61,6 +61,11 @@ __device__ __forceinline__ HeadRef head_ref(const __bf16* head, int rows) {
 }
 template <int D, int NW>
 __device__ __forceinline__ void load_tile(HeadRef h, int k0, char* tile, int w, int lane) {
+  // The buffer-resource builtin exists only for the GPU target.  The host
+  // pass of a translation unit that instantiates one kernel twice (with and
+  // without a key mask) would otherwise reject this body, so it only sees an
+  // empty one; the host never runs device functions.
+#if defined(__HIP_DEVICE_COMPILE__)
   using g = Geo<D>;
 #pragma unroll
   for (int j = 0; j < (g::NP + NW - 1) / NW; ++j) {
@@ -71,6 +76,7 @@ __device__ __forceinline__ void load_tile(HeadRef h, int k0, char* tile, int w, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
                                              voff + k0 * g::RB, 0, 0, 0);
   }
+#endif
 }
 
 __device__ __forceinline__ float xhalf_max(float v) {

@@ -225,3 +225,27 @@ def decode_work(lens, Nq, Nkv, Dh, elem_bytes):
     nbytes = 2 * total * Nkv * Dh * elem_bytes + 2 * B * Nq * Dh * elem_bytes + 4 * B
     flops = 4 * Dh * Nq * total
     return flops, nbytes
+
+
+def key_mask(B, T, pads=None, hole_frac=0.0, seed=0, block=None):
+    """Seeded key-padding mask, bool [B, T] (True = real token).
+
+    pads[b] leading keys of row b are padding (left padding of a batch of
+    prompts of different lengths); each other key is padding with probability
+    hole_frac; ``block`` = (start, stop) makes keys start..stop-1 of every row
+    padding (a whole tile of padding keys).
+    """
+    rng = np.random.default_rng(seed + 7919)
+    m = rng.random((B, T)) >= hole_frac
+    if pads is not None:
+        for b, p in enumerate(pads):
+            m[b, :p] = False
+    if block is not None:
+        m[:, block[0]:block[1]] = False
+    return m
+
+
+def token_positions(mask):
+    """Positions counted from each row's first real token (padding tokens get 0):
+    the positions a model passes to RoPE for a padded batch."""
+    return np.maximum(np.cumsum(mask, axis=1) - 1, 0).astype(np.int32)
