@@ -263,6 +263,93 @@ def _backward(torch, dev, tch, steps, warmup):
         del tq, tk, tv, tdo, O, L, dQ, dK, dV, ws
 
 
+def _rope_padding(torch, dev, tch, steps, warmup):
+    """One JSON line per measurement: RoPE in place on the prefill queries, the rotating
+    cache append (a 2048-token chunk and one decode token), and the padded prefill and
+    decode next to their unpadded forms on the same inputs."""
+    pc = workloads.WORKLOADS[PREFILL]
+    B, H, S, Dh = pc["B"], pc["Nq"], pc["S"], pc["Dh"]
+    x = torch.randn(B, H, S, Dh, device=dev, dtype=torch.bfloat16)
+    table = tch.rope_table(S, Dh, device=dev)
+    ms = _time(torch, lambda: tch.attn_rope(x, x, table, style=1), steps, warmup)
+    nbytes = 2 * x.numel() * 2 + S * Dh * 4  # rows read and written, table rows read once
+    print(json.dumps({"path": "attn_rope (in place)", "workload": f"B={B} H={H} S={S} Dh={Dh} "
+                      "bf16, half layout", "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                      "frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": nbytes}), flush=True)
+    del x, table
+
+    # rotating append: a 2048-token chunk of 8 K/V heads into a 32768-row cache
+    Nkv, T = 8, 32768
+    table = tch.rope_table(T, Dh, device=dev)
+    Kc = torch.zeros(1, Nkv, T, Dh, device=dev, dtype=torch.bfloat16)
+    Vc = torch.zeros_like(Kc)
+    for Bn, Sn in ((1, 2048), (64, 1)):
+        if Bn != Kc.shape[0]:
+            Kc = torch.zeros(Bn, Nkv, T, Dh, device=dev, dtype=torch.bfloat16)
+            Vc = torch.zeros_like(Kc)
+        kn = torch.randn(Bn, Nkv, Sn, Dh, device=dev, dtype=torch.bfloat16)
+        vn = torch.randn_like(kn)
+        pos = torch.full((Bn,), T - 4096, dtype=torch.int32, device=dev)
+        ms = _time(torch, lambda: tch.attn_kv_append_rope(kn, vn, Kc, Vc, pos, table, style=1),
+                   steps, warmup)
+        nbytes = 2 * 2 * kn.numel() * 2 + Bn * Sn * Dh * 4
+        print(json.dumps({"path": "attn_kv_append_rope", "workload": f"B={Bn} Nkv={Nkv} "
+                          f"Snew={Sn} Dh={Dh} bf16 into Tcap={T}", "ms": round(ms, 4),
+                          "GB/s": round(nbytes / ms / 1e6, 1), "algorithmic_bytes": nbytes}),
+              flush=True)
+        del kn, vn
+    del Kc, Vc, table
+
+    # padded prefill: the 4 x 8192 GQA workload's shape, left padding of 0, 1024, 2048 and
+    # 4096 tokens (causal, no window); FLOPs over the visible pairs only
+    B, Nq, Nkv, S = 4, 32, 8, 8192
+    pads = [0, 1024, 2048, 4096]
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
+    tq, tk, tv = (workloads.to_torch(a, "bf16", dev) for a in (q, k, v))
+    del q, k, v
+    mask = torch.from_numpy(workloads.key_mask(B, S, pads=pads)).to(dev)
+    bits = tch.pack_key_mask(mask)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(Dh)
+    ms_pad = _time(torch, lambda: tch.attn_prefill_padded(tq, tk, tv, bits, O, L, scale=scale),
+                   steps, warmup)
+    ms_full = _time(torch, lambda: tch.attn_prefill(tq, tk, tv, O, L, scale=scale), steps, warmup)
+    pairs = sum((S - p) * (S - p + 1) // 2 for p in pads)
+    flop = 4 * Dh * Nq * pairs
+    full_flop, _ = workloads.prefill_work(B, Nq, Nkv, S, Dh, True, 0, 2)
+    print(json.dumps({"path": "attn_prefill_padded", "workload": f"B={B} Nq={Nq} Nkv={Nkv} "
+                      f"S={S} Dh={Dh} bf16 causal, left padding {pads}", "ms": round(ms_pad, 4),
+                      "TFLOP/s": round(flop / ms_pad / 1e9, 1),
+                      "unpadded_ms": round(ms_full, 4),
+                      "unpadded_TFLOP/s": round(full_flop / ms_full / 1e9, 1),
+                      "algorithmic_flop": flop}), flush=True)
+    del tq, tk, tv, O, L, mask, bits
+
+    # padded decode: the batched decode workload with 10% of the cached keys padding
+    dc = workloads.WORKLOADS[DECODE]
+    B, Nq, Nkv, T = dc["B"], dc["Nq"], dc["Nkv"], dc["Tcap"]
+    lens, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, T, dc["len_lo"], dc["len_hi"])
+    tq, tk, tv = (workloads.to_torch(a, "bf16", dev) for a in (q, kc, vc))
+    del kc, vc
+    tl = torch.from_numpy(lens).to(dev)
+    bits = tch.pack_key_mask(torch.from_numpy(workloads.key_mask(B, T, hole_frac=0.1)).to(dev))
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, T, tch.ATTN_BF16),
+                     dtype=torch.uint8, device=dev)
+    ms_pad = _time(torch, lambda: tch.attn_decode_padded(tq, tk, tv, tl, bits, O, L, ws),
+                   steps, warmup)
+    ms_full = _time(torch, lambda: tch.attn_decode(tq, tk, tv, tl, O, L, ws), steps, warmup)
+    _, nbytes = workloads.decode_work(lens, Nq, Nkv, Dh, 2)
+    print(json.dumps({"path": "attn_decode_padded", "workload": f"{DECODE}, 10% of keys padding",
+                      "ms": round(ms_pad, 4), "GB/s": round(nbytes / ms_pad / 1e6, 1),
+                      "unpadded_ms": round(ms_full, 4),
+                      "unpadded_GB/s": round(nbytes / ms_full / 1e6, 1),
+                      "algorithmic_bytes": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,6 +366,9 @@ def main():
     ap.add_argument("--cache-paths", action="store_true",
                     help="time the cache-side entry points (chunked prefill, windowed and "
                          "rolling-buffer decode, append) instead of the main step")
+    ap.add_argument("--rope-padding", action="store_true",
+                    help="time RoPE, the rotating append and the padded prefill / decode "
+                         "instead of the main step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) instead of the main step")
     args = ap.parse_args()
@@ -310,6 +400,9 @@ def main():
         return
     if args.backward:
         _backward(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
+        return
+    if args.rope_padding:
+        _rope_padding(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
 
     pc = workloads.WORKLOADS[PREFILL]

@@ -161,11 +161,33 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   const int chunk = lo / p.ch + blockIdx.x;
   const int c0 = chunk * p.ch;
   if (c0 >= n) return;
-  const int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
-  const int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
+  int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
+  int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
   const int last = min(n, c0 + p.ch) - 1;
 
   const int lane = threadIdx.x;
+  // key-padding flags: lane j holds the 32 flags of step s_flags + j (a chunk
+  // has at most 64 steps), read in the loop with v_readlane
+  const int s_flags = s0;
+  uint32_t kw_lane = 0;
+  if constexpr (KM) {
+    // drop the leading and trailing steps whose 32 keys are all padding, so
+    // they are neither copied nor waited for; the ballot gives the ends
+    const int s = s0 + lane;
+    if (s < nsteps) {
+      const int k = c0 + s * STEP;
+      kw_lane = (uint32_t)(p.kbits[(size_t)b * p.kwords + (k >> 6)] >> (k & 32));
+    }
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(kw_lane != 0);
+    if (bal == 0) {
+      nsteps = s0;  // padding only: no step runs, the partial stays empty
+    } else {
+      nsteps = s0 + 64 - __builtin_clzll(bal);
+      s0 += __builtin_ctzll(bal);
+    }
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    nsteps = __builtin_amdgcn_readfirstlane(nsteps);
+  }
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int G = p.G;
@@ -231,18 +253,13 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
   }
 
-  // key-padding flags, read as wave-uniform scalar loads (constant address
-  // space) that stay off the vector-memory counter the copies use
-  typedef __attribute__((address_space(4))) const uint64_t const_u64;
-  const_u64* const kwrow = KM ? (const_u64*)(p.kbits + (size_t)b * p.kwords) : nullptr;
-
   auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
     const int k0 = c0 + s * STEP;
     // flags of keys k0 .. k0 + 31 (k0 is a multiple of 32); a step of padding
     // keys only changes nothing
     uint32_t kw = ~0u;
     if constexpr (KM) {
-      kw = (uint32_t)(kwrow[k0 >> 6] >> (k0 & 32));
+      kw = __builtin_amdgcn_readlane(kw_lane, s - s_flags);
       if (kw == 0) return;
     }
     // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
@@ -439,7 +456,9 @@ bool decode_bf16_supported(int Nq, int Nkv, int Dh) {
 // keys (L = Tcap, or the window when it is shorter).  The candidates are
 // multiples of 32 keys, none a power of two.
 int decode_bf16_chunk(int B, int Nkv, int L) {
+  // at most 64 steps per chunk: the key-padding trim tests one step per lane
   static const int kChunks[] = {1792, 1152, 896, 640, 384, 224, 160, 96};
+  static_assert(1792 <= 64 * STEP, "a chunk must fit one wavefront of steps");
   const long long heads = (long long)B * Nkv;
   for (int ch : kChunks)
     if (heads * ((L + ch - 1) / ch) >= 2048) return ch;

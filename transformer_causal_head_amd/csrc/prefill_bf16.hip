@@ -224,8 +224,35 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   // key range of the workgroup
   const int hi_key = p.causal ? q1 : n_keys;
   const int lo_key = (p.causal && p.window > 0) ? max(0, q0 - p.window + 1) : 0;
-  const int t_lo = lo_key / BN;
-  const int nt = (hi_key + BN - 1) / BN - t_lo;
+  int t_lo = lo_key / BN;
+  int t_end = (hi_key + BN - 1) / BN;  // one past the last tile
+  if constexpr (KM) {
+    // drop the leading and trailing tiles that hold padding keys only (a
+    // left- or right-padded batch), so they are neither copied nor waited
+    // for: each lane tests one tile's mask word, the ballot gives the ends
+    const uint64_t* kr = p.kbits + (size_t)b * p.kwords;
+    while (t_lo < t_end) {
+      const int t = t_lo + lane;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(t < t_end && kr[t] != 0);
+      if (bal) {
+        t_lo += __builtin_ctzll(bal);
+        break;
+      }
+      t_lo = min(t_lo + 64, t_end);
+    }
+    while (t_end > t_lo) {
+      const int t = t_end - 1 - lane;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(t >= t_lo && kr[t] != 0);
+      if (bal) {
+        t_end -= __builtin_ctzll(bal);
+        break;
+      }
+      t_end = max(t_end - 64, t_lo);
+    }
+    t_lo = __builtin_amdgcn_readfirstlane(t_lo);
+    t_end = __builtin_amdgcn_readfirstlane(t_end);
+  }
+  const int nt = t_end - t_lo;
 
   char* const K0 = k0s;
   char* const K1 = k1s;
@@ -288,18 +315,44 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   tl_hi = __builtin_amdgcn_readfirstlane(tl_hi);
   tf_lo = __builtin_amdgcn_readfirstlane(tf_lo);
   tf_hi = __builtin_amdgcn_readfirstlane(tf_hi);
-  // key-padding flags of tile t's 64 keys: one scalar load of a wave-uniform
-  // word through the constant address space (off the vector-memory counter
-  // the tile copies use)
-  typedef __attribute__((address_space(4))) const uint64_t const_u64;
-  const_u64* const kwrow = KM ? (const_u64*)(p.kbits + (size_t)b * p.kwords) : nullptr;
-  auto key_word = [&](int t) -> uint64_t { return KM ? kwrow[t] : ~0ull; };
+  // key-padding flags of the tiles.  Lane j holds the mask word of tile
+  // kw_base + j; two ballots over those words give, one bit per tile, "holds
+  // a real key" (kw_key) and "holds padding" (kw_pad), so the per-tile tests
+  // are scalar bit tests.  The window is refilled between runs of KW_RUN
+  // tiles, outside the loop that streams the tiles: a load inside it would
+  // make the copies of the next tiles wait.  A run of KW_RUN tiles asks about
+  // tiles up to one past its last, which the 64-tile window covers.
+  uint64_t kw_lane = 0, kw_key = ~0ull, kw_pad = 0;
+  int kw_base = t_lo;
+  auto refill = [&](int base) {
+    kw_base = base;
+    const int t = base + lane;
+    kw_lane = t < t_end ? p.kbits[(size_t)b * p.kwords + t] : 0;
+    kw_key = __builtin_amdgcn_ballot_w64(kw_lane != 0);
+    kw_pad = __builtin_amdgcn_ballot_w64(kw_lane != ~0ull);
+  };
+  if constexpr (KM) refill(t_lo);
+  constexpr int KW_RUN = 62;  // even: the two-stage loop below keeps its parity
+  auto key_word = [&](int t) -> uint64_t {  // the word itself (boundary tiles only)
+    if constexpr (!KM) {
+      return ~0ull;
+    } else {
+      const int j = t - kw_base;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)kw_lane, j);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(kw_lane >> 32), j);
+      return ((uint64_t)hi << 32) | lo;
+    }
+  };
   // does this wave see any (query, key) pair of tile t?  (a tile of padding
   // keys only is skipped like one the causal mask hides)
-  auto live = [&](int t) { return t >= tl_lo && t <= tl_hi && (!KM || key_word(t) != 0); };
+  auto live = [&](int t) {
+    return t >= tl_lo && t <= tl_hi && (!KM || ((kw_key >> (t - kw_base)) & 1));
+  };
 
   // --- pieces of the per-tile softmax ---
-  auto masked = [&](int t) { return t < tf_lo || t > tf_hi || (KM && key_word(t) != ~0ull); };
+  auto masked = [&](int t) {
+    return t < tf_lo || t > tf_hi || (KM && ((kw_pad >> (t - kw_base)) & 1));
+  };
   // Visible keys of this lane's query qi form one interval [lo_i, hi_i]
   // (causal: hi_i = qi; window: lo_i = qi - window + 1; keys < S), so a
   // boundary tile's mask is two compares per score.
@@ -407,9 +460,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     };
 
     int i = 0;
-    for (; i + 1 < nt; i += 2) {
-      iteration(i, sa, sb);
-      iteration(i + 1, sb, sa);
+    if constexpr (KM) {
+      for (int c = 0; c < nt; c += KW_RUN) {
+        if (c > 0) refill(t_lo + c);
+        const int c_end = min(nt, c + KW_RUN);
+        for (; i + 1 < c_end; i += 2) {
+          iteration(i, sa, sb);
+          iteration(i + 1, sb, sa);
+        }
+      }
+    } else {
+      for (; i + 1 < nt; i += 2) {
+        iteration(i, sa, sb);
+        iteration(i + 1, sb, sa);
+      }
     }
     if (i < nt) iteration(i, sa, sb);
   } else {
@@ -418,6 +482,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
     f32x16 s[QB][2];
     for (int i = 0; i < nt; ++i) {
       const int t = t_lo + i;
+      if (KM && i > 0 && i % KW_RUN == 0) refill(t);
       wait_dma();
       __syncthreads();
       if (i + 1 < nt) {
