@@ -28,6 +28,12 @@
 #include "common.h"
 #include "kernels.h"
 
+// Rows of X / Y (read once, written once) bypass the caches' retention with
+// non-temporal accesses; the table rows, reread by every head, do not.
+#ifndef ROPE_NT
+#define ROPE_NT 1
+#endif
+
 namespace attn {
 
 namespace {
@@ -46,14 +52,15 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* table, int P, in
 }
 
 // N consecutive elements (N * sizeof(T) bytes, 16-byte aligned when VEC) widened to fp32
-template <typename T, int N, bool VEC>
+template <typename T, int N, bool VEC, bool NT = false>
 __device__ __forceinline__ void load_row(const T* src, float (&dst)[N]) {
   if constexpr (VEC) {
     constexpr int E = 16 / sizeof(T);
     static_assert(N % E == 0, "whole 16-byte chunks");
 #pragma unroll
     for (int c = 0; c < N / E; ++c) {
-      const u32x4 w = reinterpret_cast<const u32x4*>(src)[c];
+      const u32x4* a = reinterpret_cast<const u32x4*>(src) + c;
+      const u32x4 w = NT ? __builtin_nontemporal_load(a) : *a;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if constexpr (sizeof(T) == 2)
@@ -68,7 +75,7 @@ __device__ __forceinline__ void load_row(const T* src, float (&dst)[N]) {
   }
 }
 
-template <typename T, int N, bool VEC>
+template <typename T, int N, bool VEC, bool NT = false>
 __device__ __forceinline__ void store_row(T* dst, const float (&src)[N]) {
   if constexpr (VEC) {
     constexpr int E = 16 / sizeof(T);
@@ -82,7 +89,10 @@ __device__ __forceinline__ void store_row(T* dst, const float (&src)[N]) {
         else
           w[e] = __float_as_uint(src[c * E + e]);
       }
-      reinterpret_cast<u32x4*>(dst)[c] = w;
+      if constexpr (NT)
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst) + c);
+      else
+        reinterpret_cast<u32x4*>(dst)[c] = w;
     }
   } else {
 #pragma unroll
@@ -90,35 +100,61 @@ __device__ __forceinline__ void store_row(T* dst, const float (&src)[N]) {
   }
 }
 
-// Rotate pairs m0 .. m0 + PP - 1 of one row: x -> y (y may be x), with the
-// cos / sin row cs of its position.
+// Rotate thread j's PP pairs of one row (tpr threads per row): x -> y (y may
+// be x), with the cos / sin row cs of its position.
 template <typename T, int PP, int STYLE, bool VEC>
-__device__ __forceinline__ void rotate_pairs(const T* x, T* y, const float* cs, int half, int m0) {
+__device__ __forceinline__ void rotate_pairs(const T* x, T* y, const float* cs, int half, int j,
+                                             int tpr) {
+  constexpr bool NTX = VEC && ROPE_NT != 0;
+  if constexpr (STYLE == 0 && VEC) {
+    // pairs layout, 16-byte vectors: a chunk of E elements holds CP whole
+    // pairs; thread j takes chunks j, j + tpr, ..., so that every load
+    // instruction of the wavefront reads consecutive chunks of a row
+    constexpr int E = 16 / sizeof(T);
+    constexpr int CP = E / 2;
+#pragma unroll
+    for (int u = 0; u < PP / CP; ++u) {
+      const int ch = j + u * tpr;
+      float v[E], c[CP], s[CP];
+      load_row<T, E, true, NTX>(x + ch * E, v);
+      load_row<float, CP, CP % 4 == 0>(cs + ch * CP, c);
+      load_row<float, CP, CP % 4 == 0>(cs + half + ch * CP, s);
+#pragma unroll
+      for (int k = 0; k < CP; ++k) {
+        const float a = v[2 * k], b = v[2 * k + 1];
+        v[2 * k] = __builtin_fmaf(a, c[k], -b * s[k]);
+        v[2 * k + 1] = __builtin_fmaf(a, s[k], b * c[k]);
+      }
+      store_row<T, E, true, NTX>(y + ch * E, v);
+    }
+    return;
+  }
+  const int m0 = j * PP;
   float c[PP], s[PP];
   load_row<float, PP, VEC>(cs + m0, c);
   load_row<float, PP, VEC>(cs + half + m0, s);
   if constexpr (STYLE == 0) {  // pairs (x[2m], x[2m+1]): 2 * PP consecutive elements
     float v[2 * PP];
-    load_row<T, 2 * PP, VEC>(x + 2 * m0, v);
+    load_row<T, 2 * PP, VEC, NTX>(x + 2 * m0, v);
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
       const float a = v[2 * k], b = v[2 * k + 1];
       v[2 * k] = __builtin_fmaf(a, c[k], -b * s[k]);
       v[2 * k + 1] = __builtin_fmaf(a, s[k], b * c[k]);
     }
-    store_row<T, 2 * PP, VEC>(y + 2 * m0, v);
+    store_row<T, 2 * PP, VEC, NTX>(y + 2 * m0, v);
   } else {  // halves (x[m], x[m + half])
     float va[PP], vb[PP];
-    load_row<T, PP, VEC>(x + m0, va);
-    load_row<T, PP, VEC>(x + half + m0, vb);
+    load_row<T, PP, VEC, NTX>(x + m0, va);
+    load_row<T, PP, VEC, NTX>(x + half + m0, vb);
 #pragma unroll
     for (int k = 0; k < PP; ++k) {
       const float a = va[k], b = vb[k];
       va[k] = __builtin_fmaf(a, c[k], -b * s[k]);
       vb[k] = __builtin_fmaf(a, s[k], b * c[k]);
     }
-    store_row<T, PP, VEC>(y + m0, va);
-    store_row<T, PP, VEC>(y + half + m0, vb);
+    store_row<T, PP, VEC, NTX>(y + m0, va);
+    store_row<T, PP, VEC, NTX>(y + half + m0, vb);
   }
 }
 
@@ -142,7 +178,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long item = t / tpr;
   if (item >= p.n_rows) return;
-  const int m0 = (int)(t % tpr) * PP;
+  const int j = (int)(t % tpr);
   const int h = (int)(item % p.H);
   const long long bs = item / p.H;
   const int s = (int)(bs % p.S);
@@ -151,7 +187,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
   const float* cs = p.table + (size_t)clamp_pos(pos, p.P) * p.Dh;
   const size_t row = (((size_t)b * p.H + h) * p.S + s) * p.Dh;
   rotate_pairs<T, PP, STYLE, VEC>(static_cast<const T*>(p.X) + row, static_cast<T*>(p.Y) + row,
-                                  cs, half, m0);
+                                  cs, half, j, tpr);
 }
 
 struct AppendRopeParams {
@@ -175,7 +211,7 @@ __global__ __launch_bounds__(256) void kv_append_rope_kernel(AppendRopeParams p)
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long item = t / tpr;
   if (item >= p.n_rows) return;
-  const int m0 = (int)(t % tpr) * PP;
+  const int j = (int)(t % tpr);
   const int rows = p.Snew - p.first;
   const int g = (int)(item % p.Nkv);
   const long long bi = item / p.Nkv;
@@ -194,20 +230,24 @@ __global__ __launch_bounds__(256) void kv_append_rope_kernel(AppendRopeParams p)
   const size_t src = (((size_t)b * p.Nkv + g) * p.Snew + i) * p.Dh;
   const size_t dst = (((size_t)b * p.Nkv + g) * p.Tcap + (size_t)slot) * p.Dh;
   rotate_pairs<T, PP, STYLE, VEC>(static_cast<const T*>(p.Knew) + src, static_cast<T*>(p.Kc) + dst,
-                                  p.table + (size_t)rpos * p.Dh, half, m0);
-  // V: this thread's share of the row, unchanged
+                                  p.table + (size_t)rpos * p.Dh, half, j, tpr);
+  // V: this thread's share of the row (2 * PP elements), unchanged; with
+  // vectors, thread j copies chunks j, j + tpr, ... as in the pairs layout
   const T* vs = static_cast<const T*>(p.Vnew) + src;
   T* vd = static_cast<T*>(p.Vc) + dst;
-  if constexpr (STYLE == 0) {
-    float v[2 * PP];
-    load_row<T, 2 * PP, VEC>(vs + 2 * m0, v);
-    store_row<T, 2 * PP, VEC>(vd + 2 * m0, v);
+  if constexpr (VEC) {
+    constexpr int E = 16 / sizeof(T);
+#pragma unroll
+    for (int u = 0; u < 2 * PP / E; ++u) {
+      const int ch = j + u * tpr;
+      float v[E];
+      load_row<T, E, true>(vs + ch * E, v);
+      store_row<T, E, true>(vd + ch * E, v);
+    }
   } else {
-    float v[PP];
-    load_row<T, PP, VEC>(vs + m0, v);
-    store_row<T, PP, VEC>(vd + m0, v);
-    load_row<T, PP, VEC>(vs + half + m0, v);
-    store_row<T, PP, VEC>(vd + half + m0, v);
+    float v[2 * PP];
+    load_row<T, 2 * PP, false>(vs + 2 * j * PP, v);
+    store_row<T, 2 * PP, false>(vd + 2 * j * PP, v);
   }
 }
 
