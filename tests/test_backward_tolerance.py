@@ -1,0 +1,54 @@
+"""Where the bf16 backward tolerance comes from (CPU only).
+
+The GPU backward differs from the exact gradients by the roundings its
+arithmetic requires, not by accumulation order alone: the forward output O is
+stored in bf16 and Delta = rowsum(dO * O) is formed from that stored O; the
+MFMA products take P and dS = P (dP - Delta) as bf16 operands; dQ, dK, dV are
+stored in bf16.  This test applies exactly those roundings, in float64, to the
+oracle's own forward and backward quantities and checks that the result stays
+within half of the bound the GPU parity test uses (|err| <= BF16_REL (1 + |ref|),
+mean <= BF16_MEAN), leaving the other half for fp32 accumulation order and the
+fp32 exponentials of the kernels.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from test_backward_gpu import BF16_MEAN, BF16_REL
+
+
+def _bf16(x):
+    return workloads.to_f64(workloads.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)), "bf16")
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window,seed", [
+    (1, 4, 2, 300, 128, 0, 1),
+    (1, 2, 2, 257, 64, 100, 2),
+])
+def test_emulated_roundings_fit_half_the_bound(B, Nq, Nkv, S, Dh, window, seed):
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=seed)
+    Q, K, V = (workloads.to_f64(a, "bf16") for a in (q, k, v))
+    dO = workloads.to_f64(workloads.draw((B, Nq, S, Dh), "bf16", seed, 3), "bf16")
+    dQ, dK, dV = oracle.backward_ref(Q, K, V, dO, causal=True, window=window)
+    O, L = oracle.attention_ref(Q, K, V, causal=True, window=window)
+    O_stored = _bf16(O)
+    scale = 1.0 / np.sqrt(Dh)
+    G = Nq // Nkv
+    ok = oracle.allowed_mask(np.arange(S), S, True, window)
+    eQ, eK, eV = np.zeros_like(dQ), np.zeros_like(dK), np.zeros_like(dV)
+    for b in range(B):
+        for h in range(Nq):
+            g = h // G
+            P = np.where(ok, np.exp(scale * Q[b, h] @ K[b, g].T - L[b, h][:, None]), 0.0)
+            delta = np.sum(dO[b, h] * O_stored[b, h], axis=1, keepdims=True)
+            dS = P * (dO[b, h] @ V[b, g].T - delta)
+            Pb, dSb = _bf16(P), _bf16(dS)  # MFMA operands
+            eV[b, g] += Pb.T @ dO[b, h]
+            eQ[b, h] = scale * dSb @ K[b, g]
+            eK[b, g] += scale * dSb.T @ Q[b, h]
+    for name, e, r in (("dQ", eQ, dQ), ("dK", eK, dK), ("dV", eV, dV)):
+        err = np.abs(_bf16(e) - r)
+        assert np.all(err <= 0.5 * BF16_REL * (1 + np.abs(r))), (name, float(np.max(err / (1 + np.abs(r)))))
+        assert err.mean() <= 0.5 * BF16_MEAN, (name, float(err.mean()))
