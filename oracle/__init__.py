@@ -15,6 +15,7 @@ from .attention import (
     attention_ref,
     attention_rows_ref,
     backward_ref,
+    backward_rows_ref,
     chunk_ref,
     decode_ref,
     head_attention,
@@ -31,6 +32,7 @@ __all__ = [
     "attention_ref",
     "attention_rows_ref",
     "backward_ref",
+    "backward_rows_ref",
     "chunk_ref",
     "decode_ref",
     "head_attention",

@@ -371,3 +371,60 @@ def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
             dQ[b, h] = scale * (dA @ K[b, g])
             dK[b, g] += scale * (dA.T @ Q[b, h])
     return dQ, dK, dV
+
+
+def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0, scale=None):
+    """Selected rows of the gradients of ``backward_ref``, for inputs too long
+    for the full score matrices.
+
+    q_rows: (b, h, i) triples -> dQ[b, h, i]; kv_rows: (b, g, j) triples ->
+    dK[b, g, j] and dV[b, g, j].  Same chain rule as ``backward_ref``, taken
+    one query row at a time: the row's weights P_i (``head_attention``), its
+    dP_i = V dO_i and dA_i = softmax_vjp(P_i, dP_i); dQ_i = scale * dA_i K,
+    and key j collects P_ij dO_i into dV_j and scale * dA_ij Q_i into dK_j
+    from every query row i of the group's heads that sees it.  Arrays may be
+    memory-mapped or lazily widened; only the rows used are read.
+    Returns (dQ_rows [len(q_rows), Dh], dK_rows, dV_rows [len(kv_rows), Dh]).
+    """
+    B, Nq, S, Dh = Q.shape
+    Nkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    group = Nq // Nkv
+    heads, rows = {}, {}
+
+    def head_kv(b, g):
+        if (b, g) not in heads:
+            heads[(b, g)] = (np.asarray(K[b, g], dtype=np.float64),
+                             np.asarray(V[b, g], dtype=np.float64))
+        return heads[(b, g)]
+
+    def row_grads(b, h, i):
+        if (b, h, i) not in rows:
+            Kb, Vb = head_kv(b, kv_head_of(h, Nq, Nkv))
+            q = np.asarray(Q[b, h, i], dtype=np.float64)[None, :]
+            _, _, P = head_attention(q, [i], Kb, Vb, causal, window, scale, return_probs=True)
+            dP = np.asarray(dO[b, h, i], dtype=np.float64)[None, :] @ Vb.T
+            rows[(b, h, i)] = (P[0], softmax_vjp(P, dP)[0])
+        return rows[(b, h, i)]
+
+    dQ = np.empty((len(q_rows), Dh))
+    for t, (b, h, i) in enumerate(q_rows):
+        _, dA = row_grads(b, h, i)
+        dQ[t] = scale * (dA @ head_kv(b, kv_head_of(h, Nq, Nkv))[0])
+    dK = np.zeros((len(kv_rows), Dh))
+    dV = np.zeros((len(kv_rows), Dh))
+    for t, (b, g, j) in enumerate(kv_rows):
+        # query rows that see key j: allowed_mask's rule along its column j
+        i_all = np.arange(S)
+        seen = np.ones(S, dtype=bool)
+        if causal:
+            seen &= j <= i_all
+        if window > 0:
+            seen &= (i_all - j) < window
+        for h in range(g * group, (g + 1) * group):
+            for i in np.flatnonzero(seen):
+                P, dA = row_grads(b, h, int(i))
+                dV[t] += P[j] * np.asarray(dO[b, h, i], dtype=np.float64)
+                dK[t] += scale * dA[j] * np.asarray(Q[b, h, i], dtype=np.float64)
+    return dQ, dK, dV

@@ -104,3 +104,50 @@ def test_backward_workspace_checked():
     with pytest.raises(tch.AttnError) as e:
         tch.attn_backward(t, t, t, t, t, L, t.clone(), t.clone(), t.clone(), workspace=small)
     assert e.value.status == tch.ATTN_EWORKSPACE
+
+
+class _Lazy:
+    """Widens slices of stored bf16 values to float64 on access."""
+
+    def __init__(self, arr):
+        self.arr, self.shape = arr, arr.shape
+
+    def __getitem__(self, idx):
+        return workloads.to_f64(self.arr[idx], "bf16")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("Nkv", [32, 8])
+def test_backward_full_size_sampled_rows(Nkv):
+    # the bench's backward shape (32768-token causal attention, 32 query heads,
+    # head size 128, MHA and GQA 32/8): seeded dQ rows anywhere plus rows 0 and
+    # S-1, and dK / dV rows of keys in the last tile (each seen by <= 64 queries
+    # per head), against the oracle's row form
+    B, Nq, S, Dh = 1, 32, 32768, 128
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
+    dO = workloads.draw((B, Nq, S, Dh), "bf16", 0, 3)
+    dev = device()
+    tq, tk, tv, tdo = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v, dO))
+    O, L = tch.prefill(tq, tk, tv)
+    dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo)
+    torch.cuda.synchronize()
+    qr = workloads.sample_rows(B, Nq, S, 10, seed=5, forced_rows=(0, S - 1))
+    kr = [(0, 0, S - 1), (0, Nkv // 2, S - 33), (0, Nkv - 1, S - 64)]
+    idx = lambda rows: tuple(torch.tensor(c, device=dev) for c in zip(*rows))
+    got = [workloads.to_f64(workloads.from_torch(t[idx(r)], "bf16"), "bf16")
+           for t, r in ((dQ, qr), (dK, kr), (dV, kr))]
+    del tq, tk, tv, tdo, O, L, dQ, dK, dV
+    ref = oracle.backward_rows_ref(_Lazy(q), _Lazy(k), _Lazy(v), _Lazy(dO), qr, kr)
+    # At this length the weights are ~1/S and the gradient rows are small
+    # (a last-tile key's dV is ~1e-5), so (1 + |ref|) would say little: each
+    # sampled row is held to the same relative bound against its own scale,
+    # floored at 1 % of the largest sampled row (query 0 sees only key 0, and
+    # its exact dQ is 0).
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        scale_row = np.maximum(np.abs(r).max(axis=1, keepdims=True), 1e-2 * np.abs(r).max())
+        ratio = np.abs(g - r) / scale_row
+        assert np.all(np.isfinite(g)), name
+        assert np.all(ratio <= BF16_REL), f"{name}: worst row-relative error {ratio.max():.3g}"
+        out.append(f"{name} {ratio.max():.2e}")
+    say(f"backward full size Nkv={Nkv}, row-relative: " + " ".join(out))

@@ -133,3 +133,19 @@ def test_causal_and_window_gradients_are_local():
         [Q[0, 0, S - 1] @ K[0, 0, j] for j in range(S - W, S)]) / 2.0
         - Q[0, 0, S - 1] @ K[0, 0, S - 1] / 2.0))
     np.testing.assert_allclose(dV[0, 0, S - 1], P_last * dO[0, 0, S - 1], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 3), (False, 0)])
+def test_backward_rows_equal_full_backward(causal, window):
+    # the row form used at long sequence lengths gives the full form's rows
+    from oracle import backward_rows_ref
+    B, Nq, Nkv, S, Dh = 2, 4, 2, 9, 5
+    Q, K, V = _rand((B, Nq, S, Dh), 21), _rand((B, Nkv, S, Dh), 22), _rand((B, Nkv, S, Dh), 23)
+    dO = _rand((B, Nq, S, Dh), 24)
+    dQ, dK, dV = backward_ref(Q, K, V, dO, causal=causal, window=window, scale=0.4)
+    qr = [(0, 0, 0), (1, 3, 8), (0, 2, 4), (1, 1, 5)]
+    kr = [(0, 0, 0), (1, 1, 8), (0, 1, 3), (1, 0, 6)]
+    rq, rk, rv = backward_rows_ref(Q, K, V, dO, qr, kr, causal=causal, window=window, scale=0.4)
+    np.testing.assert_allclose(rq, [dQ[t] for t in qr], atol=1e-13)
+    np.testing.assert_allclose(rk, [dK[t] for t in kr], atol=1e-13)
+    np.testing.assert_allclose(rv, [dV[t] for t in kr], atol=1e-13)
