@@ -309,3 +309,46 @@ def test_left_padded_generation_with_rope(style):
                      storage_allowance=True)
         assert np.all(Og[b, :, :r] == 0) and np.all(np.isneginf(Lg[b, :, :r]))
         say(f"padded generation {style} prompt {n}: {errs}")
+
+
+def test_bench_shapes_sampled_rows():
+    # the shapes bench.py --rope-padding times, on seeded sampled rows:
+    # RoPE in place on 32 x 32768 x 128 queries (half layout), and the padded
+    # prefill of 4 x 8192 tokens, 32/8 heads, left padding 0/1024/2048/4096
+    dev = device()
+    B, H, S, Dh = 1, 32, 32768, 128
+    x = workloads.draw((B, H, S, Dh), "bf16", 0, 0)
+    tx = workloads.to_torch(x, "bf16", dev)
+    tch.attn_rope(tx, tx, tch.rope_table(S, Dh, device=dev), style="half")
+    rows = workloads.sample_rows(B, H, S, 64, seed=7, forced_rows=(0, S - 1))
+    idx = tuple(torch.tensor(c, device=dev) for c in zip(*rows))
+    got = workloads.to_f64(workloads.from_torch(tx[idx], "bf16"), "bf16")
+    sel = np.stack([workloads.to_f64(x[b, h, i], "bf16") for b, h, i in rows])
+    ref = oracle.rope_ref(sel[None, None], np.array([[i for _, _, i in rows]]), style="half")[0, 0]
+    _check_rope(got, ref, "bf16", "rope, bench shape")
+    del tx
+
+    B, Nq, Nkv, S = 4, 32, 8, 8192
+    pads = [0, 1024, 2048, 4096]
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
+    m = workloads.key_mask(B, S, pads=pads)
+    tq, tk, tv = (workloads.to_torch(a, "bf16", dev) for a in (q, k, v))
+    O, L = tch.prefill(tq, tk, tv, key_mask=torch.from_numpy(m).to(dev))
+    rows = workloads.sample_rows(B, Nq, S, 256, seed=8,
+                                 forced_rows=(0, 1023, 1024, 2047, 2048, 4095, 4096, 8191))
+    idx = tuple(torch.tensor(c, device=dev) for c in zip(*rows))
+    Og = workloads.to_f64(workloads.from_torch(O[idx], "bf16"), "bf16")
+    Lg = L[idx].cpu().numpy().astype(np.float64)
+    del tq, tk, tv, O, L
+
+    class Lazy:
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def __getitem__(self, i):
+            return workloads.to_f64(self.a[i], "bf16")
+
+    Or, Lr = oracle.chunk_ref(Lazy(q), Lazy(k), Lazy(v), [S] * B, rows=rows, key_mask=m)
+    live, n_dead = _split_dead(Og, Lg, Or, Lr, "padded prefill, bench shape")
+    errs = check(Og[live], Lg[live], Or[live], Lr[live], "bf16", "padded prefill, bench shape")
+    say(f"bench shapes: padded prefill {len(rows)} rows ({n_dead} without keys): {errs}")
