@@ -182,6 +182,27 @@ def _cache_paths(torch, dev, tch, steps, warmup):
                       "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
                       "frac_of_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
                       "algorithmic_bytes": nbytes}), flush=True)
+    # one decode step with its append: fused (attn_decode_append) and as two launches
+    kn = torch.randn(B, Nkv, Dh, device=dev, dtype=torch.bfloat16)
+    vn = torch.randn_like(kn)
+    slot = (tl - 1).contiguous()
+    wsf = torch.empty(tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, T, tch.ATTN_BF16),
+                      dtype=torch.uint8, device=dev)
+    ms_fused = _time(torch, lambda: tch.attn_decode_append(tq, kn, vn, tk, tv, tl, slot, O, L, wsf),
+                     steps, warmup)
+    kn4, vn4 = kn[:, :, None].contiguous(), vn[:, :, None].contiguous()
+
+    def two_launches():
+        tch.attn_kv_append(kn4, vn4, tk, tv, slot)
+        tch.attn_decode_window(tq, tk, tv, tl, O, L, wsf)
+
+    ms_two = _time(torch, two_launches, steps, warmup)
+    _, dbytes = workloads.decode_work(lens, Nq, Nkv, Dh, 2)
+    print(json.dumps({"path": "attn_decode_append", "workload": f"{DECODE}, new K/V row appended "
+                      "in the same call", "ms": round(ms_fused, 4),
+                      "GB/s": round(dbytes / ms_fused / 1e6, 1),
+                      "two_launches_ms": round(ms_two, 4), "algorithmic_bytes": dbytes}), flush=True)
+
     # append of one token per sequence into the rolling buffer
     kn = torch.randn(B, Nkv, 1, Dh, device=dev, dtype=torch.bfloat16)
     vn = torch.randn_like(kn)

@@ -226,6 +226,32 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * attn_decode_append -- one decode step that also appends the new token's K
+ * and V (textbook, "Prefill и decode" and the generation walk-through: each
+ * step appends k, v to the cache and then attends over it), in one launch on
+ * the bf16 split-K path: the new rows are written to cache row slot[b] and the
+ * chunk that holds that row reads them from knew / vnew.
+ *
+ *   knew, vnew [B, Nkv, Dh]   the new token's K and V rows (already rotated,
+ *                             when RoPE is used)
+ *   slot [B] int32, DEVICE    cache row of the new token: lens[b] - 1 for a
+ *                             linear cache, position mod Tcap for a rolling
+ *                             buffer; rows outside [0, Tcap) are not written
+ *   lens [B] int32, DEVICE    keys the query sees, counting the new one
+ * The query must see row slot[b] (lens[b] - window <= slot[b] < lens[b]) for
+ * its own key to enter the softmax.  Every other argument, the workspace
+ * (attn_decode_window_workspace_bytes) and the errors are those of
+ * attn_decode_window.  fp32, head sizes other than 64/128/256, more than 32
+ * query heads per K/V head, or new rows not 16-byte aligned take two launches
+ * (attn_kv_append's kernel, then the decode) with the same result.
+ */
+int attn_decode_append(const void* q, const void* knew, const void* vnew, void* Kcache,
+                       void* Vcache, const int32_t* lens, const int32_t* slot, void* O,
+                       int B, int Nq, int Nkv, int Dh, int Tcap, int window, float scale,
+                       float* LSE, void* workspace, size_t workspace_bytes, int dtype,
+                       void* stream);
+
+/*
  * Key-padding masks (textbook, "Паддинг" under "Прямой проход по шагам": the
  * padding's key mask is added to the causal mask and the window, one mask per
  * batch row).  The attention entry points below take the mask as BITS: for a

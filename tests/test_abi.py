@@ -351,3 +351,28 @@ def _append_rope(**kw):
 ])
 def test_kv_append_rope_rejects(kw, code):
     assert _append_rope(**kw) == code
+
+
+def _decode_append(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, Kc=FAKE, Vc=FAKE, lens=FAKE, slot=FAKE, O=FAKE, B=4, Nq=32,
+             Nkv=8, Dh=128, Tcap=4096, window=0, scale=0.1, LSE=None, ws=None, wsb=0,
+             dtype=tch.ATTN_BF16)
+    a.update(kw)
+    return tch.lib().attn_decode_append(a["q"], a["kn"], a["vn"], a["Kc"], a["Vc"], a["lens"],
+                                        a["slot"], a["O"], a["B"], a["Nq"], a["Nkv"], a["Dh"],
+                                        a["Tcap"], a["window"], a["scale"], a["LSE"], a["ws"],
+                                        a["wsb"], a["dtype"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(slot=None), tch.ATTN_EINVAL),
+    (dict(kn=None), tch.ATTN_EINVAL),
+    (dict(Nkv=5), tch.ATTN_EGQA),
+    (dict(Tcap=0), tch.ATTN_EINVAL),
+    (dict(scale=-1.0), tch.ATTN_EINVAL),
+    (dict(Dh=512), tch.ATTN_EUNSUPPORTED),
+    (dict(), tch.ATTN_EWORKSPACE),           # the split-K decode needs its workspace
+])
+def test_decode_append_rejects(kw, code):
+    assert _decode_append(**kw) == code

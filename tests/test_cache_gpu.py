@@ -182,3 +182,64 @@ def test_generation_over_window_cache(mode):
         check(workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16"),
               L.cpu().numpy().astype(np.float64), Or[:, :, t], Lr[:, :, t], "bf16", (mode, t),
               storage_allowance=True)
+
+
+@pytest.mark.parametrize("dtype,B,Nq,Nkv,Dh,Tcap,lens,window,rolling,unaligned", [
+    ("bf16", 6, 32, 8, 128, 3000, [1, 31, 32, 33, 1792, 3000], 0, False, False),
+    ("bf16", 4, 16, 2, 64, 5000, [4097, 5000, 97, 1000], 100, False, False),
+    ("bf16", 3, 32, 1, 256, 2100, [1024, 1025, 2048], 0, False, False),     # MQA, Dh 256
+    ("bf16", 5, 32, 8, 128, 700, [700, 700, 350, 1, 699], 0, True, False),  # rolling buffer
+    ("bf16", 3, 8, 2, 128, 600, [600, 17, 250], 40, False, True),           # unaligned new rows
+    ("f32", 3, 4, 2, 64, 400, [400, 17, 250], 40, False, False),            # general kernels
+])
+def test_decode_append(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, rolling, unaligned):
+    # one decode step whose new K/V rows are appended in the same call: the
+    # cache must equal the oracle's append, and O / LSE must be bit-identical
+    # to attn_kv_append followed by the decode, and match the oracle
+    dev = device()
+    if rolling:   # a full buffer: every slot holds a key
+        lens = [Tcap] * B
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, dtype, seed=Dh,
+                                                lens=lens)
+    kn = workloads.draw((B, Nkv, 1, Dh), dtype, Dh, 21)
+    vn = workloads.draw((B, Nkv, 1, Dh), dtype, Dh, 22)
+    if rolling:   # token positions past the capacity: slot = position mod Tcap
+        slot = np.array([Tcap + 37 * b + 5 for b in range(B)]) % Tcap
+    else:
+        slot = lens_a - 1
+    tq, tk, tv = (workloads.to_torch(a, dtype, dev) for a in (q, kc, vc))
+    tk2, tv2 = tk.clone(), tv.clone()
+    tkn, tvn = (workloads.to_torch(a, dtype, dev) for a in (kn, vn))
+    if unaligned:  # the same values 2 bytes into a buffer: the two-launch path
+        buf = torch.zeros(2 * tkn.numel() + 8, dtype=tkn.dtype, device=dev)
+        buf[1:1 + tkn.numel()].copy_(tkn.reshape(-1))
+        buf[tkn.numel() + 3:2 * tkn.numel() + 3].copy_(tvn.reshape(-1))
+        tkn_u = buf[1:1 + tkn.numel()].view(B, Nkv, Dh)
+        tvn_u = buf[tkn.numel() + 3:2 * tkn.numel() + 3].view(B, Nkv, Dh)
+    else:
+        tkn_u, tvn_u = tkn[:, :, 0], tvn[:, :, 0]
+    tl = torch.from_numpy(np.asarray(lens_a, np.int32)).to(dev)
+    ts = torch.from_numpy(np.asarray(slot, np.int32)).to(dev)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+    nb = tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, tch._dtype_code(tq))
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    tch.attn_decode_append(tq, tkn_u, tvn_u, tk, tv, tl, ts, O, L, ws, window=window)
+    # the two-launch reference on the other copy
+    tch.attn_kv_append(tkn, tvn, tk2, tv2, ts, rolling=0)
+    O2, L2 = torch.empty_like(O), torch.empty_like(L)
+    tch.attn_decode_window(tq, tk2, tv2, tl, O2, L2, ws, window=window)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    # bit patterns: the caches hold NaN past each length
+    assert torch.equal(bits(tk), bits(tk2)) and torch.equal(bits(tv), bits(tv2))
+    assert torch.equal(O, O2) and torch.equal(L, L2)
+    Kr, Vr = oracle.append_ref(kc, vc, kn, vn, slot)  # bit-exact copy of the new rows
+    as_bits = lambda a: a.view(np.uint16) if dtype == "bf16" else a.astype(np.float32).view(np.uint32)
+    assert np.array_equal(as_bits(workloads.from_torch(tk, dtype)), as_bits(Kr))
+    assert np.array_equal(as_bits(workloads.from_torch(tv, dtype)), as_bits(Vr))
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, dtype), _Lazy(Kr, dtype), _Lazy(Vr, dtype),
+                               lens_a, window=window)
+    got = workloads.to_f64(workloads.from_torch(O, dtype), dtype)
+    say(f"decode_append {dtype} Dh={Dh} rolling={rolling} unaligned={unaligned}: "
+        f"{check(got, L.cpu().numpy().astype(np.float64), Or, Lr, dtype, lens, storage_allowance=True)}")

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
     attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype)
     attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype)
     attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None)
+    attn_decode_append(q, knew, vnew, Kcache, Vcache, lens, slot, O, LSE=None, workspace=None,
+                       window=0, scale=None, stream=None)
     attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
                   workspace=None, stream=None)
     attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype)
@@ -57,7 +59,7 @@ ATTN_F32 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
            "attn_decode_workspace_bytes", "attn_decode_window_workspace_bytes",
-           "attn_kv_append", "attn_backward", "attn_backward_workspace_bytes",
+           "attn_kv_append", "attn_decode_append", "attn_backward", "attn_backward_workspace_bytes",
            "attn_pack_key_mask", "attn_prefill_padded", "attn_prefill_cache_padded",
            "attn_decode_padded", "attn_rope_cos_sin", "attn_rope", "attn_kv_append_rope",
            "attn_strerror")
@@ -105,6 +107,9 @@ def lib():
         L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     i32, i32, f32, vp, ctypes.c_size_t, i32, vp]
         L.attn_backward.restype = i32
+        L.attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                         i32, f32, vp, vp, ctypes.c_size_t, i32, vp]
+        L.attn_decode_append.restype = i32
         L.attn_pack_key_mask.argtypes = [vp, i32, i32, vp, vp]
         L.attn_pack_key_mask.restype = i32
         L.attn_prefill_padded.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -305,6 +310,29 @@ def attn_decode_padded(q, Kcache, Vcache, lens, key_bits, O, LSE=None, workspace
                                   _dtype_code(q), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_padded")
+
+
+def attn_decode_append(q, knew, vnew, Kcache, Vcache, lens, slot, O, LSE=None, workspace=None,
+                       window=0, scale=None, stream=None):
+    """One decode step that writes knew / vnew ([B, Nkv, Dh]) to cache row slot[b]
+    (int32 [B] on the GPU) and attends over lens[b] keys, in one launch."""
+    import torch
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
+    if tuple(knew.shape) != (B, Nkv, Dh) or knew.shape != vnew.shape:
+        raise ValueError("knew and vnew must be [B, Nkv, Dh]")
+    if not (q.dtype == knew.dtype == vnew.dtype == Kcache.dtype):
+        raise ValueError("q, new rows and caches must share one dtype")
+    if slot.dtype != torch.int32 or tuple(slot.shape) != (B,):
+        raise ValueError("slot must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_append(_ptr(q), _ptr(knew), _ptr(vnew), _ptr(Kcache), _ptr(Vcache),
+                                  _ptr(lens), _ptr(slot), _ptr(O), B, Nq, Nkv, Dh, Tcap,
+                                  int(window), float(scale), _ptr(LSE), _ptr(workspace), ws_bytes,
+                                  _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_append")
 
 
 def attn_pack_key_mask(mask, key_bits, stream=None):

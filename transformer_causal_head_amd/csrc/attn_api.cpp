@@ -150,6 +150,39 @@ int attn_decode_padded(const void* q, const void* Kcache, const void* Vcache,
                      LSE, workspace, workspace_bytes, dtype, stream);
 }
 
+int attn_decode_append(const void* q, const void* knew, const void* vnew, void* Kcache,
+                       void* Vcache, const int32_t* lens, const int32_t* slot, void* O, int B,
+                       int Nq, int Nkv, int Dh, int Tcap, int window, float scale, float* LSE,
+                       void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !knew || !vnew || !Kcache || !Vcache || !lens || !slot || !O) return ATTN_EINVAL;
+  int st = validate_common(B, Nq, Nkv, Dh, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive(Tcap)) return ATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  if (window < 0) window = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype);
+  const int elem = dtype == ATTN_BF16 ? 2 : 4;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
+    if ((((uintptr_t)knew | (uintptr_t)vnew) % 16) == 0)  // one launch: append inside the decode
+      return from_hip(attn::launch_decode_bf16(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv, Dh,
+                                               Tcap, window, scale, nullptr, workspace, s, knew,
+                                               vnew, slot));
+    hipError_t e = attn::launch_kv_append(knew, vnew, Kcache, Vcache, slot, B, Nkv, 1, Dh, Tcap, 0,
+                                          elem, s);
+    if (e != hipSuccess) return ATTN_EHIP;
+    return from_hip(attn::launch_decode_bf16(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv, Dh, Tcap,
+                                             window, scale, nullptr, workspace, s));
+  }
+  // general kernels: the append, then the decode rows
+  hipError_t e = attn::launch_kv_append(knew, vnew, Kcache, Vcache, slot, B, Nkv, 1, Dh, Tcap, 0,
+                                        elem, s);
+  if (e != hipSuccess) return ATTN_EHIP;
+  return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap, lens,
+                                            nullptr, 1, window, scale, dtype == ATTN_BF16, s));
+}
+
 int attn_pack_key_mask(const uint8_t* mask, int B, int T, uint64_t* key_bits, void* stream) {
   if (!mask || !key_bits || !positive(B) || !positive(T)) return ATTN_EINVAL;
   return from_hip(attn::launch_pack_key_mask(mask, B, T, key_bits,

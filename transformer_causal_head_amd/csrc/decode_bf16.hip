@@ -80,6 +80,13 @@ struct DecParams {
   const int32_t* lens;
   const uint64_t* kbits;  // key-padding mask, one bit per cache slot (kwords words per sequence)
   int kwords;
+  // decode with append: the new token's K and V rows ([B, Nkv, D]) go to
+  // cache row slot[b]; the chunk holding that row reads them from here
+  const __bf16* knew;
+  const __bf16* vnew;
+  const int32_t* slot;
+  __bf16* Kw;  // the caches, written
+  __bf16* Vw;
   __bf16* O;
   float* LSE;
   float* ws_o;    // [B, Nkv, n_slots, G, D] unnormalised partial outputs
@@ -133,8 +140,8 @@ __device__ __forceinline__ void wait_vm() {
 
 // NB blocks of 16 query heads per K/V head (G <= 16 * NB).  KM: a key-padding
 // mask is given (p.kbits); without it the kernel is compiled as if it did not
-// exist.
-template <int D, int NB, bool KM>
+// exist.  APP: the new token's K and V rows are appended in the same launch.
+template <int D, int NB, bool KM, bool APP = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   using geo = DGeo<D>;
   constexpr int STAGE = geo::STAGE;
@@ -160,7 +167,41 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // workgroup x takes the x-th chunk from the one holding key lo
   const int chunk = lo / p.ch + blockIdx.x;
   const int c0 = chunk * p.ch;
-  if (c0 >= n) return;
+
+  // append: lane l < NC holds 16 bytes of the new K row, NC <= l < 2 NC of the
+  // new V row (loaded before any copy, so the copy waits cover it).  Workgroup
+  // 0 of (sequence, K/V head) writes them to cache row slot[b]; the chunk that
+  // holds that row (if the query sees it) copies the cache as usual and then
+  // overwrites that row of its LDS stage with them, so no workgroup uses the
+  // row being written.
+  constexpr int NCH = D / 8;
+  u32x4 new_row = {};
+  int alt_row = -1;
+  if constexpr (APP) {
+    const size_t nrow = ((size_t)b * p.Nkv + g) * D;
+    const int l = threadIdx.x;
+    if (l < NCH)
+      new_row = *reinterpret_cast<const u32x4*>(p.knew + nrow + l * 8);
+    else if (l < 2 * NCH)
+      new_row = *reinterpret_cast<const u32x4*>(p.vnew + nrow + (l - NCH) * 8);
+    const int sl = p.slot[b];
+    if (sl >= max(lo, c0) && sl < min(n, c0 + p.ch)) alt_row = sl;
+  }
+  auto write_new_row = [&]() {
+    if constexpr (APP) {
+      const int sl = p.slot[b];
+      const int l = threadIdx.x;
+      if (blockIdx.x == 0 && sl >= 0 && sl < p.Tcap && l < 2 * NCH) {
+        __bf16* dst = (l < NCH ? p.Kw : p.Vw) + (((size_t)b * p.Nkv + g) * p.Tcap + sl) * D;
+        *reinterpret_cast<u32x4*>(dst + (l % NCH) * 8) = new_row;
+      }
+    }
+  };
+  if (c0 >= n) {
+    write_new_row();
+    return;
+  }
+
   int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
   int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
   const int last = min(n, c0 + p.ch) - 1;
@@ -343,17 +384,40 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // Steps in pairs from s0: the first of a pair uses stage 0, the second stage
   // 1.  Before step s the copies of steps s and s + 1 are outstanding; once
   // step s has read its stage, the copies of step s + 2 go into it.
+  // APP: after step s's copies have landed, put the new row into its stage
+  auto substitute = [&](int s, lds_char* kst, lds_char* vst) {
+    if constexpr (APP) {
+      const int r = alt_row - (c0 + s * STEP);
+      const int l = threadIdx.x;
+      if (r >= 0 && r < STEP && l < 2 * NCH) {  // r is wave-uniform
+        const bool isk = l < NCH;
+        const int c = isk ? l : l - NCH;
+        const int off = (r / geo::RP) * 1024 +
+                        ((r % geo::RP) * NCH + (c ^ (isk ? kswz<D>(r) : vswz<D>(r)))) * 16;
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        *(lds_u32x4*)((isk ? kst : vst) + off) = new_row;
+      }
+      // the step's operand reads use other pointer types: keep them after the store
+      __asm__ __volatile__("" ::: "memory");
+    }
+  };
+
   for (int s = s0; s < nsteps; s += 2) {
     wait_vm<PER_STEP>();
+    substitute(s, K0, V0);
     step(s, K0, V0);
     load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
     load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
     wait_vm<PER_STEP>();
-    if (s + 1 < nsteps) step(s + 1, K1, V1);
+    if (s + 1 < nsteps) {
+      substitute(s + 1, K1, V1);
+      step(s + 1, K1, V1);
+    }
     load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
     load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
   }
   wait_vm<0>();  // no copy may still target LDS when the wave ends
+  write_new_row();
 
   // partial of this chunk: O^T register r of block db is d = 16*db + 4*grp + r
   // of query column l16
@@ -480,10 +544,10 @@ DecodePlan decode_plan(int B, int Nkv, int Tcap, int window) {
   return d;
 }
 
-template <int D, int NB, bool KM>
+template <int D, int NB, bool KM, bool APP = false>
 hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM>), dim3(p.n_slots, p.Nkv, p.B), dim3(64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM, APP>), dim3(p.n_slots, p.Nkv, p.B), dim3(64),
+                     0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Nq;
@@ -492,6 +556,7 @@ hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
 }
 template <int D, int NB>
 hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
+  if (p.knew) return launch_decode_km<D, NB, false, true>(p, stream);  // append (no key mask)
   return p.kbits ? launch_decode_km<D, NB, true>(p, stream) : launch_decode_km<D, NB, false>(p, stream);
 }
 }  // namespace
@@ -505,9 +570,15 @@ size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int windo
 hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
                               void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
                               int window, float scale, const uint64_t* kbits, void* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, const void* knew, const void* vnew,
+                              const int32_t* slot) {
   const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
   DecParams p;
+  p.knew = static_cast<const __bf16*>(knew);
+  p.vnew = static_cast<const __bf16*>(vnew);
+  p.slot = slot;
+  p.Kw = static_cast<__bf16*>(const_cast<void*>(Kc));
+  p.Vw = static_cast<__bf16*>(const_cast<void*>(Vc));
   p.q = static_cast<const __bf16*>(q);
   p.K = static_cast<const __bf16*>(Kc);
   p.V = static_cast<const __bf16*>(Vc);

@@ -38,10 +38,14 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
 bool decode_bf16_supported(int Nq, int Nkv, int Dh);
 int decode_bf16_chunk(int B, int Nkv, int L);
 size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window);
+// With knew / vnew / slot (no key mask then): the new token's K and V rows
+// [B, Nkv, Dh] are written to cache row slot[b] in the same launch (16-byte
+// aligned rows), and the chunk that holds that row reads them from knew/vnew.
 hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
                               void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
                               int window, float scale, const uint64_t* kbits, void* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, const void* knew = nullptr,
+                              const void* vnew = nullptr, const int32_t* slot = nullptr);
 
 // Copy Snew new K and V rows per (sequence, K/V head) into the caches at
 // positions pos[b] .. pos[b] + Snew - 1, or at those positions modulo Tcap
