@@ -12,7 +12,9 @@
 //                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
 //                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
 //                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
-//   dkv_kernel -- one wavefront per 32 keys of one K/V head, streaming the Q and
+//   dkv_kernel -- (head size 64; head size 128 uses dkv_split_kernel below,
+//                 which puts dV and dK on different wavefronts)
+//                 one wavefront per 32 keys of one K/V head, streaming the Q and
 //                 dO tiles of every query head of its group over the queries
 //                 that see those keys:
 //                   S  = Q K^T       (A: Q tile rows,  B: K in VGPRs)
@@ -28,6 +30,12 @@
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
+
+// dK / dV at head size 128: one wave per key block (0) or split over two
+// waves (1).  Head size 64 always uses one wave (the split is slower there).
+#ifndef BWD_SPLIT
+#define BWD_SPLIT 1
+#endif
 
 namespace attn {
 
@@ -402,6 +410,201 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     }
 }
 
+// dK, dV with the two gradients on different wavefronts: a workgroup of 8
+// waves holds 128 keys of one K/V head; waves 0-3 compute S, P and dV for 32
+// keys each (K fragments and one accumulator), waves 4-7 compute S, dP, dS and
+// dK for the same keys (K and V fragments and one accumulator).  S is
+// computed twice (five products per visible pair instead of four), but each
+// wave fits in 256 registers, so two waves share a SIMD and one's
+// exponentials overlap the other's MFMAs.
+template <int D>
+__global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
+  using geo = Geo<D>;
+  constexpr int NW = 8;
+  constexpr int KS = geo::KS;
+  constexpr int DB = geo::DB;
+  constexpr int KB = 128;  // keys per workgroup
+  __shared__ __attribute__((aligned(1024))) char q0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char q1s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char o0s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char o1s[geo::TILE];
+  __shared__ __attribute__((aligned(256))) float a0s[2 * BN];
+  __shared__ __attribute__((aligned(256))) float a1s[2 * BN];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool krole = w >= 4;  // wave-uniform: dK (true) or dV
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hl = lane >> 5;
+
+  const int n_kb = (p.S + KB - 1) / KB;
+  const int kt = blockIdx.x % n_kb;
+  const int bg = blockIdx.x / n_kb;
+  const int g = bg % p.Nkv;
+  const int b = bg / p.Nkv;
+
+  const int k0 = kt * KB;
+  const int k1 = min(p.S, k0 + KB);
+  const int kw0 = k0 + (w & 3) * 32;  // this wave's first key
+  const int kw1 = min(p.S, kw0 + 32);
+  const bool wave_live = kw0 < p.S;
+  const size_t kv_row0 = ((size_t)b * p.Nkv + g) * (size_t)p.S;
+
+  const int qlo = p.causal ? k0 : 0;
+  const int qhi = (p.causal && p.window > 0) ? min(p.S, k1 - 1 + p.window) : p.S;
+  const int t_lo = qlo / BN;
+  const int n_qt = (qhi + BN - 1) / BN - t_lo;
+  const int n_items = p.G * max(n_qt, 0);
+
+  auto issue = [&](int item, char* qdst, char* odst, float* adst) {
+    const int hh = item / n_qt;
+    const int q0 = (t_lo + item % n_qt) * BN;
+    const size_t row0 = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S;
+    load_tile<D, NW>(head_ref<D>(p.Q + row0 * D, p.S), q0, qdst, w, lane);
+    load_tile<D, NW>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, w, lane);
+    if (w < 2) {
+      const float* src = (w == 0 ? p.LSE : p.delta) + row0;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.S * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(adst + w * BN), 4, (q0 + lane) * 4,
+                                               0, 0, 0);
+    }
+  };
+  if (n_items > 0) issue(0, q0s, o0s, a0s);
+
+  const int kj = min(kw0 + ln, p.S - 1);
+  bf16x8 kf[KS], vf[KS];
+  {
+    const bf16x8* ks_ = reinterpret_cast<const bf16x8*>(p.K + (kv_row0 + kj) * D + hl * 8);
+    const bf16x8* vs_ = reinterpret_cast<const bf16x8*>(p.V + (kv_row0 + kj) * D + hl * 8);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = ks_[ks * 2];
+      vf[ks] = krole ? vs_[ks * 2] : bf16x8{};
+    }
+  }
+
+  int roff[KS];
+  row_operand_offsets<D>(ln, hl, roff);
+  int troff[2][DB];
+  tr_operand_offsets<D>(lane, troff);
+
+  f32x16 acc[DB];  // dV (waves 0-3) or dK / scale (waves 4-7)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  for (int it = 0; it < n_items; ++it) {
+    const int q0 = (t_lo + it % n_qt) * BN;
+    const char* Qt = (it & 1) ? q1s : q0s;
+    const char* Ot = (it & 1) ? o1s : o0s;
+    const float* At = (it & 1) ? a1s : a0s;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (it + 1 < n_items)
+      issue(it + 1, (it & 1) ? q0s : q1s, (it & 1) ? o0s : o1s, (it & 1) ? a0s : a1s);
+    bool live = wave_live && q0 < p.S;
+    if (p.causal) live = live && q0 + BN - 1 >= kw0;
+    if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
+    if (!live) continue;
+    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
+    if (p.causal) full = full && q0 >= kw1 - 1;
+    if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
+
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+      }
+      // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln
+      float lse2[16];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lse2[a * 4 + u] = l4[u] * kLog2e;
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
+        }
+      }
+      if (!krole) {
+        // dV^T += dO^T P
+        bf16x8 pf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 pp;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r0 = kk * 8 + 2 * j;
+            pp[j] = pack_bf16x2(exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0])),
+                                exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1])));
+          }
+          pf[kk] = __builtin_bit_cast(bf16x8, pp);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 oa = read_tr_operand<D>(Ot, mb * 2 + kk, troff, db);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[kk], acc[db], 0, 0, 0);
+          }
+      } else {
+        // dP = dO V^T, dS = P (dP - Delta), dK^T += Q^T dS
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+        }
+        bf16x8 sf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 ss;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r0 = kk * 8 + 2 * j;
+            const int a = r0 >> 2;
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
+            const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0]));
+            const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1]));
+            ss[j] = pack_bf16x2(p0 * (dp[r0] - d4[r0 & 3]), p1 * (dp[r0 + 1] - d4[(r0 + 1) & 3]));
+          }
+          sf[kk] = __builtin_bit_cast(bf16x8, ss);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 qa = read_tr_operand<D>(Qt, mb * 2 + kk, troff, db);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf[kk], acc[db], 0, 0, 0);
+          }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  if (!wave_live || kw0 + ln >= p.S) return;
+  __bf16* row = (krole ? p.dK : p.dV) + (kv_row0 + kw0 + ln) * D;
+  const float f = krole ? p.scale : 1.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d0 = db * 32 + a4 * 8 + hl * 4;
+      u32x2 st;
+      st[0] = pack_bf16x2(acc[db][a4 * 4 + 0] * f, acc[db][a4 * 4 + 1] * f);
+      st[1] = pack_bf16x2(acc[db][a4 * 4 + 2] * f, acc[db][a4 * 4 + 3] * f);
+      *reinterpret_cast<u32x2*>(row + d0) = st;
+    }
+}
+
 template <int D>
 hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   constexpr int NWQ = 8;  // dQ waves per workgroup
@@ -412,12 +615,17 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   p.qspan = (NWQ / p.hp) * 32;
   p.n_qtiles = (p.S + p.qspan - 1) / p.qspan;
   const long long nq = (long long)p.n_qtiles * p.B * p.Nkv * p.n_hsub;
-  const long long nk = (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
+  constexpr bool split = BWD_SPLIT && D == 128;
+  const long long nk = split ? (long long)((p.S + 127) / 128) * p.B * p.Nkv
+                             : (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)nq), dim3(NWQ * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
+  if (split)
+    hipLaunchKernelGGL((dkv_split_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
   return hipGetLastError();
 }
 
