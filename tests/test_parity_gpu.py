@@ -251,28 +251,30 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
     check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, Tcap, lens), storage_allowance=True)
 
 
-def _decode_chunk(B, Nkv, Tcap):
+def _decode_chunk(B, Nkv, Tcap, G):
     # the host's choice of keys per chunk, restated: the longest candidate that
-    # gives at least 2048 (sequence, K/V head, chunk) items at full length
+    # gives at least 2048 (sequence, K/V head, chunk) items at full length,
+    # 1024 with 16 or more query heads per K/V head
     for ch in (1792, 1152, 896, 640, 384, 224, 160, 96):
-        if B * Nkv * -(-Tcap // ch) >= 2048:
+        if B * Nkv * -(-Tcap // ch) >= (1024 if G >= 16 else 2048):
             return ch
     return 96
 
 
-@pytest.mark.parametrize("B,Nkv,Tcap,ch", [
-    (16, 8, 3000, 160),
-    (16, 8, 4000, 224),
-    (16, 8, 8192, 384),
-    (16, 8, 12000, 640),
-    (16, 8, 16384, 896),
-    (24, 8, 16384, 1152),
+@pytest.mark.parametrize("B,Nq,Nkv,Tcap,ch", [
+    (16, 32, 8, 3000, 160),
+    (16, 32, 8, 4000, 224),
+    (16, 32, 8, 8192, 384),
+    (16, 32, 8, 12000, 640),
+    (16, 32, 8, 16384, 896),
+    (24, 32, 8, 16384, 1152),
+    (16, 32, 2, 16384, 384),    # 16 query heads per K/V head: 1024 items
+    (64, 32, 1, 32768, 1792),   # MQA with 32 query heads
 ])
-def test_decode_chunk_sizes(B, Nkv, Tcap, ch):
+def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch):
     # every chunk length the host can pick, with lengths on and around chunk
     # edges; the workspace size shows which chunk length was taken
-    Nq = 32
-    assert _decode_chunk(B, Nkv, Tcap) == ch
+    assert _decode_chunk(B, Nkv, Tcap, Nq // Nkv) == ch
     ws = tch.attn_decode_workspace_bytes(B, Nq, Nkv, 128, Tcap, tch.ATTN_BF16)
     assert ws == B * Nq * -(-Tcap // ch) * (128 + 2) * 4
     rng = np.random.default_rng(Tcap + B)

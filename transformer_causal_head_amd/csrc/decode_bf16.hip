@@ -516,16 +516,21 @@ bool decode_bf16_supported(int Nq, int Nkv, int Dh) {
 }
 
 // Keys per chunk: the longest candidate that still gives the grid at least
-// 2048 (sequence, K/V head, chunk) items when every sequence has L visible
-// keys (L = Tcap, or the window when it is shorter).  The candidates are
-// multiples of 32 keys, none a power of two.
-int decode_bf16_chunk(int B, int Nkv, int L) {
+// 2048 (sequence, K/V head, chunk) items -- 1024 for 16 or more query heads
+// per K/V head -- when every sequence has L visible keys (L = Tcap, or the
+// window when it is shorter).  The candidates are multiples of 32 keys, none
+// a power of two.
+int decode_bf16_chunk(int B, int Nkv, int L, int G) {
   // at most 64 steps per chunk: the key-padding trim tests one step per lane
   static const int kChunks[] = {1792, 1152, 896, 640, 384, 224, 160, 96};
   static_assert(1792 <= 64 * STEP, "a chunk must fit one wavefront of steps");
+  // each chunk writes G x (Dh + 2) fp32 partials that the merge reads back;
+  // with 16 or more query heads per K/V head that is several percent of a
+  // short chunk's K/V bytes, so those groups take half the item count
+  const long long min_items = G >= 16 ? 1024 : 2048;
   const long long heads = (long long)B * Nkv;
   for (int ch : kChunks)
-    if (heads * ((L + ch - 1) / ch) >= 2048) return ch;
+    if (heads * ((L + ch - 1) / ch) >= min_items) return ch;
   return kChunks[sizeof(kChunks) / sizeof(kChunks[0]) - 1];
 }
 
@@ -534,10 +539,10 @@ namespace {
 struct DecodePlan {
   int ch, n_slots;
 };
-DecodePlan decode_plan(int B, int Nkv, int Tcap, int window) {
+DecodePlan decode_plan(int B, int Nq, int Nkv, int Tcap, int window) {
   const int L = (window > 0 && window < Tcap) ? window : Tcap;
   DecodePlan d;
-  d.ch = decode_bf16_chunk(B, Nkv, L);
+  d.ch = decode_bf16_chunk(B, Nkv, L, Nq / Nkv);
   const int all = (Tcap + d.ch - 1) / d.ch;
   // a window of L keys starting anywhere touches at most ceil(L / ch) + 1 chunks
   d.n_slots = L < Tcap ? std::min(all, (L + d.ch - 1) / d.ch + 1) : all;
@@ -562,7 +567,7 @@ hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
-  const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
+  const DecodePlan d = decode_plan(B, Nq, Nkv, Tcap, window);
   const size_t parts = (size_t)B * Nq * d.n_slots;  // B * Nkv * n_slots * G
   return parts * Dh * sizeof(float) + parts * 2 * sizeof(float);
 }
@@ -572,7 +577,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
                               int window, float scale, const uint64_t* kbits, void* ws,
                               hipStream_t stream, const void* knew, const void* vnew,
                               const int32_t* slot) {
-  const DecodePlan d = decode_plan(B, Nkv, Tcap, window);
+  const DecodePlan d = decode_plan(B, Nq, Nkv, Tcap, window);
   DecParams p;
   p.knew = static_cast<const __bf16*>(knew);
   p.vnew = static_cast<const __bf16*>(vnew);

@@ -36,7 +36,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
 // 256, up to 32 query heads per K/V head.  The query of sequence b sees keys
 // max(0, lens[b] - window) .. lens[b] - 1 (window 0: all of them).
 bool decode_bf16_supported(int Nq, int Nkv, int Dh);
-int decode_bf16_chunk(int B, int Nkv, int L);
+int decode_bf16_chunk(int B, int Nkv, int L, int G);
 size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window);
 // With knew / vnew / slot (no key mask then): the new token's K and V rows
 // [B, Nkv, Dh] are written to cache row slot[b] in the same launch (16-byte
