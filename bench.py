@@ -42,11 +42,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # FETCH_SIZE unit = 2047.9 bytes, one WRITE_SIZE unit = 1024 bytes); valid only
 # for the kernel source it was taken on (sha256[:16] of the .hip file).
 TRAFFIC = {
-    "prefill_bf16.hip": {"f884b453a75b2b3a": 5297900052,   # 5.025e9 fetched + 2.726e8 written
-                         "7176b81b1d0fbaee": 5444386499},  # 5.172e9 fetched + 2.727e8 written
+    "prefill_bf16.hip": {"40cd74c95da77142": 5288144616},  # 5.015e9 fetched + 2.727e8 written
     # partial + merge kernels
-    "decode_bf16.hip": {"bdec2559054b8cb5": 4539851941,    # 4.529e9 fetched + 1.131e7 written
-                        "4a2b04c1474c0f3d": 4539988760},   # 4.529e9 fetched + 1.131e7 written
+    "decode_bf16.hip": {"5167baa2332c6c3d": 4539968102},   # 4.529e9 fetched + 1.131e7 written
 }
 
 
