@@ -96,6 +96,29 @@ def test_backward_deterministic():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("Nkv,Dh", [(32, 128), (8, 128), (32, 64)])
+def test_backward_repeat_bitwise_long(Nkv, Dh):
+    # dK / dV at head size 128 pass the weights from one wavefront to another
+    # through LDS; three calls on an 8192-token causal input give the same bits
+    B, Nq, S = 1, 32, 8192
+    dev = device()
+    g = torch.Generator(device=dev).manual_seed(Nkv + Dh)
+    tq = torch.randn(B, Nq, S, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    tk = torch.randn(B, Nkv, S, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    tv = torch.randn(B, Nkv, S, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    tdo = torch.randn(B, Nq, S, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    O, L = tch.prefill(tq, tk, tv)
+    runs = []
+    for _ in range(3):
+        grads = tch.backward(tq, tk, tv, O, L, tdo)
+        torch.cuda.synchronize()
+        runs.append([x.view(torch.int16).clone() for x in grads])
+    for r in runs[1:]:
+        for a, b in zip(r, runs[0]):
+            assert torch.equal(a, b)
+
+
 def test_backward_workspace_checked():
     dev = device()
     t = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16, device=dev)

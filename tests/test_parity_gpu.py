@@ -332,6 +332,48 @@ def test_decode_equals_prefill_row():
         np.testing.assert_allclose(Ld, Lp[:, :, t - 1], atol=2e-3)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("Dh,Nkv,window,append", [
+    (64, 8, 0, False), (128, 8, 0, False), (256, 8, 0, False), (128, 1, 0, False),
+    (128, 8, 4096, False), (128, 8, 0, True), (64, 8, 0, True),
+])
+def test_decode_repeat_bitwise_full_size(Dh, Nkv, window, append):
+    # The split-K decode kernel streams each chunk through two LDS stages with
+    # no workgroup barrier, so a copy into a stage must wait for that stage's
+    # reads; a copy that overtook them would change the rows it raced on from
+    # one call to the next.  At the decode workload's size (64 sequences, 32
+    # query heads, cached lengths 1024..32768) five calls give the same bits,
+    # also with a window and with the append fused into the call.
+    B, Nq, Tcap = 64, 32, 32768
+    dev = device()
+    lens = np.random.default_rng(0).integers(1024, Tcap, B, endpoint=True).astype(np.int32)
+    g = torch.Generator(device=dev).manual_seed(Dh * 10 + Nkv)
+    kc = torch.randn(B, Nkv, Tcap, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    vc = torch.randn(B, Nkv, Tcap, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    q = torch.randn(B, Nq, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+    tl = torch.from_numpy(lens).to(dev)
+    O = torch.empty_like(q)
+    L = torch.empty(B, Nq, device=dev)
+    ws = torch.empty(tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, 0),
+                     dtype=torch.uint8, device=dev)
+    if append:
+        kn = torch.randn(B, Nkv, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+        vn = torch.randn(B, Nkv, Dh, device=dev, dtype=torch.bfloat16, generator=g)
+        slot = (tl - 1).to(torch.int32)
+        call = lambda: tch.attn_decode_append(q, kn, vn, kc, vc, tl, slot, O, L, workspace=ws)
+    else:
+        call = lambda: tch.attn_decode_window(q, kc, vc, tl, O, L, workspace=ws, window=window)
+    outs = []
+    for _ in range(5):
+        call()
+        torch.cuda.synchronize()
+        outs.append((O.view(torch.int16).clone(), L.view(torch.int32).clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    assert torch.isfinite(O.float()).all()
+    say(f"decode repeat Dh={Dh} Nkv={Nkv} window={window} append={append}: 5 calls bit-identical")
+
+
 def test_decode_deterministic_and_workspace_checked():
     lens, q, kc, vc = workloads.decode_inputs(8, 32, 8, 128, 4096, 1, 4096, seed=4)
     O1, L1 = run_decode(q, kc, vc, lens, "bf16")

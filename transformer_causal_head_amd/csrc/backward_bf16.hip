@@ -12,7 +12,7 @@
 //                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
 //                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
 //                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
-//   dkv_kernel -- (head size 64; head size 128 uses dkv_split_kernel below,
+//   dkv_kernel -- (head size 64; head size 128 uses dkv_pair_kernel below,
 //                 which puts dV and dK on different wavefronts)
 //                 one wavefront per 32 keys of one K/V head, streaming the Q and
 //                 dO tiles of every query head of its group over the queries
@@ -31,10 +31,14 @@
 #include "kernels.h"
 #include "tiles.h"
 
-// dK / dV at head size 128: one wave per key block (0) or split over two
-// waves (1).  Head size 64 always uses one wave (the split is slower there).
-#ifndef BWD_SPLIT
-#define BWD_SPLIT 1
+// dK / dV on two wavefronts per 32 keys with the weights passed through LDS
+// (dkv_pair_kernel, 1) or on one wavefront per 32 keys (dkv_kernel, 0), at
+// head size 128 and at head size 64.
+#ifndef BWD_PAIR128
+#define BWD_PAIR128 1
+#endif
+#ifndef BWD_PAIR64
+#define BWD_PAIR64 0
 #endif
 
 namespace attn {
@@ -154,17 +158,18 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
   tf_lo = __builtin_amdgcn_readfirstlane(tf_lo);
   tf_hi = __builtin_amdgcn_readfirstlane(tf_hi);
 
-  for (int i = 0; i < nt; ++i) {
+  // tile i reads stage (Kt, Vt) and copies tile i + 1 into the other stage;
+  // the loop below passes the stages as fixed LDS objects so that the
+  // compiler can tell the copies in flight from the tile being read
+  auto step = [&](int i, const char* Kt, const char* Vt, char* Kn, char* Vn) {
     const int t = t_lo + i;
-    const char* Kt = (i & 1) ? k1s : k0s;
-    const char* Vt = (i & 1) ? v1s : v0s;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this tile's copies have landed
     __syncthreads();
     if (i + 1 < nt) {
-      load_tile<D, NW>(Kh, (t + 1) * BN, (i & 1) ? k0s : k1s, w, lane);
-      load_tile<D, NW>(Vh, (t + 1) * BN, (i & 1) ? v0s : v1s, w, lane);
+      load_tile<D, NW>(Kh, (t + 1) * BN, Kn, w, lane);
+      load_tile<D, NW>(Vh, (t + 1) * BN, Vn, w, lane);
     }
-    if (t < tl_lo || t > tl_hi) continue;
+    if (t < tl_lo || t > tl_hi) return;
     const bool need_mask = t < tf_lo || t > tf_hi;
     const int k0 = t * BN;
 #pragma unroll
@@ -209,7 +214,13 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
           dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], dq[db], 0, 0, 0);
         }
     }
+  };
+  int i = 0;
+  for (; i + 1 < nt; i += 2) {
+    step(i, k0s, v0s, k1s, v1s);
+    step(i + 1, k1s, v1s, k0s, v0s);
   }
+  if (i < nt) step(i, k0s, v0s, k1s, v1s);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS when the wave ends
 
   if (!wave_live || qa + ln >= p.S) return;
@@ -313,20 +324,19 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     dv[db] = f32x16{};
   }
 
-  for (int it = 0; it < n_items; ++it) {
+  // item `it` reads stage (Qt, Ot, At) and copies item it + 1 into the other
+  // stage (fixed LDS objects, as in dq_kernel)
+  auto item = [&](int it, const char* Qt, const char* Ot, const float* At, char* Qn, char* On,
+                  float* An) {
     const int q0 = (t_lo + it % n_qt) * BN;
-    const char* Qt = (it & 1) ? q1s : q0s;
-    const char* Ot = (it & 1) ? o1s : o0s;
-    const float* At = (it & 1) ? a1s : a0s;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (it + 1 < n_items)
-      issue(it + 1, (it & 1) ? q0s : q1s, (it & 1) ? o0s : o1s, (it & 1) ? a0s : a1s);
+    if (it + 1 < n_items) issue(it + 1, Qn, On, An);
     // does this wave see any (query, key) pair of the tile?  all of them?
     bool live = wave_live && q0 < p.S;
     if (p.causal) live = live && q0 + BN - 1 >= kw0;
     if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
-    if (!live) continue;
+    if (!live) return;
     bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
     if (p.causal) full = full && q0 >= kw1 - 1;
     if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
@@ -389,7 +399,13 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf[kk], dk[db], 0, 0, 0);
         }
     }
+  };
+  int it = 0;
+  for (; it + 1 < n_items; it += 2) {
+    item(it, q0s, o0s, a0s, q1s, o1s, a1s);
+    item(it + 1, q1s, o1s, a1s, q0s, o0s, a0s);
   }
+  if (it < n_items) item(it, q0s, o0s, a0s, q1s, o1s, a1s);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (!wave_live || kw0 + ln >= p.S) return;
@@ -410,15 +426,16 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     }
 }
 
-// dK, dV with the two gradients on different wavefronts: a workgroup of 8
-// waves holds 128 keys of one K/V head; waves 0-3 compute S, P and dV for 32
-// keys each (K fragments and one accumulator), waves 4-7 compute S, dP, dS and
-// dK for the same keys (K and V fragments and one accumulator).  S is
-// computed twice (five products per visible pair instead of four), but each
-// wave fits in 256 registers, so two waves share a SIMD and one's
-// exponentials overlap the other's MFMAs.
+// dK, dV on two wavefronts per 32 keys, P computed once: a workgroup of 8
+// waves holds 128 keys of one K/V head.  For each (query head, 64-query tile)
+// item, waves 0-3 compute S = Q K^T and P, write P (fp32, in their
+// accumulator layout) to LDS and keep it as the bf16 operand of dV^T += dO^T P,
+// while waves 4-7 compute dP = dO V^T for the same keys; after a barrier waves
+// 4-7 read P back, form dS = P (dP - Delta) and accumulate dK^T += Q^T dS.
+// Four products per visible pair, the exponentials once, each wave holding one
+// accumulator; the values are those of the other two forms bit for bit.
 template <int D>
-__global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
+__global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
   using geo = Geo<D>;
   constexpr int NW = 8;
   constexpr int KS = geo::KS;
@@ -430,6 +447,8 @@ __global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
   __shared__ __attribute__((aligned(1024))) char o1s[geo::TILE];
   __shared__ __attribute__((aligned(256))) float a0s[2 * BN];
   __shared__ __attribute__((aligned(256))) float a1s[2 * BN];
+  // P of the current item: [wave pair][32-query block][register group of 4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 ps[4 * 2 * 4 * 64];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -446,7 +465,7 @@ __global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
 
   const int k0 = kt * KB;
   const int k1 = min(p.S, k0 + KB);
-  const int kw0 = k0 + (w & 3) * 32;  // this wave's first key
+  const int kw0 = k0 + (w & 3) * 32;  // this wave's first key (same for waves w and w + 4)
   const int kw1 = min(p.S, kw0 + 32);
   const bool wave_live = kw0 < p.S;
   const size_t kv_row0 = ((size_t)b * p.Nkv + g) * (size_t)p.S;
@@ -473,110 +492,115 @@ __global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
   };
   if (n_items > 0) issue(0, q0s, o0s, a0s);
 
+  // K fragments (dV waves, for S) or V fragments (dK waves, for dP) as B
+  // operands: key column ln, head dims 16*ks + 8*hl + i
   const int kj = min(kw0 + ln, p.S - 1);
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 bf[KS];
   {
-    const bf16x8* ks_ = reinterpret_cast<const bf16x8*>(p.K + (kv_row0 + kj) * D + hl * 8);
-    const bf16x8* vs_ = reinterpret_cast<const bf16x8*>(p.V + (kv_row0 + kj) * D + hl * 8);
+    const bf16x8* src =
+        reinterpret_cast<const bf16x8*>((krole ? p.V : p.K) + (kv_row0 + kj) * D + hl * 8);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = ks_[ks * 2];
-      vf[ks] = krole ? vs_[ks * 2] : bf16x8{};
-    }
+    for (int ks = 0; ks < KS; ++ks) bf[ks] = src[ks * 2];
   }
 
   int roff[KS];
   row_operand_offsets<D>(ln, hl, roff);
   int troff[2][DB];
   tr_operand_offsets<D>(lane, troff);
+  f32x4* const pw = ps + (w & 3) * 2 * 4 * 64 + lane;  // this pair's P, this lane
 
   f32x16 acc[DB];  // dV (waves 0-3) or dK / scale (waves 4-7)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  for (int it = 0; it < n_items; ++it) {
+  // item `it` reads stage (Qt, Ot, At) and copies item it + 1 into the other
+  // stage; the loop below passes the stages as fixed LDS objects so that the
+  // compiler can tell the copies in flight from the tile being read
+  auto item = [&](int it, const char* Qt, const char* Ot, const float* At, char* Qn, char* On,
+                  float* An) {
     const int q0 = (t_lo + it % n_qt) * BN;
-    const char* Qt = (it & 1) ? q1s : q0s;
-    const char* Ot = (it & 1) ? o1s : o0s;
-    const float* At = (it & 1) ? a1s : a0s;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (it + 1 < n_items)
-      issue(it + 1, (it & 1) ? q0s : q1s, (it & 1) ? o0s : o1s, (it & 1) ? a0s : a1s);
+    if (it + 1 < n_items) issue(it + 1, Qn, On, An);
     bool live = wave_live && q0 < p.S;
     if (p.causal) live = live && q0 + BN - 1 >= kw0;
     if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
-    if (!live) continue;
     bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
     if (p.causal) full = full && q0 >= kw1 - 1;
     if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
 
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-      }
-      // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln
-      float lse2[16];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) lse2[a * 4 + u] = l4[u] * kLog2e;
-      }
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
-        }
-      }
+    // register r of a block: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln
+    bf16x8 pf[2][2];  // dV waves: P as the bf16 operand, kept over the barrier
+    f32x16 dp[2];     // dK waves: dP of both 32-query blocks
+    if (live) {
       if (!krole) {
-        // dV^T += dO^T P
-        bf16x8 pf[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 pp;
+        for (int mb = 0; mb < 2; ++mb) {
+          f32x16 s = f32x16{};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r0 = kk * 8 + 2 * j;
-            pp[j] = pack_bf16x2(exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0])),
-                                exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1])));
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, bf[ks], s, 0, 0, 0);
           }
-          pf[kk] = __builtin_bit_cast(bf16x8, pp);
+          if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+              if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
+            f32x4 e;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              e[u] = exp2_fast(__builtin_fmaf(s[a * 4 + u], p.c, -(l4[u] * kLog2e)));
+            pw[(mb * 4 + a) * 64] = e;
+            u32x4& dst = *reinterpret_cast<u32x4*>(&pf[mb][a >> 1]);
+            dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0], e[1]);
+            dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2], e[3]);
+          }
         }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          dp[mb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
+            dp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, bf[ks], dp[mb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    lds_barrier();  // P of this item is in LDS; the next item's copies stay in flight
+    if (!live) return;
+    if (!krole) {
+      // dV^T += dO^T P
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
             const bf16x8 oa = read_tr_operand<D>(Ot, mb * 2 + kk, troff, db);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[kk], acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[mb][kk], acc[db], 0, 0, 0);
           }
-      } else {
-        // dP = dO V^T, dS = P (dP - Delta), dK^T += Q^T dS
-        f32x16 dp = f32x16{};
+    } else {
+      // dS = P (dP - Delta), dK^T += Q^T dS
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
         bf16x8 sf[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 ss;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r0 = kk * 8 + 2 * j;
-            const int a = r0 >> 2;
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
-            const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0]));
-            const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1]));
-            ss[j] = pack_bf16x2(p0 * (dp[r0] - d4[r0 & 3]), p1 * (dp[r0 + 1] - d4[(r0 + 1) & 3]));
-          }
-          sf[kk] = __builtin_bit_cast(bf16x8, ss);
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 e = pw[(mb * 4 + a) * 64];
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
+          u32x4& dst = *reinterpret_cast<u32x4*>(&sf[a >> 1]);
+          dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0] * (dp[mb][a * 4 + 0] - d4[0]),
+                                             e[1] * (dp[mb][a * 4 + 1] - d4[1]));
+          dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2] * (dp[mb][a * 4 + 2] - d4[2]),
+                                             e[3] * (dp[mb][a * 4 + 3] - d4[3]));
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -587,7 +611,13 @@ __global__ __launch_bounds__(512) void dkv_split_kernel(BwdMfmaParams p) {
           }
       }
     }
+  };
+  int it = 0;
+  for (; it + 1 < n_items; it += 2) {
+    item(it, q0s, o0s, a0s, q1s, o1s, a1s);
+    item(it + 1, q1s, o1s, a1s, q0s, o0s, a0s);
   }
+  if (it < n_items) item(it, q0s, o0s, a0s, q1s, o1s, a1s);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (!wave_live || kw0 + ln >= p.S) return;
@@ -615,15 +645,15 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   p.qspan = (NWQ / p.hp) * 32;
   p.n_qtiles = (p.S + p.qspan - 1) / p.qspan;
   const long long nq = (long long)p.n_qtiles * p.B * p.Nkv * p.n_hsub;
-  constexpr bool split = BWD_SPLIT && D == 128;
-  const long long nk = split ? (long long)((p.S + 127) / 128) * p.B * p.Nkv
-                             : (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
+  constexpr bool pair = D == 128 ? BWD_PAIR128 != 0 : BWD_PAIR64 != 0;
+  const long long nk = pair ? (long long)((p.S + 127) / 128) * p.B * p.Nkv
+                            : (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)nq), dim3(NWQ * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (split)
-    hipLaunchKernelGGL((dkv_split_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
+  if constexpr (pair)
+    hipLaunchKernelGGL((dkv_pair_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
   return hipGetLastError();

@@ -30,6 +30,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Wait until this wave's LDS reads have returned (s_waitcnt lgkmcnt(0)), as
+// a point that no memory access moves across.  A global -> LDS copy issued
+// while reads of its target are still queued may land before they execute
+// (a copy served from L2 takes a few hundred cycles): a wave that reuses a
+// stage without a workgroup barrier calls this before copying into it.
+__device__ __forceinline__ void wait_lds_reads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  asm volatile("" ::: "memory");
+}
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

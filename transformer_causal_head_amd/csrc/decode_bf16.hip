@@ -318,6 +318,22 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
           sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], sc[nb][kb], 0, 0, 0);
       }
     }
+    // V^T operands of this step, read now where the registers allow: they
+    // return while the softmax runs, so the copies that reuse this stage
+    // after the step need not wait for them
+    auto read_v = [&](int db) {
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr bool EARLY_V = D * NB <= 256;
+    bf16x8 va[EARLY_V ? DB : 1];
+    if constexpr (EARLY_V) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[db] = read_v(db);
+    }
     if (k0 + STEP > n || k0 < lo || (KM && kw != ~0u)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -370,11 +386,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 a = EARLY_V ? va[EARLY_V ? db : 0] : read_v(db);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
@@ -402,19 +414,30 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     }
   };
 
-  for (int s = s0; s < nsteps; s += 2) {
+  // The loop starts with the copies of step s + 2, not with a read of stage
+  // 0: entered at such a read, the loop merges the states of its entry and
+  // its back edge there, and the compiler can no longer tell which copies may
+  // still target stage 0; it then drains every copy in flight.
+  if (s0 < nsteps) {
     wait_vm<PER_STEP>();
-    substitute(s, K0, V0);
-    step(s, K0, V0);
-    load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
-    load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
-    wait_vm<PER_STEP>();
-    if (s + 1 < nsteps) {
+    substitute(s0, K0, V0);
+    step(s0, K0, V0);
+    for (int s = s0;; s += 2) {
+      wait_lds_reads();  // step s has read stage 0
+      load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
+      load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
+      wait_vm<PER_STEP>();
+      if (s + 1 >= nsteps) break;
       substitute(s + 1, K1, V1);
       step(s + 1, K1, V1);
+      wait_lds_reads();  // step s + 1 has read stage 1
+      load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
+      load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
+      wait_vm<PER_STEP>();
+      if (s + 2 >= nsteps) break;
+      substitute(s + 2, K0, V0);
+      step(s + 2, K0, V0);
     }
-    load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
-    load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
   }
   wait_vm<0>();  // no copy may still target LDS when the wave ends
   write_new_row();
