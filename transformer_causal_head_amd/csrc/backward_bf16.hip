@@ -12,7 +12,7 @@
 //                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
 //                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
 //                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
-//   dkv_kernel -- (head size 64; head size 128 uses dkv_pair_kernel below,
+//   dkv_kernel -- (head size 64; head size 128 uses dkv_pipe_kernel below,
 //                 which puts dV and dK on different wavefronts)
 //                 one wavefront per 32 keys of one K/V head, streaming the Q and
 //                 dO tiles of every query head of its group over the queries
@@ -32,7 +32,7 @@
 #include "tiles.h"
 
 // dK / dV on two wavefronts per 32 keys with the weights passed through LDS
-// (dkv_pair_kernel, 1) or on one wavefront per 32 keys (dkv_kernel, 0), at
+// (dkv_pipe_kernel, 1) or on one wavefront per 32 keys (dkv_kernel, 0), at
 // head size 128 and at head size 64.
 #ifndef BWD_PAIR128
 #define BWD_PAIR128 1
@@ -426,33 +426,48 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     }
 }
 
-// dK, dV on two wavefronts per 32 keys, P computed once: a workgroup of 8
-// waves holds 128 keys of one K/V head.  For each (query head, 64-query tile)
-// item, waves 0-3 compute S = Q K^T and P, write P (fp32, in their
-// accumulator layout) to LDS and keep it as the bf16 operand of dV^T += dO^T P,
-// while waves 4-7 compute dP = dO V^T for the same keys; after a barrier waves
-// 4-7 read P back, form dS = P (dP - Delta) and accumulate dK^T += Q^T dS.
-// Four products per visible pair, the exponentials once, each wave holding one
-// accumulator; the values are those of the other two forms bit for bit.
+// dK, dV on two wavefronts per 32 keys, skewed by one item: a workgroup of 8
+// waves holds 128 keys of one K/V head and runs the (query head, 64-query
+// tile) items of its group in order.  In round `it`:
+//   waves 0-3 (dV) compute S = Q K^T and P for item it, store P (fp32, in
+//              their accumulator layout) to LDS and accumulate dV^T += dO^T P;
+//   waves 4-7 (dK) compute dP = dO V^T for item it and keep it in registers,
+//              then form dS = P (dP - Delta) for item it - 1 from the P the dV
+//              waves stored in the previous round, and accumulate
+//              dK^T += Q^T dS.
+// One barrier per round orders everything: it publishes the previous round's
+// P and frees the stages the next copies overwrite.  Q and Delta live for
+// three rounds (item it - 1 on the dK side, it, and it + 1 being copied), dO,
+// LSE and P for two.  Each role issues the copies of the stages it reads
+// transposed (dV: dO and LSE; dK: Q and Delta) and runs its own loop unrolled
+// by that stage count, so every transposing read names a fixed LDS object and
+// the compiler keeps the copies in flight across it.  Same products and
+// roundings as the other forms: the results are bit for bit theirs.
 template <int D>
-__global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
+__global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
   using geo = Geo<D>;
-  constexpr int NW = 8;
+  constexpr int NR = 4;  // waves per role
   constexpr int KS = geo::KS;
   constexpr int DB = geo::DB;
   constexpr int KB = 128;  // keys per workgroup
+  constexpr int PW = 2 * 4 * 64;  // f32x4 of P per wave pair: [32-query block][register group][lane]
   __shared__ __attribute__((aligned(1024))) char q0s[geo::TILE];
   __shared__ __attribute__((aligned(1024))) char q1s[geo::TILE];
+  __shared__ __attribute__((aligned(1024))) char q2s[geo::TILE];
   __shared__ __attribute__((aligned(1024))) char o0s[geo::TILE];
   __shared__ __attribute__((aligned(1024))) char o1s[geo::TILE];
-  __shared__ __attribute__((aligned(256))) float a0s[2 * BN];
-  __shared__ __attribute__((aligned(256))) float a1s[2 * BN];
-  // P of the current item: [wave pair][32-query block][register group of 4][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 ps[4 * 2 * 4 * 64];
+  __shared__ __attribute__((aligned(256))) float l0s[BN];
+  __shared__ __attribute__((aligned(256))) float l1s[BN];
+  __shared__ __attribute__((aligned(256))) float d0s[BN];
+  __shared__ __attribute__((aligned(256))) float d1s[BN];
+  __shared__ __attribute__((aligned(256))) float d2s[BN];
+  __shared__ __attribute__((aligned(16))) f32x4 p0s[NR * PW];
+  __shared__ __attribute__((aligned(16))) f32x4 p1s[NR * PW];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool krole = w >= 4;  // wave-uniform: dK (true) or dV
+  const bool krole = w >= NR;  // wave-uniform: dK (true) or dV
+  const int wl = w & (NR - 1);  // index within the role; waves w and w + 4 share keys
   const int lane = tid & 63;
   const int ln = lane & 31;
   const int hl = lane >> 5;
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
 
   const int k0 = kt * KB;
   const int k1 = min(p.S, k0 + KB);
-  const int kw0 = k0 + (w & 3) * 32;  // this wave's first key (same for waves w and w + 4)
+  const int kw0 = k0 + wl * 32;  // this wave's first key
   const int kw1 = min(p.S, kw0 + 32);
   const bool wave_live = kw0 < p.S;
   const size_t kv_row0 = ((size_t)b * p.Nkv + g) * (size_t)p.S;
@@ -476,21 +491,45 @@ __global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
   const int n_qt = (qhi + BN - 1) / BN - t_lo;
   const int n_items = p.G * max(n_qt, 0);
 
-  auto issue = [&](int item, char* qdst, char* odst, float* adst) {
-    const int hh = item / n_qt;
-    const int q0 = (t_lo + item % n_qt) * BN;
-    const size_t row0 = ((size_t)b * p.Nq + (size_t)g * p.G + hh) * (size_t)p.S;
-    load_tile<D, NW>(head_ref<D>(p.Q + row0 * D, p.S), q0, qdst, w, lane);
-    load_tile<D, NW>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, w, lane);
-    if (w < 2) {
-      const float* src = (w == 0 ? p.LSE : p.delta) + row0;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.S * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(adst + w * BN), 4, (q0 + lane) * 4,
-                                               0, 0, 0);
-    }
+  auto item_q0 = [&](int it) { return (t_lo + it % n_qt) * BN; };
+  auto item_row0 = [&](int it) {
+    return ((size_t)b * p.Nq + (size_t)g * p.G + it / n_qt) * (size_t)p.S;
   };
-  if (n_items > 0) issue(0, q0s, o0s, a0s);
+  // one 4-byte DMA per lane: 64 values of an fp32 row vector (LSE or Delta)
+  auto load_vec = [&](const float* src, int q0, float* dst) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.S * 4, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (q0 + lane) * 4, 0, 0, 0);
+  };
+  auto issue_v = [&](int it, char* odst, float* ldst) {  // dV waves: dO and LSE
+    const size_t row0 = item_row0(it);
+    const int q0 = item_q0(it);
+    load_tile<D, NR>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, wl, lane);
+    if (wl == 0) load_vec(p.LSE + row0, q0, ldst);
+  };
+  auto issue_k = [&](int it, char* qdst, float* ddst) {  // dK waves: Q and Delta
+    const size_t row0 = item_row0(it);
+    const int q0 = item_q0(it);
+    load_tile<D, NR>(head_ref<D>(p.Q + row0 * D, p.S), q0, qdst, wl, lane);
+    if (wl == 0) load_vec(p.delta + row0, q0, ddst);
+  };
+  // does the wave pair see any (query, key) pair of item it?  all of them?
+  auto live_of = [&](int it) {
+    if (it >= n_items) return false;
+    const int q0 = item_q0(it);
+    bool live = wave_live && q0 < p.S;
+    if (p.causal) live = live && q0 + BN - 1 >= kw0;
+    if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
+    return live;
+  };
+  auto full_of = [&](int it) {
+    const int q0 = item_q0(it);
+    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
+    if (p.causal) full = full && q0 >= kw1 - 1;
+    if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
+    return full;
+  };
+  auto qstage = [&](int k) -> const char* { return k == 0 ? q0s : (k == 1 ? q1s : q2s); };
 
   // K fragments (dV waves, for S) or V fragments (dK waves, for dP) as B
   // operands: key column ln, head dims 16*ks + 8*hl + i
@@ -502,81 +541,69 @@ __global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bf[ks] = src[ks * 2];
   }
-
   int roff[KS];
   row_operand_offsets<D>(ln, hl, roff);
   int troff[2][DB];
   tr_operand_offsets<D>(lane, troff);
-  f32x4* const pw = ps + (w & 3) * 2 * 4 * 64 + lane;  // this pair's P, this lane
 
   f32x16 acc[DB];  // dV (waves 0-3) or dK / scale (waves 4-7)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  // item `it` reads stage (Qt, Ot, At) and copies item it + 1 into the other
-  // stage; the loop below passes the stages as fixed LDS objects so that the
-  // compiler can tell the copies in flight from the tile being read
-  auto item = [&](int it, const char* Qt, const char* Ot, const float* At, char* Qn, char* On,
-                  float* An) {
-    const int q0 = (t_lo + it % n_qt) * BN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (it + 1 < n_items) issue(it + 1, Qn, On, An);
-    bool live = wave_live && q0 < p.S;
-    if (p.causal) live = live && q0 + BN - 1 >= kw0;
-    if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
-    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
-    if (p.causal) full = full && q0 >= kw1 - 1;
-    if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
+  if (n_items > 0) {
+    if (krole)
+      issue_k(0, q0s, d0s);
+    else
+      issue_v(0, o0s, l0s);
+  }
 
-    // register r of a block: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln
-    bf16x8 pf[2][2];  // dV waves: P as the bf16 operand, kept over the barrier
-    f32x16 dp[2];     // dK waves: dP of both 32-query blocks
-    if (live) {
-      if (!krole) {
+  if (!krole) {
+    // round it: item it; dO, LSE and P in stage it % 2, Q in stage it % 3
+    auto v_round = [&](int it, const char* Ot, const float* Lt, f32x4* Pt, char* On, float* Ln) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (!live_of(it)) {
+        if (it + 1 < n_items) issue_v(it + 1, On, Ln);
+        return;
+      }
+      const int q0 = item_q0(it);
+      const bool full = full_of(it);
+      const char* Qt = qstage(it % 3);
+      f32x4* const pw = Pt + wl * PW + lane;
+      bf16x8 pf[2][2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          f32x16 s = f32x16{};
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 s = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, bf[ks], s, 0, 0, 0);
-          }
-          if (!full) {
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qt + mb * 32 * geo::RB + roff[ks]);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, bf[ks], s, 0, 0, 0);
+        }
+        // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln
+        if (!full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-              if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
-            }
-          }
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
-            f32x4 e;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              e[u] = exp2_fast(__builtin_fmaf(s[a * 4 + u], p.c, -(l4[u] * kLog2e)));
-            pw[(mb * 4 + a) * 64] = e;
-            u32x4& dst = *reinterpret_cast<u32x4*>(&pf[mb][a >> 1]);
-            dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0], e[1]);
-            dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2], e[3]);
+          for (int r = 0; r < 16; ++r) {
+            const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+            if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
           }
         }
-      } else {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          dp[mb] = f32x16{};
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + mb * 32 + a * 8 + hl * 4);
+          f32x4 e;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
-            dp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, bf[ks], dp[mb], 0, 0, 0);
-          }
+          for (int u = 0; u < 4; ++u)
+            e[u] = exp2_fast(__builtin_fmaf(s[a * 4 + u], p.c, -(l4[u] * kLog2e)));
+          pw[(mb * 4 + a) * 64] = e;
+          u32x4& dst = *reinterpret_cast<u32x4*>(&pf[mb][a >> 1]);
+          dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0], e[1]);
+          dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2], e[3]);
         }
       }
-    }
-    lds_barrier();  // P of this item is in LDS; the next item's copies stay in flight
-    if (!live) return;
-    if (!krole) {
+      // the next item's copies go out after the reads of the Q stage, which
+      // is picked at run time (the compiler would otherwise wait for the
+      // copies before those reads) and before the transposing reads of dO
+      if (it + 1 < n_items) issue_v(it + 1, On, Ln);
       // dV^T += dO^T P
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -587,37 +614,85 @@ __global__ __launch_bounds__(512) void dkv_pair_kernel(BwdMfmaParams p) {
             const bf16x8 oa = read_tr_operand<D>(Ot, mb * 2 + kk, troff, db);
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pf[mb][kk], acc[db], 0, 0, 0);
           }
-    } else {
-      // dS = P (dP - Delta), dK^T += Q^T dS
+    };
+    int it = 0;
+    for (; it + 1 < n_items; it += 2) {
+      v_round(it, o0s, l0s, p0s, o1s, l1s);
+      v_round(it + 1, o1s, l1s, p1s, o0s, l0s);
+    }
+    if (it < n_items) v_round(it, o0s, l0s, p0s, o1s, l1s);
+    // the dK waves' last round (the dS and dK of the last item)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  } else {
+    f32x16 dp_prev[2] = {f32x16{}, f32x16{}};
+    bool live_prev = false;
+    // round it (0 .. n_items): dP of item it (dO in stage it % 2); dS and dK
+    // of item it - 1 (Q and Delta in stage (it - 1) % 3, P in stage (it - 1) % 2)
+    auto k_round = [&](int it, const char* Qp, const float* Dp, char* Qn, float* Dn) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const bool live = live_of(it);
+      f32x16 dp[2];
+      if (live) {
+        const char* Ot = (it & 1) ? o1s : o0s;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        bf16x8 sf[2];
+        for (int mb = 0; mb < 2; ++mb) {
+          dp[mb] = f32x16{};
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 e = pw[(mb * 4 + a) * 64];
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
-          u32x4& dst = *reinterpret_cast<u32x4*>(&sf[a >> 1]);
-          dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0] * (dp[mb][a * 4 + 0] - d4[0]),
-                                             e[1] * (dp[mb][a * 4 + 1] - d4[1]));
-          dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2] * (dp[mb][a * 4 + 2] - d4[2]),
-                                             e[3] * (dp[mb][a * 4 + 3] - d4[3]));
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ot + mb * 32 * geo::RB + roff[ks]);
+            dp[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, bf[ks], dp[mb], 0, 0, 0);
+          }
         }
+      }
+      // dS of item it - 1 from the P stored in the previous round
+      bf16x8 sf[2][2];
+      if (live_prev) {
+        const f32x4* const pr = ((it & 1) ? p0s : p1s) + wl * PW + lane;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 qa = read_tr_operand<D>(Qt, mb * 2 + kk, troff, db);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf[kk], acc[db], 0, 0, 0);
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 e = pr[(mb * 4 + a) * 64];
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dp + mb * 32 + a * 8 + hl * 4);
+            u32x4& dst = *reinterpret_cast<u32x4*>(&sf[mb][a >> 1]);
+            dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0] * (dp_prev[mb][a * 4 + 0] - d4[0]),
+                                               e[1] * (dp_prev[mb][a * 4 + 1] - d4[1]));
+            dst[(a & 1) * 2 + 1] = pack_bf16x2(e[2] * (dp_prev[mb][a * 4 + 2] - d4[2]),
+                                               e[3] * (dp_prev[mb][a * 4 + 3] - d4[3]));
           }
       }
+      // the next item's copies go out after the reads of the dO and P stages,
+      // which are picked at run time, and before the transposing reads of Q
+      if (it + 1 < n_items) issue_k(it + 1, Qn, Dn);
+      if (live_prev) {
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const bf16x8 qa = read_tr_operand<D>(Qp, mb * 2 + kk, troff, db);
+              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sf[mb][kk], acc[db], 0, 0, 0);
+            }
+      }
+      if (live) {
+        dp_prev[0] = dp[0];
+        dp_prev[1] = dp[1];
+      }
+      live_prev = live;
+    };
+    for (int it = 0;; it += 3) {
+      if (it > n_items) break;
+      k_round(it, q2s, d2s, q1s, d1s);
+      if (it + 1 > n_items) break;
+      k_round(it + 1, q0s, d0s, q2s, d2s);
+      if (it + 2 > n_items) break;
+      k_round(it + 2, q1s, d1s, q0s, d0s);
     }
-  };
-  int it = 0;
-  for (; it + 1 < n_items; it += 2) {
-    item(it, q0s, o0s, a0s, q1s, o1s, a1s);
-    item(it + 1, q1s, o1s, a1s, q0s, o0s, a0s);
   }
-  if (it < n_items) item(it, q0s, o0s, a0s, q1s, o1s, a1s);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (!wave_live || kw0 + ln >= p.S) return;
@@ -653,7 +728,7 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (pair)
-    hipLaunchKernelGGL((dkv_pair_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((dkv_pipe_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
   return hipGetLastError();

@@ -48,18 +48,6 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
-// Workgroup barrier that orders LDS reads and writes only.  __syncthreads()
-// also waits for every outstanding vector memory operation, including the
-// global -> LDS copies of a tile issued ahead; this one waits for the wave's
-// own LDS operations (lgkmcnt(0)) and leaves those copies in flight.  The
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt not waited
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Copy keys [k0, k0+64) of one head (a buffer resource over the head) into a
 // swizzled LDS tile.  The tile is NP pieces of 1 KB (RP rows); wave w issues
 // pieces w, w + NW, ...  The whole offset is in the per-lane operand, which the
