@@ -70,7 +70,9 @@ __device__ __forceinline__ void load_tile(HeadRef h, int k0, char* tile, int w, 
 #pragma unroll
   for (int j = 0; j < (g::NP + NW - 1) / NW; ++j) {
     const int piece = w + j * NW;  // wave-uniform
-    if (piece >= g::NP) break;
+    // with NP a multiple of NW every wave issues the same copies, with no
+    // branch the compiler would have to count around
+    if (g::NP % NW != 0 && piece >= g::NP) break;
     const int r = piece * g::RP + lane / g::NC;
     const int voff = r * g::RB + (((lane % g::NC) ^ swz<D>(r)) << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.rs, (lds_void*)(tile + piece * 1024), 16,
