@@ -212,6 +212,59 @@ def _cache_paths(torch, dev, tch, steps, warmup):
           flush=True)
 
 
+def _workloads(torch, dev, tch, steps, warmup):
+    """One JSON line per named workload, each in the launch configuration the parity tests
+    check at full size: the three bf16 prefill workloads against the bf16 MFMA peak and the
+    decode workload against HBM bandwidth.  The 1024-token workload is short (tens of us) and
+    its inputs would stay in the 256 MB last-level cache, so its calls rotate over eight input
+    sets (about 400 MB) and are timed back to back."""
+    for name, cfg in workloads.WORKLOADS.items():
+        if cfg["kind"] != "prefill" or cfg["dtype"] != "bf16":
+            continue
+        B, Nq, Nkv, S, Dh = cfg["B"], cfg["Nq"], cfg["Nkv"], cfg["S"], cfg["Dh"]
+        sets = 8 if S <= 4096 else 1
+        inputs = []
+        for i in range(sets):
+            q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=i)
+            inputs.append(tuple(workloads.to_torch(x, "bf16", dev) for x in (q, k, v)))
+            del q, k, v
+        O = torch.empty_like(inputs[0][0])
+        L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(Dh)
+        state = {"i": 0}
+
+        def call():
+            tq, tk, tv = inputs[state["i"] % sets]
+            state["i"] += 1
+            tch.attn_prefill(tq, tk, tv, O, L, causal=int(cfg["causal"]), window=cfg["window"],
+                             scale=scale)
+        n = steps * (20 if sets > 1 else 1)
+        ms = _time(torch, call, n, max(warmup, sets))
+        flop, nbytes = workloads.prefill_work(B, Nq, Nkv, S, Dh, cfg["causal"], cfg["window"], 2)
+        tf = flop / (ms * 1e-3) / 1e12
+        print(json.dumps({"path": "attn_prefill", "workload": name, "ms": round(ms, 4),
+                          "TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "algorithmic_flop": flop, "compulsory_bytes": nbytes,
+                          "input_sets": sets}), flush=True)
+        del inputs, O, L
+    dc = workloads.WORKLOADS[DECODE]
+    B, Nq, Nkv, Dh, T = dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"], dc["Tcap"]
+    lens, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, T, dc["len_lo"], dc["len_hi"])
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+    del kc, vc
+    tl = torch.from_numpy(lens).to(dev)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, tch.attn_decode_workspace_bytes(B, Nq, Nkv, Dh, T, tch.ATTN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    ms = _time(torch, lambda: tch.attn_decode(tq, tk, tv, tl, O, L, ws), steps, warmup)
+    _, nbytes = workloads.decode_work(lens, Nq, Nkv, Dh, 2)
+    gbs = nbytes / ms / 1e6
+    print(json.dumps({"path": "attn_decode", "workload": DECODE, "ms": round(ms, 4),
+                      "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": nbytes}), flush=True)
+
+
 def _head_sizes(torch, dev, tch, steps, warmup):
     """One JSON line per shape: causal MHA prefill at head sizes 64 / 128 / 256 with the same
     32-head layout, and the batched decode workload at head sizes 64 / 256 and as MQA."""
@@ -230,6 +283,21 @@ def _head_sizes(torch, dev, tch, steps, warmup):
                           "bf16 causal", "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
                           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
         del tq, tk, tv, O, L
+    # non-causal attention (every query sees every key), 8192 tokens
+    B, H, S, Dh = 1, 32, 8192, 128
+    q, k, v = workloads.prefill_inputs(B, H, H, S, Dh, "bf16", seed=0)
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
+    del q, k, v
+    O = torch.empty_like(tq)
+    L = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    ms = _time(torch, lambda: tch.attn_prefill(tq, tk, tv, O, L, causal=0,
+                                               scale=1.0 / math.sqrt(Dh)), steps, warmup)
+    flop, _ = workloads.prefill_work(B, H, H, S, Dh, False, 0, 2)
+    tf = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({"path": "attn_prefill", "workload": f"B={B} heads={H} S={S} Dh={Dh} "
+                      "bf16 non-causal", "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                      "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+    del tq, tk, tv, O, L
     dc = workloads.WORKLOADS[DECODE]
     for Dh, Nq, Nkv in ((64, 32, 8), (256, 32, 8), (128, 32, 1)):
         B, T = dc["B"], dc["Tcap"]
@@ -388,6 +456,9 @@ def main():
     ap.add_argument("--rope-padding", action="store_true",
                     help="time RoPE, the rotating append and the padded prefill / decode "
                          "instead of the main step")
+    ap.add_argument("--workloads", action="store_true",
+                    help="time each named workload (the 1024-token, 32768-token and GQA window "
+                    "prefills, and the decode step) in its own JSON line instead of the main step")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) instead of the main step")
     args = ap.parse_args()
@@ -416,6 +487,9 @@ def main():
         return
     if args.head_sizes:
         _head_sizes(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
+        return
+    if args.workloads:
+        _workloads(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
     if args.backward:
         _backward(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
