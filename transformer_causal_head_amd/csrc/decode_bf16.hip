@@ -294,6 +294,26 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
   }
 
+  // Where the registers allow (Dh x query-head blocks <= 256), a step's V^T
+  // operands are read right after its K operands, and its PV products run in
+  // finish_pv() after the copies that refill its stage have been issued: the
+  // products read only registers, so the copies need not queue behind them.
+  constexpr bool EARLY_V = D * NB <= 256;
+  bf16x8 va[EARLY_V ? DB : 1];
+  bf16x8 pf[NB];
+  bool pv_pending = false;
+  auto finish_pv = [&]() {
+    if constexpr (EARLY_V) {
+      if (pv_pending) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf[nb], o[nb][db], 0, 0, 0);
+        pv_pending = false;
+      }
+    }
+  };
   auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
     const int k0 = c0 + s * STEP;
     // flags of keys k0 .. k0 + 31 (k0 is a multiple of 32); a step of padding
@@ -319,8 +339,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       }
     }
     // V^T operands of this step, read now where the registers allow: they
-    // return while the softmax runs, so the copies that reuse this stage
-    // after the step need not wait for them
+    // return while the softmax runs
     auto read_v = [&](int db) {
       const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
@@ -328,8 +347,6 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
           (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    constexpr bool EARLY_V = D * NB <= 256;
-    bf16x8 va[EARLY_V ? DB : 1];
     if constexpr (EARLY_V) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) va[db] = read_v(db);
@@ -348,7 +365,6 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
           }
         }
     }
-    bf16x8 pf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 (&t)[2] = sc[nb];
@@ -384,12 +400,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       pk[3] = pack_bf16x2(t[1][2], t[1][3]);
       pf[nb] = __builtin_bit_cast(bf16x8, pk);
     }
+    if constexpr (EARLY_V) {
+      pv_pending = true;  // the products run in finish_pv()
+    } else {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 a = EARLY_V ? va[EARLY_V ? db : 0] : read_v(db);
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 a = read_v(db);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb)
+          o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
+      }
     }
   };
 
@@ -426,6 +446,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       wait_lds_reads();  // step s has read stage 0
       load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
       load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
+      finish_pv();
       wait_vm<PER_STEP>();
       if (s + 1 >= nsteps) break;
       substitute(s + 1, K1, V1);
@@ -433,6 +454,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       wait_lds_reads();  // step s + 1 has read stage 1
       load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
       load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
+      finish_pv();
       wait_vm<PER_STEP>();
       if (s + 2 >= nsteps) break;
       substitute(s + 2, K0, V0);
