@@ -106,6 +106,11 @@ struct Params {
   int qspan;      // queries per workgroup
   int n_qtiles;
   int n_hsub;     // G / hp
+  // 0: a workgroup's query blocks are consecutive (qspan rows from qt *
+  // qspan).  1: they are strided, block qt + k * n_qtiles for k = 0 ..
+  // NW / hp - 1, so that every workgroup of a causal prefill holds early and
+  // late queries alike (used when the whole grid runs in one round).
+  int strided;
 };
 
 template <int D, int QB_>
@@ -209,10 +214,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
   const int q_off = p.lens ? n_keys - p.S : 0;
 
   const int head = g * p.G + hsub * p.hp + (w % p.hp);
-  const int qa_row = qt * p.qspan + (w / p.hp) * QW;  // first query row of this wave
-  const int qa = q_off + qa_row;                      // ... and its position
-  const int q0 = q_off + qt * p.qspan;
-  const int q1 = q_off + min(p.S, qt * p.qspan + p.qspan);
+  const int nblk = NW / p.hp;  // query blocks of QW rows per workgroup
+  // first query row of this wave (and its position); the workgroup's rows
+  // span [q0, q1)
+  const int qa_row = p.strided ? (qt + (w / p.hp) * p.n_qtiles) * QW
+                               : qt * p.qspan + (w / p.hp) * QW;
+  const int qa = q_off + qa_row;
+  const int q0 = q_off + (p.strided ? qt * QW : qt * p.qspan);
+  const int q1 = q_off + min(p.S, p.strided ? (qt + (nblk - 1) * p.n_qtiles + 1) * QW
+                                            : qt * p.qspan + p.qspan);
   const int wq1 = q_off + min(p.S, qa_row + QW);
   const bool wave_live = qa_row < p.S;
 
@@ -554,6 +564,19 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.n_qtiles = (S + p.qspan - 1) / p.qspan;
   const long long nblocks = (long long)p.n_qtiles * B * Nkv * p.n_hsub;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // A causal prefill whose grid runs in one round lasts as long as its
+  // heaviest workgroup: with consecutive query blocks the last tile of a head
+  // sees n_qtiles times the keys of the first.  Strided blocks give every
+  // workgroup the same mix (a window keeps them consecutive: strided blocks
+  // would make each workgroup stream most of the sequence).
+  p.strided = 0;
+  if (causal && window == 0 && lens == nullptr && p.n_qtiles > 1) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        nblocks <= n_cu)
+      p.strided = 1;
+  }
   if (kbits)
     hipLaunchKernelGGL((prefill_kernel<D, NW, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                        stream, p);
