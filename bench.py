@@ -265,6 +265,34 @@ def _workloads(torch, dev, tch, steps, warmup):
                       "algorithmic_bytes": nbytes}), flush=True)
 
 
+def _decode_batches(torch, dev, tch, steps, warmup):
+    """One JSON line per decode batch shape: few sequences at long context (every
+    sequence at full length), where the chunk length, not the batch, has to supply
+    the parallelism, and the decode workload's 64 sequences for reference."""
+    for B, T, Nkv, Nq in ((1, 32768, 8, 32), (1, 131072, 8, 32), (4, 32768, 8, 32),
+                          (8, 32768, 8, 32), (1, 32768, 1, 32), (2, 65536, 8, 64)):
+        lens = np.full(B, T, dtype=np.int32)
+        q = workloads.draw((B, Nq, 128), "bf16", 0, 10)
+        tq = workloads.to_torch(q, "bf16", dev)
+        g = torch.Generator(device=dev).manual_seed(B * 1000 + Nkv)
+        # cache contents do not change the time; drawn on the device to keep set-up short
+        tk = torch.randn(B, Nkv, T, 128, device=dev, dtype=torch.bfloat16, generator=g)
+        tv = torch.randn(B, Nkv, T, 128, device=dev, dtype=torch.bfloat16, generator=g)
+        tl = torch.from_numpy(lens).to(dev)
+        O = torch.empty_like(tq)
+        L = torch.empty((B, Nq), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, tch.attn_decode_workspace_bytes(B, Nq, Nkv, 128, T, tch.ATTN_BF16)),
+                         dtype=torch.uint8, device=dev)
+        ms = _time(torch, lambda: tch.attn_decode(tq, tk, tv, tl, O, L, ws), steps * 2, warmup)
+        _, nbytes = workloads.decode_work(lens, Nq, Nkv, 128, 2)
+        gbs = nbytes / ms / 1e6
+        print(json.dumps({"path": "attn_decode", "workload": f"B={B} lens={T} Nq={Nq} Nkv={Nkv} Dh=128 bf16",
+                          "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                          "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}),
+              flush=True)
+        del tq, tk, tv, O, L, ws
+
+
 def _head_sizes(torch, dev, tch, steps, warmup):
     """One JSON line per shape: causal MHA prefill at head sizes 64 / 128 / 256 with the same
     32-head layout, and the batched decode workload at head sizes 64 / 256 and as MQA."""
@@ -456,6 +484,9 @@ def main():
     ap.add_argument("--rope-padding", action="store_true",
                     help="time RoPE, the rotating append and the padded prefill / decode "
                          "instead of the main step")
+    ap.add_argument("--decode-batches", action="store_true",
+                    help="time decode at small batches and long context (1-8 sequences, "
+                    "32K-128K tokens) instead of the main step")
     ap.add_argument("--workloads", action="store_true",
                     help="time each named workload (the 1024-token, 32768-token and GQA window "
                     "prefills, and the decode step) in its own JSON line instead of the main step")
@@ -487,6 +518,9 @@ def main():
         return
     if args.head_sizes:
         _head_sizes(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
+        return
+    if args.decode_batches:
+        _decode_batches(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))
         return
     if args.workloads:
         _workloads(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))

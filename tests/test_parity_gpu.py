@@ -254,21 +254,23 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
 def _decode_chunk(B, Nkv, Tcap, G):
     # the host's choice of keys per chunk, restated: the longest candidate that
     # gives at least 2048 (sequence, K/V head, chunk) items at full length,
-    # 1024 with 16 or more query heads per K/V head
+    # 1024 with 16 or more query heads per K/V head, but not shorter than 640
+    # keys (224 with 16 or more query heads per K/V head)
+    floor = 224 if G >= 16 else 640
     for ch in (1792, 1152, 896, 640, 384, 224, 160, 96):
-        if B * Nkv * -(-Tcap // ch) >= (1024 if G >= 16 else 2048):
+        if ch <= floor or B * Nkv * -(-Tcap // ch) >= (1024 if G >= 16 else 2048):
             return ch
-    return 96
+    return floor
 
 
 @pytest.mark.parametrize("B,Nq,Nkv,Tcap,ch", [
-    (16, 32, 8, 3000, 160),
-    (16, 32, 8, 4000, 224),
-    (16, 32, 8, 8192, 384),
+    (16, 32, 8, 3000, 640),     # the item count alone would ask for 160
+    (9, 8, 1, 32768, 640),      # few long sequences: 96 by the item count
     (16, 32, 8, 12000, 640),
     (16, 32, 8, 16384, 896),
     (24, 32, 8, 16384, 1152),
     (16, 32, 2, 16384, 384),    # 16 query heads per K/V head: 1024 items
+    (9, 32, 1, 3000, 224),      # MQA, the floor for wide groups
     (64, 32, 1, 32768, 1792),   # MQA with 32 query heads
 ])
 def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch):
