@@ -95,6 +95,7 @@ struct DecParams {
   int n_slots;    // chunks that can hold visible keys, per (sequence, K/V head)
   int ch;         // keys per chunk (a multiple of STEP)
   int window;     // > 0: only keys lens[b] - window .. lens[b] - 1 are visible
+  int mw;         // merge: wavefronts per (sequence, query head) row, 1 to 16
   float c;        // scale * log2(e)
 };
 
@@ -485,68 +486,110 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   }
 }
 
-// One wavefront per (sequence, query head): merge the chunk partials.  Lanes
-// first read the chunks' (m, l) side by side and reduce them across the
-// wavefront; then each lane accumulates D/64 head-dims over the chunks, with
-// the chunk weights broadcast from the lane that computed them.
+// Merge the chunk partials of one (sequence, query head) row: slot x holds a
+// chunk's running max m_x (log2 units), its sum l_x and its unnormalised output
+// o_x; the row's output is sum_x 2^(m_x - M) o_x / sum_x 2^(m_x - M) l_x with
+// M = max_x m_x, and its LSE is (M + log2 of the denominator) ln 2.
+//
+// p.mw wavefronts share a row (1 to 16; blockDim.x = 64 * max(4, p.mw)), each
+// folding a contiguous run of slots under its own running max; the row's first
+// wavefront then folds the wavefronts' results, rescaled to the common max,
+// from LDS, in wavefront order.  The kernel is latency-bound (a row's partials
+// are a few KB): a wavefront requests eight partial outputs at a time, the
+// first eight together with their (m, l), before the weights are known.
 template <int D, bool KM>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
+__global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
   constexpr int PL = D / 64;  // head-dims per lane
   typedef float fvec __attribute__((ext_vector_type(PL)));
+  __shared__ fvec s_acc[16][64];
+  __shared__ float s_m[16], s_l[16];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.B * p.Nq) return;
-  const int b = row / p.Nq;
-  const int h = row % p.Nq;
+  const int wv = threadIdx.x >> 6;
+  const int mw = p.mw;
+  const int row = blockIdx.x * ((int)(blockDim.x >> 6) / mw) + wv / mw;
+  const int part = wv % mw;
+  const bool valid = row < p.B * p.Nq;
   const int G = p.G;
-  const int g = h / G;
-  const int hh = h % G;
-  const int n = min(p.lens[b], p.Tcap);
-  const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
-  // partial slot x holds chunk c_lo + x; chunks c_lo .. nc-1 wrote one
-  const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
-  const size_t part0 = ((size_t)b * p.Nkv + g) * p.n_slots * G + hh;  // slot x: part0 + x*G
+  int ns = 0;  // slots written for this row
+  size_t part0 = 0;
+  if (valid) {
+    const int b = row / p.Nq;
+    const int h = row % p.Nq;
+    const int n = min(p.lens[b], p.Tcap);
+    const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
+    // partial slot x holds chunk c_lo + x; chunks c_lo .. nc-1 wrote one
+    const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
+    ns = max(0, nc - c_lo);
+    part0 = ((size_t)b * p.Nkv + h / G) * p.n_slots * G + h % G;  // slot x: part0 + x*G
+  }
+  const int x0 = part * ns / mw, x1 = (part + 1) * ns / mw;  // this wavefront's slots
 
-  const int ns = max(0, nc - c_lo);  // slots written
-  float M = -INFINITY;
-  for (int x = lane; x < ns; x += 64) M = fmaxf(M, p.ws_ml[(part0 + (size_t)x * G) * 2]);
-  M = wave_max(M);
-  // with a key-padding mask every chunk may hold padding only (M = -inf)
-  const float Mu = (KM && M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  float Mw = -INFINITY;  // running max of the slots folded so far
+  float Ll = 0.f;        // this lane's share of the weighted l sum
   fvec acc = {};
-  for (int cb = 0; cb < ns; cb += 64) {
-    // lane j of this batch holds slot cb + j's weight
-    float wgt = 0.f;
-    if (cb + lane < ns) {
-      const size_t part = part0 + (size_t)(cb + lane) * G;
-      wgt = exp2_fast(p.ws_ml[part * 2] - Mu);
-      L = __builtin_fmaf(wgt, p.ws_ml[part * 2 + 1], L);
+  auto load_o = [&](int x) { return *reinterpret_cast<const fvec*>(p.ws_o + (part0 + (size_t)x * G) * D + lane * PL); };
+  for (int cb = x0; cb < x1; cb += 64) {
+    const int cnt = min(64, x1 - cb);
+    // lane j holds slot cb + j's (m, l); lanes past the run hold a zero weight
+    float m = -INFINITY, l = 0.f;
+    if (lane < cnt) {
+      const float2 v = *reinterpret_cast<const float2*>(p.ws_ml + (part0 + (size_t)(cb + lane) * G) * 2);
+      m = v.x;
+      l = v.y;
     }
-    const int cnt = min(64, ns - cb);
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {
-      fvec ov[4];
-      float wj[4];
+    fvec ov[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ov[u] = *reinterpret_cast<const fvec*>(p.ws_o + (part0 + (size_t)(cb + j + u) * G) * D + lane * PL);
-        wj[u] = __shfl(wgt, j + u, 64);
+    for (int u = 0; u < 8; ++u) ov[u] = u < cnt ? load_o(cb + u) : fvec{};
+    const float Mn = fmaxf(Mw, wave_max(m));
+    // every slot so far may hold padding only (M = -inf): weights 0, not NaN
+    const float Mu = Mn == -INFINITY ? 0.f : Mn;
+    const float r = exp2_fast(Mw - Mu);
+    acc = acc * r;
+    const float wgt = exp2_fast(m - Mu);
+    Ll = __builtin_fmaf(wgt, l, Ll * r);
+    Mw = Mn;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = __shfl(wgt, u, 64);
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wu, ov[u][e], acc[e]);
+    }
+    for (int j = 8; j < cnt; j += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ov[u] = j + u < cnt ? load_o(cb + j + u) : fvec{};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __shfl(wgt, j + u, 64);
+#pragma unroll
+        for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wu, ov[u][e], acc[e]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wj[u], ov[u][e], acc[e]);
-    }
-    for (; j < cnt; ++j) {
-      const fvec ov = *reinterpret_cast<const fvec*>(p.ws_o + (part0 + (size_t)(cb + j) * G) * D + lane * PL);
-      const float wj = __shfl(wgt, j, 64);
-#pragma unroll
-      for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wj, ov[e], acc[e]);
     }
   }
-  L = wave_sum(L);
-  // n < 1 leaves L = 0: a NaN row, or O = 0 and LSE = -inf with a key-padding mask
+  float M = Mw;
+  float L = wave_sum(Ll);
+  if (mw > 1) {
+    s_acc[wv][lane] = acc;
+    if (lane == 0) {
+      s_m[wv] = Mw;
+      s_l[wv] = L;
+    }
+    __syncthreads();
+    if (part != 0) return;
+    for (int w = 1; w < mw; ++w) M = fmaxf(M, s_m[wv + w]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float r0 = exp2_fast(Mw - Mu);
+    acc = acc * r0;
+    L *= r0;
+    for (int w = 1; w < mw; ++w) {
+      const float r = exp2_fast(s_m[wv + w] - Mu);
+      const fvec o = s_acc[wv + w][lane];
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(r, o[e], acc[e]);
+      L = __builtin_fmaf(r, s_l[wv + w], L);
+    }
+  }
+  if (!valid) return;
+  // no slot (n < 1) leaves L = 0: a NaN row, or O = 0 and LSE = -inf with a key-padding mask
   const float inv = (KM && L == 0.f) ? 0.f : 1.f / L;
   __bf16* dst = p.O + (size_t)row * D + lane * PL;
 #pragma unroll
@@ -585,10 +628,14 @@ int decode_bf16_chunk(int B, int Nkv, int L, int G) {
   return floor_ch;
 }
 
+#ifndef DEC_MERGE_SLOTS
+#define DEC_MERGE_SLOTS 12
+#endif
+
 namespace {
 // chunk length and partial slots per (sequence, K/V head)
 struct DecodePlan {
-  int ch, n_slots;
+  int ch, n_slots, mw;
 };
 DecodePlan decode_plan(int B, int Nq, int Nkv, int Tcap, int window) {
   const int L = (window > 0 && window < Tcap) ? window : Tcap;
@@ -597,6 +644,10 @@ DecodePlan decode_plan(int B, int Nq, int Nkv, int Tcap, int window) {
   const int all = (Tcap + d.ch - 1) / d.ch;
   // a window of L keys starting anywhere touches at most ceil(L / ch) + 1 chunks
   d.n_slots = L < Tcap ? std::min(all, (L + d.ch - 1) / d.ch + 1) : all;
+  // merge: enough wavefronts per row that each folds at most DEC_MERGE_SLOTS
+  // slots (one or two rounds of eight requests)
+  d.mw = 1;
+  while (d.mw < 16 && (d.n_slots + d.mw - 1) / d.mw > DEC_MERGE_SLOTS) d.mw *= 2;
   return d;
 }
 
@@ -607,7 +658,10 @@ hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Nq;
-  hipLaunchKernelGGL((decode_merge_kernel<D, KM>), dim3((rows + 3) / 4), dim3(256), 0, stream, p);
+  const int wpb = p.mw < 4 ? 4 : p.mw;  // wavefronts per block
+  const int rpb = wpb / p.mw;           // rows per block
+  hipLaunchKernelGGL((decode_merge_kernel<D, KM>), dim3((rows + rpb - 1) / rpb), dim3(64 * wpb), 0,
+                     stream, p);
   return hipGetLastError();
 }
 template <int D, int NB>
@@ -650,6 +704,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   p.Tcap = Tcap;
   p.ch = d.ch;
   p.n_slots = d.n_slots;
+  p.mw = d.mw;
   const size_t parts = (size_t)B * Nq * p.n_slots;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * Dh;
