@@ -51,6 +51,9 @@
 // Variant knobs (compile-time): 32-query blocks per wave, waves per
 // workgroup, and whether the next tile's QK^T is issued before this tile's
 // softmax (needs a second score buffer).
+#ifndef PREFILL_SMALL_NW4
+#define PREFILL_SMALL_NW4 1
+#endif
 #ifndef PREFILL_QB
 #define PREFILL_QB 1
 #endif
@@ -178,7 +181,10 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
 // KM: a key-padding mask is given (p.kbits); without it the kernel is
 // compiled exactly as if the mask did not exist.
 template <int D, int NW, bool KM>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(Params p) {
+// Head size 128 also runs as 4 waves (one per SIMD) with two workgroups per CU
+// (at most 256 registers per lane), for grids that would fill the chip only
+// once with 8-wave workgroups.
+__global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : 1) void prefill_kernel(Params p) {
   using geo = Geo<D>;
   constexpr int TILE = geo::TILE;
   constexpr int KS = geo::KS;
@@ -558,31 +564,55 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.window = window;
   p.c = scale * kLog2e;
   p.G = Nq / Nkv;
-  p.hp = (p.G % 4 == 0 && NW % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
-  p.n_hsub = p.G / p.hp;
-  p.qspan = (NW / p.hp) * 32 * QB;
-  p.n_qtiles = (S + p.qspan - 1) / p.qspan;
-  const long long nblocks = (long long)p.n_qtiles * B * Nkv * p.n_hsub;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  // query blocks per workgroup and the grid for nw waves per workgroup
+  auto geometry = [&](int nw) {
+    p.hp = (p.G % 4 == 0 && nw % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.n_hsub = p.G / p.hp;
+    p.qspan = (nw / p.hp) * 32 * QB;
+    p.n_qtiles = (S + p.qspan - 1) / p.qspan;
+    return (long long)p.n_qtiles * B * Nkv * p.n_hsub;
+  };
+  long long nblocks = geometry(NW);
+  // A plain prefill whose grid of 8-wave workgroups fills the chip at most
+  // once runs as 4-wave workgroups, two per CU: twice the workgroups, and the
+  // two on a CU do not wait at each other's barriers, so one's softmax
+  // overlaps the other's matrix work.  Each wave computes the same rows
+  // either way.  (A chunk against a long cache stays on 8 waves: there the
+  // second copy of every K/V tile per CU costs more than the overlap gains.)
+  const bool small = D == 128 && NW == 8 && PREFILL_SMALL_NW4 && lens == nullptr && n_cu > 0 &&
+                     nblocks <= n_cu;
+  if (small) nblocks = geometry(4);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // A causal prefill whose grid runs in one round lasts as long as its
   // heaviest workgroup: with consecutive query blocks the last tile of a head
   // sees n_qtiles times the keys of the first.  Strided blocks give every
   // workgroup the same mix (a window keeps them consecutive: strided blocks
-  // would make each workgroup stream most of the sequence).
-  p.strided = 0;
-  if (causal && window == 0 && lens == nullptr && p.n_qtiles > 1) {
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        nblocks <= n_cu)
-      p.strided = 1;
+  // would make each workgroup stream most of the sequence).  The 4-wave
+  // form is faster with consecutive blocks.
+  p.strided = !small && causal && window == 0 && lens == nullptr && p.n_qtiles > 1 &&
+              nblocks <= n_cu;
+  if constexpr (D == 128 && NW == 8) {
+    if (small) {
+      if (kbits)
+        hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3((unsigned)nblocks), dim3(256), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((prefill_kernel<D, 4, false>), dim3((unsigned)nblocks), dim3(256), 0,
+                           stream, p);
+      return hipGetLastError();
+    }
   }
-  if (kbits)
+  if (kbits) {
     hipLaunchKernelGGL((prefill_kernel<D, NW, true>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                        stream, p);
-  else
+  } else {
     hipLaunchKernelGGL((prefill_kernel<D, NW, false>), dim3((unsigned)nblocks), dim3(NW * 64), 0,
                        stream, p);
+  }
   return hipGetLastError();
 }
 
