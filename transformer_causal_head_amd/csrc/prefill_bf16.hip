@@ -89,7 +89,7 @@ constexpr float TAU = 8.f;
 
 // waves per workgroup: two per SIMD while the registers allow it
 template <int D>
-constexpr int waves_for() { return D == 128 ? PREFILL_NW : (D < 128 ? 8 : 4); }
+constexpr int waves_for() { return D == 128 ? PREFILL_NW : 4; }
 
 struct Params {
   const __bf16* Q;
@@ -183,8 +183,10 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
 template <int D, int NW, bool KM>
 // Head size 128 also runs as 4 waves (one per SIMD) with two workgroups per CU
 // (at most 256 registers per lane), for grids that would fill the chip only
-// once with 8-wave workgroups.
-__global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : 1) void prefill_kernel(Params p) {
+// once with 8-wave workgroups.  Head size 64 always runs as 4 waves with three
+// workgroups per CU (at most 168 registers; two with a key-padding mask, whose
+// extra registers would spill at that bound).
+__global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && NW == 4) ? (KM ? 2 : 3) : 1)) void prefill_kernel(Params p) {
   using geo = Geo<D>;
   constexpr int TILE = geo::TILE;
   constexpr int KS = geo::KS;
