@@ -42,7 +42,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,        /* null pointer, non-positive size, bad flag/scale  */
   ATTN_EGQA = -2,          /* Nq is not a multiple of Nkv                      */
-  ATTN_EUNSUPPORTED = -3,  /* dtype or head size outside what is implemented   */
+  ATTN_EUNSUPPORTED = -3,  /* dtype or head size outside what is implemented,
+                              or a head too long for the bf16 MFMA kernels      */
   ATTN_EWORKSPACE = -4,    /* workspace missing or smaller than required       */
   ATTN_EHIP = -5           /* HIP runtime reported an error at launch          */
 } attn_status;
@@ -67,6 +68,9 @@ typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
  *   dtype    attn_dtype of Q, K, V and O.
  * Supported: Dh in 1..256 for both dtypes; bf16 with Dh in {64, 128, 256}
  * takes the MFMA kernel, the rest a general kernel.  B, Nq, Nkv, S >= 1.
+ * The MFMA kernel addresses one head through a 31-bit byte range: it needs
+ * S * Dh * 2 < 2^31 (S <= 8388607 at Dh = 128); longer heads return
+ * ATTN_EUNSUPPORTED before anything is launched.
  * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -95,7 +99,8 @@ int attn_prefill(const void* Q, const void* K, const void* V, void* O, float* LS
  * or past lens[b] are never read.  With Sq == lens[b] this is attn_prefill.
  * lens lives on the device: values above Tcap are clamped to Tcap, and a
  * value below Sq leaves rows with no visible key (NaN).
- * Supported: as attn_prefill (bf16 Dh in {64, 128, 256} takes the MFMA kernel).
+ * Supported: as attn_prefill (bf16 Dh in {64, 128, 256} takes the MFMA kernel,
+ * which needs Tcap * Dh * 2 < 2^31, else ATTN_EUNSUPPORTED).
  * Errors: ATTN_EINVAL (also Sq > Tcap), ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_prefill_cache(const void* Q, const void* Kcache, const void* Vcache,
@@ -216,7 +221,8 @@ size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int 
  *   workspace / workspace_bytes     device scratch of at least
  *                                   attn_backward_workspace_bytes(...) bytes
  * dQ, dK, dV are written in the element type of the inputs (accumulation in
- * fp32); they are overwritten, not accumulated into.
+ * fp32); they are overwritten, not accumulated into.  bf16 with Dh 64 or 128
+ * runs the MFMA kernels, which need S * Dh * 2 < 2^31 (else ATTN_EUNSUPPORTED).
  * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP.
  */
 int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -94,6 +94,10 @@ def _prefill(**kw):
     (dict(scale=-1.0), tch.ATTN_EINVAL),
     (dict(scale=float("inf")), tch.ATTN_EINVAL),
     (dict(scale=float("nan")), tch.ATTN_EINVAL),
+    # one head of the MFMA kernel must fit a 31-bit byte range
+    (dict(S=8388608), tch.ATTN_EUNSUPPORTED),
+    (dict(S=16777216, Dh=64), tch.ATTN_EUNSUPPORTED),
+    (dict(S=4194304, Dh=256), tch.ATTN_EUNSUPPORTED),
 ])
 def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
@@ -156,6 +160,7 @@ def _prefill_cache(**kw):
     (dict(dtype=3), tch.ATTN_EUNSUPPORTED),
     (dict(scale=0.0), tch.ATTN_EINVAL),
     (dict(scale=float("nan")), tch.ATTN_EINVAL),
+    (dict(Tcap=8388608), tch.ATTN_EUNSUPPORTED),
 ])
 def test_prefill_cache_rejects(kw, code):
     assert _prefill_cache(**kw) == code
@@ -237,6 +242,7 @@ def _backward(**kw):
     (dict(Dh=512), tch.ATTN_EUNSUPPORTED),
     (dict(ws=None), tch.ATTN_EWORKSPACE),
     (dict(ws_bytes=4), tch.ATTN_EWORKSPACE),
+    (dict(S=8388608), tch.ATTN_EUNSUPPORTED),
 ])
 def test_backward_rejects(kw, code):
     assert _backward(**kw) == code

@@ -21,6 +21,10 @@ int validate_common(int B, int Nq, int Nkv, int Dh, int dtype) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
+// The bf16 MFMA kernels address one head of a tensor (rows x Dh bf16 values)
+// through a buffer descriptor with a 31-bit byte range.
+bool mfma_head_fits(long long rows, int Dh) { return rows * Dh * 2 <= 0x7fffffffLL; }
+
 }  // namespace
 
 static int prefill_impl(const void* Q, const void* K, const void* V, const uint64_t* kbits,
@@ -34,6 +38,8 @@ static int prefill_impl(const void* Q, const void* K, const void* V, const uint6
   if (window > 0 && !causal) return ATTN_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
+  if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh) && !mfma_head_fits(S, Dh))
+    return ATTN_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
@@ -52,6 +58,8 @@ static int prefill_cache_impl(const void* Q, const void* Kcache, const void* Vca
   if (!positive(Sq) || !positive(Tcap) || Sq > Tcap) return ATTN_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
+  if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh) && !mfma_head_fits(Tcap, Dh))
+    return ATTN_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh,
@@ -257,6 +265,8 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
   if (window > 0 && !causal) return ATTN_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
   if (window < 0) window = 0;
+  if (dtype == ATTN_BF16 && attn::backward_bf16_supported(Dh) && !mfma_head_fits(S, Dh))
+    return ATTN_EUNSUPPORTED;
   const size_t need = attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -273,7 +283,8 @@ const char* attn_strerror(int status) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null pointer, non-positive size, bad flag or scale)";
     case ATTN_EGQA: return "number of query heads is not a multiple of the number of K/V heads";
-    case ATTN_EUNSUPPORTED: return "unsupported element type or head size";
+    case ATTN_EUNSUPPORTED:
+      return "unsupported element type or head size, or a head too long for the MFMA kernels";
     case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_EHIP: return "HIP runtime error at launch";
     default: return "unknown status";
