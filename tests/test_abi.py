@@ -137,6 +137,57 @@ def test_python_binding_refuses_cpu_tensors():
         tch.attn_prefill(q, q, q, q.clone(), None)
 
 
+def _decode_tensors(dtype=torch.bfloat16, k=None, v=None, o=None, kn=None, vn=None):
+    B, Nq, Nkv, Dh, T = 2, 4, 2, 64, 8
+    q = torch.zeros(B, Nq, Dh, dtype=dtype)
+    return dict(q=q, Kcache=torch.zeros(B, Nkv, T, Dh, dtype=k or dtype),
+                Vcache=torch.zeros(B, Nkv, T, Dh, dtype=v or dtype),
+                lens=torch.ones(B, dtype=torch.int32), O=torch.zeros(B, Nq, Dh, dtype=o or dtype),
+                knew=torch.zeros(B, Nkv, Dh, dtype=kn or dtype),
+                vnew=torch.zeros(B, Nkv, Dh, dtype=vn or dtype))
+
+
+@pytest.mark.parametrize("mix", [dict(k=torch.float32), dict(v=torch.float32),
+                                 dict(o=torch.float32), dict(kn=torch.float32),
+                                 dict(vn=torch.float32)])
+@pytest.mark.parametrize("entry", ["attn_decode", "attn_decode_window", "attn_decode_padded",
+                                   "attn_decode_append"])
+def test_decode_binding_refuses_mixed_dtypes(entry, mix):
+    # the C ABI takes q's element type for every buffer: a bf16 query with an
+    # fp32 cache (or output, or new row) must be refused before the library
+    # is called.  The tensors are on the CPU, so a call would raise too; the
+    # message shows which check fired.
+    if entry != "attn_decode_append" and ("kn" in mix or "vn" in mix):
+        pytest.skip("no new rows in this entry point")
+    t = _decode_tensors(**mix)
+    args = {"attn_decode": (t["q"], t["Kcache"], t["Vcache"], t["lens"], t["O"]),
+            "attn_decode_window": (t["q"], t["Kcache"], t["Vcache"], t["lens"], t["O"]),
+            "attn_decode_padded": (t["q"], t["Kcache"], t["Vcache"], t["lens"], None, t["O"]),
+            "attn_decode_append": (t["q"], t["knew"], t["vnew"], t["Kcache"], t["Vcache"],
+                                   t["lens"], t["lens"], t["O"])}[entry]
+    with pytest.raises(ValueError, match="share one dtype"):
+        getattr(tch, entry)(*args)
+
+
+@pytest.mark.parametrize("entry", ["attn_prefill", "attn_decode", "attn_prefill_cache"])
+def test_binding_requires_float32_lse(entry):
+    # LSE is fp32 in the C ABI: a 4-byte integer tensor must be refused
+    if entry == "attn_decode":
+        t = _decode_tensors()
+        lse = torch.zeros(2, 4, dtype=torch.int32)
+        call = lambda: tch.attn_decode(t["q"], t["Kcache"], t["Vcache"], t["lens"], t["O"], lse)
+    else:
+        q = torch.zeros(1, 2, 4, 8, dtype=torch.bfloat16)
+        lse = torch.zeros(1, 2, 4, dtype=torch.int32)
+        if entry == "attn_prefill":
+            call = lambda: tch.attn_prefill(q, q, q, q.clone(), lse)
+        else:
+            call = lambda: tch.attn_prefill_cache(q, q, q, torch.full((1,), 4, dtype=torch.int32),
+                                                  q.clone(), lse)
+    with pytest.raises(ValueError, match="LSE must be float32"):
+        call()
+
+
 def _prefill_cache(**kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, lens=FAKE, O=FAKE, LSE=None, B=2, Nq=8, Nkv=2, Sq=16,
              Dh=128, Tcap=64, window=0, scale=0.125, dtype=tch.ATTN_BF16, stream=None)

@@ -143,11 +143,13 @@ def test_kv_append(dtype, Dh, Snew, Tcap, pos, rolling):
     assert np.array_equal(workloads.from_torch(tv, dtype), Vr)
 
 
-@pytest.mark.parametrize("mode", ["rolling", "linear"])
+@pytest.mark.parametrize("mode", ["rolling", "linear", "fused"])
 def test_generation_over_window_cache(mode):
     # the textbook's walk-through at attention-kernel scale: a 200-token prompt
     # by chunked prefill, then 40 tokens one at a time, window 64; each output
-    # row must match the one-pass oracle
+    # row must match the one-pass oracle.  "fused" appends each token inside
+    # the decode call (attn_decode_append) on a linear cache that holds NaN in
+    # every row not yet written
     Nq, Nkv, Dh, T, P, W = 32, 8, 128, 240, 200, 64
     q, k, v = workloads.prefill_inputs(1, Nq, Nkv, T, Dh, "bf16", seed=91)
     Or, Lr = oracle.attention_ref(*(workloads.to_f64(x, "bf16") for x in (q, k, v)),
@@ -170,9 +172,22 @@ def test_generation_over_window_cache(mode):
                        rolling=int(mode == "rolling"))
     for t in range(P, T):
         pos = torch.tensor([t], dtype=torch.int32, device=dev)
+        qt = tq[:, :, t].contiguous()
+        if mode == "fused":
+            O = torch.empty_like(qt)
+            L = torch.empty((1, Nq), dtype=torch.float32, device=dev)
+            ws = torch.empty(tch.attn_decode_window_workspace_bytes(1, Nq, Nkv, Dh, cap, W,
+                                                                    tch.ATTN_BF16),
+                             dtype=torch.uint8, device=dev)
+            tch.attn_decode_append(qt, tk[:, :, t].contiguous(), tv[:, :, t].contiguous(), Kc, Vc,
+                                   pos + 1, pos, O, L, ws, window=W)
+            torch.cuda.synchronize()
+            check(workloads.to_f64(workloads.from_torch(O, "bf16"), "bf16"),
+                  L.cpu().numpy().astype(np.float64), Or[:, :, t], Lr[:, :, t], "bf16", (mode, t),
+                  storage_allowance=True)
+            continue
         tch.attn_kv_append(tk[:, :, t:t + 1].contiguous(), tv[:, :, t:t + 1].contiguous(), Kc, Vc,
                            pos, rolling=int(mode == "rolling"))
-        qt = tq[:, :, t].contiguous()
         if mode == "rolling":   # the buffer holds exactly the window: attend to all of it
             O, L = tch.decode(qt, Kc, Vc, torch.tensor([min(t + 1, W)], dtype=torch.int32,
                                                        device=dev))
@@ -208,6 +223,11 @@ def test_decode_append(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, rolling, unali
     else:
         slot = lens_a - 1
     tq, tk, tv = (workloads.to_torch(a, dtype, dev) for a in (q, kc, vc))
+    # the new token's row has never been written (an empty cache slot): NaN
+    # before the call, so nothing may read its old bytes
+    for b in range(B):
+        tk[b, :, int(slot[b])] = float("nan")
+        tv[b, :, int(slot[b])] = float("nan")
     tk2, tv2 = tk.clone(), tv.clone()
     tkn, tvn = (workloads.to_torch(a, dtype, dev) for a in (kn, vn))
     if unaligned:  # the same values 2 bytes into a buffer: the two-launch path

@@ -172,6 +172,12 @@ def _check_bits(key_bits, B, T):
         raise ValueError(f"key_bits must be int64 [B, ceil({T} / 64)]")
 
 
+def _check_lse(LSE, shape):
+    import torch
+    if LSE is not None and (tuple(LSE.shape) != tuple(shape) or LSE.dtype != torch.float32):
+        raise ValueError(f"LSE must be float32 {list(shape)}")
+
+
 def _check_prefill(Q, K, V, O, LSE):
     B, Nq, S, Dh = Q.shape
     Nkv = K.shape[1]
@@ -179,8 +185,7 @@ def _check_prefill(Q, K, V, O, LSE):
         raise ValueError("shape mismatch between Q, K, V, O")
     if not (Q.dtype == K.dtype == V.dtype == O.dtype):
         raise ValueError("Q, K, V, O must share one dtype")
-    if LSE is not None and (tuple(LSE.shape) != (B, Nq, S) or LSE.dtype.itemsize != 4):
-        raise ValueError("LSE must be fp32 [B, Nq, S]")
+    _check_lse(LSE, (B, Nq, S))
     return B, Nq, Nkv, S, Dh
 
 
@@ -225,8 +230,10 @@ def _check_decode(q, Kcache, Vcache, lens, O, LSE):
         raise ValueError("cache shapes must be [B, Nkv, Tcap, Dh]")
     if O.shape != q.shape or lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
         raise ValueError("O must match q; lens must be int32 [B]")
-    if LSE is not None and (tuple(LSE.shape) != (B, Nq) or LSE.dtype.itemsize != 4):
-        raise ValueError("LSE must be fp32 [B, Nq]")
+    # the C ABI takes one element type (q's): the caches and O must have it too
+    if not (q.dtype == Kcache.dtype == Vcache.dtype == O.dtype):
+        raise ValueError("q, Kcache, Vcache and O must share one dtype")
+    _check_lse(LSE, (B, Nq))
     return B, Nq, Nkv, Dh, Tcap
 
 
@@ -268,8 +275,7 @@ def attn_prefill_cache(Q, Kcache, Vcache, lens, O, LSE, window=0, scale=None, st
         raise ValueError("O must match Q; lens must be int32 [B]")
     if not (Q.dtype == Kcache.dtype == Vcache.dtype == O.dtype):
         raise ValueError("Q, caches and O must share one dtype")
-    if LSE is not None and (tuple(LSE.shape) != (B, Nq, Sq) or LSE.dtype.itemsize != 4):
-        raise ValueError("LSE must be fp32 [B, Nq, Sq]")
+    _check_lse(LSE, (B, Nq, Sq))
     if scale is None:
         scale = 1.0 / math.sqrt(Dh)
     if key_bits is None:
@@ -320,8 +326,8 @@ def attn_decode_append(q, knew, vnew, Kcache, Vcache, lens, slot, O, LSE=None, w
     B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
     if tuple(knew.shape) != (B, Nkv, Dh) or knew.shape != vnew.shape:
         raise ValueError("knew and vnew must be [B, Nkv, Dh]")
-    if not (q.dtype == knew.dtype == vnew.dtype == Kcache.dtype):
-        raise ValueError("q, new rows and caches must share one dtype")
+    if not (q.dtype == knew.dtype == vnew.dtype == Kcache.dtype == Vcache.dtype == O.dtype):
+        raise ValueError("q, new rows, caches and O must share one dtype")
     if slot.dtype != torch.int32 or tuple(slot.shape) != (B,):
         raise ValueError("slot must be int32 [B]")
     if scale is None:
@@ -447,8 +453,9 @@ def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=Non
         raise ValueError("dK, dV must have the shape of K")
     if len({t.dtype for t in (Q, K, V, O, dO, dQ, dK, dV)}) != 1:
         raise ValueError("all tensors but LSE must share one dtype")
-    if tuple(LSE.shape) != (B, Nq, S) or LSE.dtype.itemsize != 4:
-        raise ValueError("LSE must be fp32 [B, Nq, S]")
+    if LSE is None:
+        raise ValueError("LSE is required")
+    _check_lse(LSE, (B, Nq, S))
     if scale is None:
         scale = 1.0 / math.sqrt(Dh)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -112,16 +112,24 @@ size_t attn_decode_workspace_bytes(int B, int Nq, int Nkv, int Dh, int Tcap, int
   return attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, 0, dtype);
 }
 
-static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
-                       const int32_t* lens, const uint64_t* kbits, void* O, int B, int Nq,
-                       int Nkv, int Dh, int Tcap,
-                       int window, float scale, float* LSE, void* workspace,
-                       size_t workspace_bytes, int dtype, void* stream) {
+static int decode_check(const void* q, const void* Kcache, const void* Vcache,
+                        const int32_t* lens, const void* O, int B, int Nq, int Nkv, int Dh,
+                        int Tcap, float scale, int dtype) {
   if (!q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
   if (!positive(Tcap)) return ATTN_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
+                       const int32_t* lens, const uint64_t* kbits, void* O, int B, int Nq,
+                       int Nkv, int Dh, int Tcap,
+                       int window, float scale, float* LSE, void* workspace,
+                       size_t workspace_bytes, int dtype, void* stream) {
+  int st = decode_check(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, scale, dtype);
+  if (st != ATTN_OK) return st;
   if (window < 0) window = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t need = attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype);
