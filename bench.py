@@ -79,12 +79,24 @@ def _cpu_baseline(q, k, v, cfg, budget_s=12.0):
                       f"float64 NumPy full score rows"}
 
 
+PROBE_LIB = os.path.join(ROOT, "_build", "libhbm_probe.so")
+
+
+def _build_probe():
+    """Compile hbm_probe.hip (benchmark tooling, not the library) into _build/."""
+    from transformer_causal_head_amd import build as lib_build
+    os.makedirs(os.path.dirname(PROBE_LIB), exist_ok=True)
+    obj = lib_build._compile("hbm_probe.hip", ROOT, os.path.dirname(PROBE_LIB))
+    lib_build._link([obj], PROBE_LIB)
+    print("built", PROBE_LIB)
+
+
 def _read_ceiling(torch, dev, gib=4.5, reps=5):
-    """Streaming-read rate of the device (libhbm_probe.so) for a few launch shapes."""
+    """Streaming-read rate of the device (hbm_probe.hip) for a few launch shapes."""
     import ctypes
-    path = os.path.join(ROOT, "transformer_causal_head_amd", "libhbm_probe.so")
+    path = PROBE_LIB
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build the package first")
+        raise RuntimeError(f"{path} is missing: run `python bench.py --build-probe` first")
     L = ctypes.CDLL(path)
     L.hbm_read_probe.restype = ctypes.c_int
     L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
@@ -475,6 +487,8 @@ def main():
                     help="run only a 1 GiB device copy (counter calibration)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run only the streaming-read probe over 4.5 GB (HBM reference point)")
+    ap.add_argument("--build-probe", action="store_true",
+                    help="compile the streaming-read probe (hbm_probe.hip) and exit")
     ap.add_argument("--head-sizes", action="store_true",
                     help="time prefill and decode at head sizes 64 / 256 and decode with 32 "
                          "query heads per K/V head instead of the main step")
@@ -493,6 +507,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) instead of the main step")
     args = ap.parse_args()
+    if args.build_probe:
+        _build_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this path runs without sharding or collectives)", file=sys.stderr)

@@ -1,7 +1,8 @@
 // Streaming-read probe: the practical HBM read rate of the device, the
-// reference point for the decode kernel's roofline.  Not part of the attention
-// path; built into its own library (libhbm_probe.so) and called only by the
-// benchmark's read-ceiling mode.
+// reference point for the decode kernel's roofline.  Measurement tooling of
+// the benchmark, not part of the attention library: `python bench.py
+// --build-probe` compiles it into _build/libhbm_probe.so, and `python bench.py
+// --read-ceiling` calls it.
 //
 // Each lane reads 16-byte words, `unroll` of them in flight, grid-stride over
 // the buffer, and XOR-folds them so no load can be dropped; a lane writes the

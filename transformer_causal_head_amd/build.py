@@ -2,10 +2,9 @@
 
     python -m transformer_causal_head_amd.build
 
-Objects go to ``_build/`` beside this file; the attention library to
-``libattn.so``, and the streaming-read probe the benchmark uses as its HBM
-reference point to ``libhbm_probe.so``.  Packed fp32 VALU instructions are
-disabled for all device code.
+Objects go to ``_build/`` beside this file and the attention library to
+``libattn.so``.  Packed fp32 VALU instructions are disabled for all device
+code.
 """
 
 import os
@@ -17,13 +16,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "general.hip", "cache.hip", "backward.hip", "backward_bf16.hip", "rope.hip", "keymask.hip",
            "attn_api.cpp"]
-PROBE_SOURCES = ["hbm_probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -32,9 +29,9 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, src_dir=CSRC, build_dir=BUILD):
+    obj = os.path.join(build_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(src_dir, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,13 +51,11 @@ def _link(objs, out):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
-    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB)
     if verbose:
-        print("built", LIB, "and", PROBE_LIB)
+        print("built", LIB)
     return LIB
 
 

@@ -31,15 +31,6 @@
 #include "kernels.h"
 #include "tiles.h"
 
-// dK / dV on two wavefronts per 32 keys with the weights passed through LDS
-// (dkv_pipe_kernel, 1) or on one wavefront per 32 keys (dkv_kernel, 0), at
-// head size 128 and at head size 64.
-#ifndef BWD_PAIR128
-#define BWD_PAIR128 1
-#endif
-#ifndef BWD_PAIR64
-#define BWD_PAIR64 0
-#endif
 
 namespace attn {
 
@@ -720,7 +711,10 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   p.qspan = (NWQ / p.hp) * 32;
   p.n_qtiles = (p.S + p.qspan - 1) / p.qspan;
   const long long nq = (long long)p.n_qtiles * p.B * p.Nkv * p.n_hsub;
-  constexpr bool pair = D == 128 ? BWD_PAIR128 != 0 : BWD_PAIR64 != 0;
+  // dK / dV: at head size 128 on two wavefronts per 32 keys with the weights
+  // passed through LDS (dkv_pipe_kernel), at head size 64 on one wavefront per
+  // 32 keys (dkv_kernel)
+  constexpr bool pair = D == 128;
   const long long nk = pair ? (long long)((p.S + 127) / 128) * p.B * p.Nkv
                             : (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;

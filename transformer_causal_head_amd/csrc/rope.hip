@@ -28,11 +28,6 @@
 #include "common.h"
 #include "kernels.h"
 
-// Rows of X / Y (read once, written once) bypass the caches' retention with
-// non-temporal accesses; the table rows, reread by every head, do not.
-#ifndef ROPE_NT
-#define ROPE_NT 1
-#endif
 
 namespace attn {
 
@@ -105,7 +100,9 @@ __device__ __forceinline__ void store_row(T* dst, const float (&src)[N]) {
 template <typename T, int PP, int STYLE, bool VEC>
 __device__ __forceinline__ void rotate_pairs(const T* x, T* y, const float* cs, int half, int j,
                                              int tpr) {
-  constexpr bool NTX = VEC && ROPE_NT != 0;
+  // rows of X / Y (read once, written once) bypass the caches' retention with
+  // non-temporal accesses; the table rows, reread by every head, do not
+  constexpr bool NTX = VEC;
   if constexpr (STYLE == 0 && VEC) {
     // pairs layout, 16-byte vectors: a chunk of E elements holds CP whole
     // pairs; thread j takes chunks j, j + tpr, ..., so that every load
