@@ -7,6 +7,10 @@ One step is one pass of the whole path over one batch of synthetic input:
     (the long-context workload; 8.796e12 algorithmic FLOPs per call), then
   * one KV-cache decode step, bf16, 64 sequences, 32 query / 8 K/V heads,
     Dh=128, cached lengths uniform in [1024, 32768].
+After the timed steps the two other bf16 prefill workloads are timed on their
+own and reported as sub-objects: grouped-query 32/8 heads, B=4, S=8192,
+window 4096 (`gqa_window`), and B=2, 32 heads, S=1024 over eight rotating
+input sets (`mha_s1024`).
 Inputs are seeded N(0,1) draws (see workloads/), resident in HBM before the
 timed region.  W untimed steps, then K timed steps bracketed by device
 synchronisation; kernel durations come from HIP events recorded on the stream
@@ -34,6 +38,9 @@ import workloads  # noqa: E402
 
 PREFILL = "mha_bf16_b1_h32_s32768_d128"
 DECODE = "decode_bf16_b64_h32kv8_t32768_d128"
+# the other two bf16 prefill workloads, timed on their own after the main step
+GQA_WINDOW = "gqa_bf16_b4_h32kv8_s8192_w4096_d128"
+MHA_S1024 = "mha_bf16_b2_h32_s1024_d128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
@@ -141,6 +148,36 @@ def _time(torch, fn, steps, warmup):
     b.record(stream)
     b.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def _prefill_line(torch, dev, tch, name, steps, warmup, sets):
+    """Time one named bf16 prefill workload on its own (HIP events on the launch stream):
+    `sets` input sets drawn with seeds 0.. are used in rotation, so that a workload small
+    enough for the 256 MB last-level cache still reads its inputs from HBM."""
+    cfg = workloads.WORKLOADS[name]
+    B, Nq, Nkv, S, Dh = cfg["B"], cfg["Nq"], cfg["Nkv"], cfg["S"], cfg["Dh"]
+    inputs = []
+    for i in range(sets):
+        q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=i)
+        inputs.append(tuple(workloads.to_torch(x, "bf16", dev) for x in (q, k, v)))
+        del q, k, v
+    O = torch.empty_like(inputs[0][0])
+    L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(Dh)
+    state = {"i": 0}
+
+    def call():
+        tq, tk, tv = inputs[state["i"] % sets]
+        state["i"] += 1
+        tch.attn_prefill(tq, tk, tv, O, L, causal=int(cfg["causal"]), window=cfg["window"],
+                         scale=scale)
+    ms = _time(torch, call, steps, max(warmup, sets))
+    flop, nbytes = workloads.prefill_work(B, Nq, Nkv, S, Dh, cfg["causal"], cfg["window"], 2)
+    tf = flop / (ms * 1e-3) / 1e12
+    del inputs, O, L
+    return {"workload": name, "ms": round(ms, 5), "tflops": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "calls": steps,
+            "input_sets": sets, "algorithmic_flop": flop, "compulsory_bytes": nbytes}
 
 
 def _cache_paths(torch, dev, tch, steps, warmup):
@@ -599,6 +636,14 @@ def main():
     tflops = pflops / (pre_ms * 1e-3) / 1e12
     gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
+    # the GQA sliding-window and 1024-token prefills, each timed on its own (the
+    # 1024-token calls rotate over eight input sets, about 400 MB, and run back to back)
+    del tq, tk, tv, O, LSE, tdq, tkc, tvc, dO, dL, ws
+    torch.cuda.empty_cache()
+    print("timing the GQA window and 1024-token prefills", file=sys.stderr, flush=True)
+    gqa = _prefill_line(torch, dev, tch, GQA_WINDOW, args.steps, args.warmup, 1)
+    short = _prefill_line(torch, dev, tch, MHA_S1024, args.steps * 20, args.warmup, 8)
+
     sha = _kernel_sha("prefill_bf16.hip")
     traffic = TRAFFIC["prefill_bf16.hip"].get(sha)
     dsha = _kernel_sha("decode_bf16.hip")
@@ -632,6 +677,8 @@ def main():
         "decode": {"ms": round(dec_ms, 4), "value": round(gbs, 1), "unit": "GB/s",
                    "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                    "algorithmic_bytes": dbytes, "traffic": dtraffic, "kernel_sha": dsha},
+        "gqa_window": gqa,
+        "mha_s1024": short,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill_kernel", "kernel_sha": sha},
