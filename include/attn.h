@@ -15,7 +15,9 @@
  *   - All tensor pointers are DEVICE pointers to dense row-major (contiguous)
  *     buffers owned by the caller.  The library never allocates, frees,
  *     synchronises or keeps a pointer after the call returns; the caller keeps
- *     every buffer alive until the stream has passed the call.
+ *     every buffer alive until the stream has passed the call.  The one
+ *     buffer of its own is attn_decode_noalloc's fixed scratch array (see
+ *     there).
  *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *     Work is enqueued asynchronously on it.
  *   - Return value: ATTN_OK (0) or a negative attn_status.  Argument errors
@@ -26,7 +28,8 @@
  *     multiple of Nkv (MHA: Nkv == Nq, MQA: Nkv == 1).
  *   - Element types: ATTN_BF16 (inputs and O in bfloat16, accumulation in
  *     fp32) or ATTN_F32.  LSE is always fp32.
- *   - The library is stateless and re-entrant.
+ *   - The library is stateless and re-entrant, apart from that scratch array,
+ *     which calls of attn_decode_noalloc on one device share.
  */
 #ifndef TCH_ATTN_H
 #define TCH_ATTN_H
@@ -45,7 +48,9 @@ typedef enum {
   ATTN_EUNSUPPORTED = -3,  /* dtype or head size outside what is implemented,
                               or a head too long for the bf16 MFMA kernels      */
   ATTN_EWORKSPACE = -4,    /* workspace missing or smaller than required       */
-  ATTN_EHIP = -5           /* HIP runtime reported an error at launch          */
+  ATTN_EHIP = -5,          /* HIP runtime reported an error at launch          */
+  ATTN_ESCRATCH = -6       /* attn_decode_noalloc: the call needs more scratch
+                              than ATTN_NOALLOC_SCRATCH_BYTES                   */
 } attn_status;
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
@@ -143,6 +148,32 @@ int attn_decode(const void* q, const void* Kcache, const void* Vcache,
                 int B, int Nq, int Nkv, int Dh, int Tcap,
                 float* LSE, void* workspace, size_t workspace_bytes,
                 int dtype, void* stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same result bit for bit.  The split-K partials go to a
+ * scratch array of ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on, from the first call on that device until the process
+ * ends; the call itself allocates and frees nothing.
+ *   Limit: attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype) must not
+ *   exceed ATTN_NOALLOC_SCRATCH_BYTES (the 64-sequence, 32/8-head, 32768-slot
+ *   cache at Dh 128 needs 20.2 MB); larger calls return ATTN_ESCRATCH before
+ *   anything is enqueued.  Shapes that need no workspace (fp32, the general
+ *   kernel) use no scratch.
+ *   Concurrency: every call on one device shares that device's scratch and
+ *   leaves its contents behind (nothing in it needs clearing: each call
+ *   writes every partial it reads).  Calls that overlap on one device -- on
+ *   two streams, or from two host threads without ordering -- race on it;
+ *   order them on one stream.
+ * Errors: as attn_decode, with ATTN_ESCRATCH in place of ATTN_EWORKSPACE.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_noalloc(const void* q, const void* Kcache, const void* Vcache,
+                        const int32_t* lens, void* O,
+                        int B, int Nq, int Nkv, int Dh, int Tcap,
+                        float* LSE, int dtype, void* stream);
 
 /*
  * attn_decode_window -- attn_decode with a sliding window and an explicit

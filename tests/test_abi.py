@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_all_codes():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert tch.attn_strerror(code) and "unknown" not in tch.attn_strerror(code)
     assert "unknown" in tch.attn_strerror(-99)
 
@@ -433,3 +433,42 @@ def _decode_append(**kw):
 ])
 def test_decode_append_rejects(kw, code):
     assert _decode_append(**kw) == code
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, K=FAKE, V=FAKE, lens=FAKE, O=FAKE, B=2, Nq=8, Nkv=2, Dh=128, Tcap=64,
+             LSE=None, dtype=tch.ATTN_BF16, stream=None)
+    a.update(kw)
+    return tch.lib().attn_decode_noalloc(a["q"], a["K"], a["V"], a["lens"], a["O"], a["B"],
+                                         a["Nq"], a["Nkv"], a["Dh"], a["Tcap"], a["LSE"],
+                                         a["dtype"], a["stream"])
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), tch.ATTN_EINVAL),
+    (dict(lens=None), tch.ATTN_EINVAL),
+    (dict(O=None), tch.ATTN_EINVAL),
+    (dict(B=0), tch.ATTN_EINVAL),
+    (dict(Tcap=0), tch.ATTN_EINVAL),
+    (dict(Nq=8, Nkv=3), tch.ATTN_EGQA),
+    (dict(Dh=300), tch.ATTN_EUNSUPPORTED),
+    (dict(dtype=5), tch.ATTN_EUNSUPPORTED),
+    # twice the decode workload's batch needs 40 MB of partials: more than the fixed scratch
+    (dict(B=128, Nq=32, Nkv=8, Tcap=32768), tch.ATTN_ESCRATCH),
+    (dict(B=1, Nq=32, Nkv=8, Tcap=1 << 22), tch.ATTN_ESCRATCH),
+])
+def test_decode_noalloc_rejects(kw, code):
+    assert _decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_limit_covers_the_decode_workload():
+    # the 64-sequence, 32/8-head, 32768-slot decode at head size 128 fits the fixed
+    # scratch; twice its batch does not
+    need = tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_BF16)
+    assert 0 < need <= tch.ATTN_NOALLOC_SCRATCH_BYTES
+    assert tch.attn_decode_workspace_bytes(128, 32, 8, 128, 32768,
+                                           tch.ATTN_BF16) > tch.ATTN_NOALLOC_SCRATCH_BYTES
+    header = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in header
+    assert tch.ATTN_NOALLOC_SCRATCH_BYTES == 32 << 20

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=None)
     attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None,
                        window=0, scale=None, stream=None)
+    attn_decode_noalloc(q, Kcache, Vcache, lens, O, LSE=None, stream=None)
     attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype)
     attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, dtype)
     attn_kv_append(Knew, Vnew, Kcache, Vcache, pos, rolling=0, stream=None)
@@ -54,6 +55,8 @@ ATTN_EGQA = -2
 ATTN_EUNSUPPORTED = -3
 ATTN_EWORKSPACE = -4
 ATTN_EHIP = -5
+ATTN_ESCRATCH = -6
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 ATTN_BF16 = 0
 ATTN_F32 = 1
 
@@ -62,7 +65,7 @@ EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_win
            "attn_kv_append", "attn_decode_append", "attn_backward", "attn_backward_workspace_bytes",
            "attn_pack_key_mask", "attn_prefill_padded", "attn_prefill_cache_padded",
            "attn_decode_padded", "attn_rope_cos_sin", "attn_rope", "attn_kv_append_rope",
-           "attn_strerror")
+           "attn_decode_noalloc", "attn_strerror")
 ROPE_STYLES = {"pairs": 0, "half": 1}
 
 _lib = None
@@ -94,6 +97,9 @@ def lib():
         L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp,
                                   ctypes.c_size_t, i32, vp]
         L.attn_decode.restype = i32
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32,
+                                          vp]
+        L.attn_decode_noalloc.restype = i32
         L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, f32, i32, vp]
         L.attn_prefill_cache.restype = i32
@@ -246,6 +252,16 @@ def attn_decode(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, stream=Non
                            _dtype_code(q), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+
+
+def attn_decode_noalloc(q, Kcache, Vcache, lens, O, LSE=None, stream=None):
+    """attn_decode without a workspace: the library's fixed device scratch holds the
+    partials (at most ATTN_NOALLOC_SCRATCH_BYTES; calls on one device must not overlap)."""
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
+    st = lib().attn_decode_noalloc(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(O), B,
+                                   Nq, Nkv, Dh, Tcap, _ptr(LSE), _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_noalloc")
 
 
 def attn_decode_window(q, Kcache, Vcache, lens, O, LSE=None, workspace=None, window=0,

@@ -150,6 +150,21 @@ int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int
                      workspace, workspace_bytes, dtype, stream);
 }
 
+int attn_decode_noalloc(const void* q, const void* Kcache, const void* Vcache,
+                        const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                        float* LSE, int dtype, void* stream) {
+  const float scale = Dh > 0 ? 1.0f / sqrtf((float)Dh) : 1.0f;
+  int st = decode_check(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_decode_workspace_bytes(B, Nq, Nkv, Dh, Tcap, dtype);
+  static_assert(attn::kDecodeScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "header and library");
+  if (need > attn::kDecodeScratchBytes) return ATTN_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && attn::decode_scratch(&ws) != hipSuccess) return ATTN_EHIP;
+  return decode_impl(q, Kcache, Vcache, lens, nullptr, O, B, Nq, Nkv, Dh, Tcap, 0, scale, LSE, ws,
+                     need > 0 ? attn::kDecodeScratchBytes : 0, dtype, stream);
+}
+
 int attn_decode_window(const void* q, const void* Kcache, const void* Vcache,
                        const int32_t* lens, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
                        int window, float scale, float* LSE, void* workspace,
@@ -295,6 +310,8 @@ const char* attn_strerror(int status) {
       return "unsupported element type or head size, or a head too long for the MFMA kernels";
     case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_EHIP: return "HIP runtime error at launch";
+    case ATTN_ESCRATCH:
+      return "the call needs more scratch than the allocation-free entry point's fixed buffer";
     default: return "unknown status";
   }
 }

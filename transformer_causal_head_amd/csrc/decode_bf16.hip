@@ -42,6 +42,7 @@
 //     to the last valid row and those keys get probability 0.
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -725,6 +726,35 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
     case 256: return two ? launch_decode<256, 2>(p, stream) : launch_decode<256, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Scratch of the allocation-free decode (attn_decode_noalloc): the split-K
+// partials live in this fixed array instead of a caller's workspace.  Each
+// device that loads the library holds its own copy until the process ends.
+// In host code `scratch` only names the symbol; its device address is looked
+// up once per device (with that device current) and kept in scratch_ptr.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

@@ -47,6 +47,11 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
                               hipStream_t stream, const void* knew = nullptr,
                               const void* vnew = nullptr, const int32_t* slot = nullptr);
 
+// The allocation-free decode's fixed device scratch: its size, and its address
+// on the current device (looked up on the first call per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Copy Snew new K and V rows per (sequence, K/V head) into the caches at
 // positions pos[b] .. pos[b] + Snew - 1, or at those positions modulo Tcap
 // (rolling buffer).  elem_bytes: 2 (bf16) or 4 (fp32).
