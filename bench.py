@@ -87,15 +87,76 @@ def _cpu_baseline(q, k, v, cfg, budget_s=12.0):
 
 
 PROBE_LIB = os.path.join(ROOT, "_build", "libhbm_probe.so")
+ISSUE_LIB = os.path.join(ROOT, "_build", "libissue_probe.so")
 
 
 def _build_probe():
-    """Compile hbm_probe.hip (benchmark tooling, not the library) into _build/."""
+    """Compile the probes beside this file (benchmark tooling, not the library) into _build/."""
     from transformer_causal_head_amd import build as lib_build
     os.makedirs(os.path.dirname(PROBE_LIB), exist_ok=True)
-    obj = lib_build._compile("hbm_probe.hip", ROOT, os.path.dirname(PROBE_LIB))
-    lib_build._link([obj], PROBE_LIB)
-    print("built", PROBE_LIB)
+    for src, lib in (("hbm_probe.hip", PROBE_LIB), ("issue_probe.hip", ISSUE_LIB)):
+        obj = lib_build._compile(src, ROOT, os.path.dirname(lib))
+        lib_build._link([obj], lib)
+        print("built", lib)
+
+
+def _issue_probe(torch, dev, iters=4000):
+    """Matrix-core / VALU / LDS issue probe (issue_probe.hip): one line per mix.
+
+    ns_per_mfma: elapsed time per MFMA slot of one SIMD's MFMA waves, i.e.
+    elapsed / (iters * 32 * MFMA waves per SIMD); a 32x32x16 bf16 MFMA is 32
+    cycles of the matrix core, so 32 / ns_per_mfma is the clock in GHz when the
+    matrix core is never idle.  ns_per_slot: elapsed / (iters * 32)."""
+    import ctypes
+    if not os.path.exists(ISSUE_LIB):
+        raise RuntimeError(f"{ISSUE_LIB} is missing: run `python bench.py --build-probe` first")
+    L = ctypes.CDLL(ISSUE_LIB)
+    L.issue_probe.restype = ctypes.c_int
+    L.issue_probe.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(n_cu * 2 * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    # (kind, waves, lds, reuse, exp, nv): kind 0 MFMA, 1 VALU, 2 both in one wave, 3 split
+    mixes = [(0, 4, 0, 1, 0, 0), (0, 8, 0, 1, 0, 0), (0, 4, 1, 1, 0, 0), (0, 8, 1, 1, 0, 0),
+             (0, 4, 1, 2, 0, 0), (0, 8, 1, 2, 0, 0),
+             (1, 4, 0, 1, 1, 2), (1, 4, 0, 1, 1, 4), (1, 4, 0, 1, 1, 8), (1, 4, 0, 1, 0, 4),
+             (1, 4, 0, 1, 0, 8),
+             (2, 4, 0, 1, 1, 2), (2, 4, 0, 1, 1, 4), (2, 4, 0, 1, 1, 8), (2, 4, 0, 1, 0, 4),
+             (2, 4, 0, 1, 0, 8), (2, 8, 0, 1, 1, 4), (2, 8, 0, 1, 0, 4),
+             (2, 4, 1, 1, 1, 4), (2, 4, 1, 1, 0, 4), (2, 8, 1, 1, 1, 4), (2, 8, 1, 1, 0, 4),
+             (3, 8, 0, 1, 1, 4), (3, 8, 0, 1, 1, 8), (3, 8, 0, 1, 0, 4), (3, 8, 0, 1, 0, 8),
+             (3, 8, 1, 1, 1, 4)]
+    for kind, waves, lds, reuse, exp, nv in mixes:
+        def launch():
+            rc = L.issue_probe(kind, waves, n_cu, iters, lds, reuse, exp, nv, out.data_ptr(),
+                               ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"issue_probe returned {rc}")
+        ms = _time(torch, launch, 5, 2)
+        mfma_waves = 0 if kind == 1 else (waves // 4 if kind != 3 else waves // 8)
+        row = {"kind": ["mfma", "valu", "mixed", "split"][kind], "waves_per_cu": waves,
+               "lds_operand": bool(lds), "reuse": reuse, "valu_per_slot": nv, "exp": bool(exp),
+               "us": round(ms * 1e3, 1), "ns_per_slot": round(ms * 1e6 / (iters * 32), 2)}
+        if mfma_waves:
+            row["ns_per_mfma"] = round(ms * 1e6 / (iters * 32 * mfma_waves), 2)
+        print(json.dumps(row), flush=True)
+    # LDS read bandwidth per CU: 16-byte row reads, transposing 8-byte read pairs, and the
+    # pairs feeding one MFMA each (every kind moves 1 KB per wave per slot)
+    L.lds_probe.restype = ctypes.c_int
+    L.lds_probe.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    for kind, waves in ((4, 4), (4, 8), (5, 4), (5, 8), (6, 4), (6, 8)):
+        def launch():
+            rc = L.lds_probe(kind, waves, n_cu, iters, out.data_ptr(),
+                             ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"lds_probe returned {rc}")
+        ms = _time(torch, launch, 5, 2)
+        nbytes = n_cu * waves * iters * 32 * 1024
+        row = {"kind": {4: "lds_b128", 5: "lds_tr_b64_pairs", 6: "lds_tr_b64_pairs+mfma"}[kind],
+               "waves_per_cu": waves, "us": round(ms * 1e3, 1),
+               "lds_GBs_per_cu": round(nbytes / n_cu / (ms * 1e-3) / 1e9, 1),
+               "ns_per_slot_per_simd": round(ms * 1e6 / (iters * 32 * waves / 4), 2)}
+        print(json.dumps(row), flush=True)
 
 
 def _read_ceiling(torch, dev, gib=4.5, reps=5):
@@ -525,7 +586,9 @@ def main():
     ap.add_argument("--read-ceiling", action="store_true",
                     help="run only the streaming-read probe over 4.5 GB (HBM reference point)")
     ap.add_argument("--build-probe", action="store_true",
-                    help="compile the streaming-read probe (hbm_probe.hip) and exit")
+                    help="compile the probes (hbm_probe.hip, issue_probe.hip) and exit")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="run only the MFMA / VALU / LDS issue probe (issue_probe.hip)")
     ap.add_argument("--head-sizes", action="store_true",
                     help="time prefill and decode at head sizes 64 / 256 and decode with 32 "
                          "query heads per K/V head instead of the main step")
@@ -566,6 +629,9 @@ def main():
         return
     if args.read_ceiling:
         _read_ceiling(torch, dev)
+        return
+    if args.issue_probe:
+        _issue_probe(torch, dev)
         return
     if args.cache_paths:
         _cache_paths(torch, dev, tch, max(args.steps, 5), max(args.warmup, 1))

@@ -27,10 +27,14 @@
 //     reads and the transposing V reads free of bank conflicts.
 //   * V stays row-major in LDS; ds_read_b64_tr_b16 transposes it on the way
 //     into the V^T operand.
-//   * The next tile's QK^T is issued before this tile's softmax, and a wave
-//     raises its issue priority while it issues that MFMA block, so the two
-//     waves on a SIMD drift out of lock-step and one wave's MFMAs overlap the
-//     other's exponentials.
+//   * Software pipeline by one tile: the iteration for tile t computes S(t+1)
+//     = K(t+1) Q^T, the exponentials of S(t), O += V(t)^T P(t), and the mask
+//     and running maximum of S(t+1).  On interior tiles the two MFMA blocks
+//     each form one basic block with the VALU work that does not depend on
+//     them (the exponentials of t beside QK^T of t+1, the row maxima of t+1
+//     beside PV of t), interleaved by scheduling groups, so a wave's own VALU
+//     work issues between its MFMAs.  Boundary tiles keep the steps apart and
+//     raise the wave's issue priority while it issues its QK^T block.
 //   * Lazy rescale: the running maximum moves only when a new score exceeds it
 //     by more than TAU (log2 units).  Exponentials stay <= 2^TAU, and the
 //     accumulator is rescaled only on those rare moves.  The final O / l and
@@ -48,48 +52,16 @@
 #include "kernels.h"
 #include "tiles.h"
 
-// Variant knobs (compile-time): 32-query blocks per wave, waves per
-// workgroup, and whether the next tile's QK^T is issued before this tile's
-// softmax (needs a second score buffer).
-#ifndef PREFILL_SMALL_NW4
-#define PREFILL_SMALL_NW4 1
-#endif
-#ifndef PREFILL_QB
-#define PREFILL_QB 1
-#endif
-#ifndef PREFILL_NW
-#define PREFILL_NW 8
-#endif
-#ifndef PREFILL_PIPE
-#define PREFILL_PIPE 1
-#endif
-// Wave priority while a wave issues its MFMA blocks (bit 0: QK^T, bit 1: PV).
-// The wave that reaches the matrix core first finishes its block first and
-// moves on to the softmax VALU work while the other wave on the SIMD gets
-// the matrix core, so the two waves fall out of lock-step.
-#ifndef PREFILL_PRIO
-#define PREFILL_PRIO 1
-#endif
-// LDS read-ahead inside the MFMA blocks: with it, the K fragments of QK^T
-// run six reads ahead of their MFMAs and the V^T fragments of PV four
-// MFMAs ahead, instead of the compiler's one or two, so the LDS latency is
-// hidden behind the matrix core.
-#ifndef PREFILL_RA
-#define PREFILL_RA 1
-#endif
-
-
 namespace attn {
 
 namespace {
 
-constexpr int QB = PREFILL_QB; // 32-query blocks per wave
-constexpr bool PIPE = PREFILL_PIPE != 0;
+constexpr int QB = 1;  // 32-query blocks per wave
 constexpr float TAU = 8.f;
 
 // waves per workgroup: two per SIMD while the registers allow it
 template <int D>
-constexpr int waves_for() { return D == 128 ? PREFILL_NW : 4; }
+constexpr int waves_for() { return D == 128 ? 8 : 4; }
 
 struct Params {
   const __bf16* Q;
@@ -121,7 +93,10 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>
                                         const bf16x8 (&qf)[QB_][Geo<D>::KS],
                                         f32x16 (&s)[QB_][2]) {
   constexpr int KS = Geo<D>::KS;
-  if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(1);
+  // raised issue priority while this wave issues its QK^T block: the wave
+  // that reaches the matrix core first finishes its block first and moves on
+  // to softmax VALU work while the other wave on the SIMD takes the matrix core
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int qb = 0; qb < QB_; ++qb)
 #pragma unroll
@@ -135,7 +110,9 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>
       for (int qb = 0; qb < QB_; ++qb)
         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
     }
-  if (PREFILL_RA && QB_ == 1) {
+  // LDS read-ahead: the K fragments run six reads ahead of their MFMAs (the
+  // compiler's own schedule keeps one or two)
+  if (QB_ == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
 #pragma unroll
     for (int k = 0; k < 2 * KS - 6; ++k) {
@@ -144,7 +121,7 @@ __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   }
-  if (PREFILL_PRIO & 1) __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int QB_>
@@ -152,7 +129,6 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
                                         const bf16x8 (&pf)[QB_][4],
                                         f32x16 (&o)[QB_][Geo<D>::DB]) {
   constexpr int DB = Geo<D>::DB;
-  if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -166,7 +142,8 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
       for (int qb = 0; qb < QB_; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][db], 0, 0, 0);
     }
-  if (PREFILL_RA && QB_ == 1) {
+  // the V^T fragments run four MFMAs ahead of their products
+  if (QB_ == 1) {
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 transposing reads
 #pragma unroll
     for (int k = 0; k < 4 * DB - 4; ++k) {
@@ -175,7 +152,44 @@ __device__ __forceinline__ void pv_tile(const char* Vt, const int (&voff)[2][Geo
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
-  if (PREFILL_PRIO & 2) __builtin_amdgcn_s_setprio(0);
+}
+
+// The two products without scheduling constraints of their own: the fused
+// interior step interleaves them with softmax VALU work.
+template <int D, int QB_>
+__device__ __forceinline__ void qk_body(const char* Kt, const int (&koff)[Geo<D>::KS],
+                                        const bf16x8 (&qf)[QB_][Geo<D>::KS],
+                                        f32x16 (&s)[QB_][2]) {
+  constexpr int KS = Geo<D>::KS;
+#pragma unroll
+  for (int qb = 0; qb < QB_; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * Geo<D>::RB + koff[ks]);
+#pragma unroll
+      for (int qb = 0; qb < QB_; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
+    }
+}
+
+template <int D, int QB_>
+__device__ __forceinline__ void pv_body(const char* Vt, const int (&voff)[2][Geo<D>::DB],
+                                        const bf16x8 (&pf)[QB_][4],
+                                        f32x16 (&o)[QB_][Geo<D>::DB]) {
+  constexpr int DB = Geo<D>::DB;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 a = read_tr_operand<D>(Vt, kk, voff, db);
+#pragma unroll
+      for (int qb = 0; qb < QB_; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kk], o[qb][db], 0, 0, 0);
+    }
 }
 
 // KM: a key-padding mask is given (p.kbits); without it the kernel is
@@ -192,6 +206,9 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   constexpr int KS = geo::KS;
   constexpr int DB = geo::DB;
   constexpr int QW = 32 * QB;  // queries per wave
+  // interior tiles take the fused step (see fused_step) in the 8-wave head-
+  // size-128 kernel without a key mask; the other forms keep every step apart
+  constexpr bool FUSED = QB == 1 && D == 128 && NW == 8 && !KM;
   // four separate LDS objects, so the compiler can tell that the DMA copies
   // into one stage never alias reads of another
   __shared__ __attribute__((aligned(1024))) char k0s[TILE];
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   // start the copies first, they overlap the set-up below
   load_tile<D, NW>(Kh, t_lo * BN, K0, w, lane);
   load_tile<D, NW>(Vh, t_lo * BN, V0, w, lane);
-  if (PIPE && nt > 1) load_tile<D, NW>(Kh, (t_lo + 1) * BN, K1, w, lane);
+  if (nt > 1) load_tile<D, NW>(Kh, (t_lo + 1) * BN, K1, w, lane);
 
   // Q^T operand fragments: query column ln of block qb, d = 16*ks + 8*hl + i
   bf16x8 qf[QB][KS];
@@ -421,9 +438,8 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
       }
     }
   };
-  // P = exp2(S*c - m) rounded to bf16, l += row sum, O^T += V^T P^T
-  auto exp_pv = [&](f32x16 (&s)[QB][2], const char* Vt) {
-    bf16x8 pf[QB][4];
+  // P = exp2(S*c - m) rounded to bf16, l += row sum
+  auto exp_part = [&](f32x16 (&s)[QB][2], bf16x8 (&pf)[QB][4]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
@@ -445,74 +461,150 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
         }
       l_run[qb] += rs;
     }
+  };
+  // O^T += V^T P^T
+  auto exp_pv = [&](f32x16 (&s)[QB][2], const char* Vt) {
+    bf16x8 pf[QB][4];
+    exp_part(s, pf);
     pv_tile<D, QB>(Vt, voff, pf, oacc);
   };
-
-  // mask (boundary tiles only), running max / rescale, then P and PV
-  auto softmax_pv = [&](int t, f32x16 (&s)[QB][2], const char* Vt) {
-    if (masked(t)) mask_tile(t, s);
-    max_rescale(s);
-    exp_pv(s, Vt);
+  // the row maxima of a tile (log2 units), and whether any exceeds the
+  // running maximum by more than TAU; apply_max then moves the maximum and
+  // rescales (the same arithmetic as max_rescale, split in two)
+  auto find_max = [&](f32x16 (&s)[QB][2], float (&m_cand)[QB]) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      m_cand[qb] = xhalf_max(mx) * p.c;
+      any = any || __builtin_amdgcn_ballot_w64(m_cand[qb] > m_run[qb] + TAU) != 0;
+    }
+    return any;
+  };
+  auto apply_max = [&](const float (&m_cand)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = fmaxf(m_run[qb], m_cand[qb]);
+      const float alpha = exp2_fast(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
+      m_run[qb] = m_new;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+    }
+  };
+  // One interior step in two phases, each a single basic block: the QK^T
+  // block of tile t+1 on the matrix cores while the VALU forms P(t) (four
+  // VALU instructions per MFMA, the K fragments six reads ahead); then the PV
+  // block of tile t while the VALU finds the row maxima of tile t+1 (two per
+  // MFMA, the V^T fragments four MFMAs ahead).  The rare rescale comes last.
+  // The same operations in the same order as the separate steps, so the
+  // results are bit-identical.
+  auto fused_step = [&](const char* Kt, const char* Vt, f32x16 (&sc)[QB][2], f32x16 (&sn)[QB][2]) {
+    bf16x8 pf[QB][4];
+    qk_body<D, QB>(Kt, koff, qf, sn);
+    exp_part(sc, pf);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // 4 VALU
+      if (k < 10) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv_body<D, QB>(Vt, voff, pf, oacc);
+    float m_cand[QB];
+    const bool need = find_max(sn, m_cand);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 transposing reads
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
+      if (k < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (need) apply_max(m_cand);
   };
 
-  if constexpr (PIPE) {
-    f32x16 sa[QB][2], sb[QB][2];
+
+
+
+  // The pipelined loop: iteration i (tile t = t_lo + i) holds S(t) in
+  // registers, masked and with its running maximum applied; K(t+1) and V(t)
+  // are in LDS, and the copies of K(t+2) and V(t+1) are issued at its top.
+  // The iteration computes S(t+1) (QK^T), P(t) (exponentials, row sums),
+  // O += V(t)^T P(t), and the mask and running maximum of tile t+1.
+  f32x16 sa[QB][2], sb[QB][2];
+  wait_dma();
+  __syncthreads();
+  if (live(t_lo)) {
+    qk_tile<D, QB>(K0, koff, qf, sa);
+    if (masked(t_lo)) mask_tile(t_lo, sa);
+    max_rescale(sa);
+  }
+  auto iteration = [&](int i, f32x16 (&s_cur)[QB][2], f32x16 (&s_next)[QB][2], bool fused) {
+    const int t = t_lo + i;
+    char* const Kcur = (i & 1) ? K1 : K0;   // holds K(t), free after the barrier
+    char* const Knext = (i & 1) ? K0 : K1;  // holds K(t+1)
+    char* const Vcur = (i & 1) ? V1 : V0;   // holds V(t)
+    char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
     wait_dma();
     __syncthreads();
-    if (live(t_lo)) qk_tile<D, QB>(K0, koff, qf, sa);
-
-    // iteration i (tile t = t_lo + i): S(t) is in registers, K(t+1) and V(t)
-    // are in LDS; the copies of K(t+2) and V(t+1) are issued at the top.
-    auto iteration = [&](int i, f32x16 (&s_cur)[QB][2], f32x16 (&s_next)[QB][2]) {
-      const int t = t_lo + i;
-      char* const Kcur = (i & 1) ? K1 : K0;   // holds K(t), free after the barrier
-      char* const Knext = (i & 1) ? K0 : K1;  // holds K(t+1)
-      char* const Vcur = (i & 1) ? V1 : V0;   // holds V(t)
-      char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
-      wait_dma();
-      __syncthreads();
-      if (i + 2 < nt) load_tile<D, NW>(Kh, (t + 2) * BN, Kcur, w, lane);
-      if (i + 1 < nt) load_tile<D, NW>(Vh, (t + 1) * BN, Vnext, w, lane);
-      if (i + 1 < nt && live(t + 1)) qk_tile<D, QB>(Knext, koff, qf, s_next);
-      if (live(t)) softmax_pv(t, s_cur, Vcur);
-    };
-
-    int i = 0;
-    if constexpr (KM) {
-      for (int c = 0; c < nt; c += KW_RUN) {
-        if (c > 0) refill(t_lo + c);
-        const int c_end = min(nt, c + KW_RUN);
-        for (; i + 1 < c_end; i += 2) {
-          iteration(i, sa, sb);
-          iteration(i + 1, sb, sa);
-        }
-      }
+    if (i + 2 < nt) load_tile<D, NW>(Kh, (t + 2) * BN, Kcur, w, lane);
+    if (i + 1 < nt) load_tile<D, NW>(Vh, (t + 1) * BN, Vnext, w, lane);
+    if (fused) {
+      fused_step(Knext, Vcur, s_cur, s_next);
     } else {
-      for (; i + 1 < nt; i += 2) {
-        iteration(i, sa, sb);
-        iteration(i + 1, sb, sa);
+      const bool nx = i + 1 < nt && live(t + 1);
+      if (nx) qk_tile<D, QB>(Knext, koff, qf, s_next);
+      if (live(t)) exp_pv(s_cur, Vcur);
+      if (nx) {
+        if (masked(t + 1)) mask_tile(t + 1, s_next);
+        max_rescale(s_next);
       }
     }
-    if (i < nt) iteration(i, sa, sb);
+  };
+
+  // The loop runs in pairs of iterations, so that stages and score buffers
+  // alternate with a static pattern.
+  int i = 0;
+  if constexpr (KM) {
+    for (int c = 0; c < nt; c += KW_RUN) {
+      if (c > 0) refill(t_lo + c);
+      const int c_end = min(nt, c + KW_RUN);
+      for (; i + 1 < c_end; i += 2) {
+        iteration(i, sa, sb, false);
+        iteration(i + 1, sb, sa, false);
+      }
+    }
   } else {
-    // iteration i (tile t): K(t), V(t) are in LDS; K(t+1), V(t+1) are copied
-    // into the other stage while tile t is computed.
-    f32x16 s[QB][2];
-    for (int i = 0; i < nt; ++i) {
-      const int t = t_lo + i;
-      if (KM && i > 0 && i % KW_RUN == 0) refill(t);
-      wait_dma();
-      __syncthreads();
-      if (i + 1 < nt) {
-        load_tile<D, NW>(Kh, (t + 1) * BN, (i & 1) ? K0 : K1, w, lane);
-        load_tile<D, NW>(Vh, (t + 1) * BN, (i & 1) ? V0 : V1, w, lane);
-      }
-      if (live(t)) {
-        qk_tile<D, QB>((i & 1) ? K1 : K0, koff, qf, s);
-        softmax_pv(t, s, (i & 1) ? V1 : V0);
-      }
+    // This wave's fused iterations: tile t live, tile t+1 live and unmasked,
+    // i.e. t in [max(tl_lo, tf_lo - 1), min(tl_hi, tf_hi - 1)].  They run in a
+    // loop of their own (one loop body holding both step forms would not fit
+    // the registers), from the first even iteration of the range; every loop
+    // runs one barrier per iteration, so the waves stay in step.
+    const int f_lo = max(tl_lo, tf_lo - 1) - t_lo;
+    const int f_hi = min(min(tl_hi, tf_hi - 1) - t_lo, nt - 2);
+    const int fa = (max(f_lo, 0) + 1) & ~1;
+    const int npairs = (FUSED && f_hi >= fa) ? (f_hi - fa + 1) / 2 : 0;
+    const int a_end = npairs > 0 ? fa : 0;
+    for (; i < a_end; i += 2) {
+      iteration(i, sa, sb, false);
+      iteration(i + 1, sb, sa, false);
+    }
+    for (int q = 0; q < npairs; ++q, i += 2) {
+      iteration(i, sa, sb, true);
+      iteration(i + 1, sb, sa, true);
+    }
+    for (; i + 1 < nt; i += 2) {
+      iteration(i, sa, sb, false);
+      iteration(i + 1, sb, sa, false);
     }
   }
+  if (i < nt) iteration(i, sa, sb, false);
 
   if (!wave_live) return;
   // epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
@@ -585,7 +677,7 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   // overlaps the other's matrix work.  Each wave computes the same rows
   // either way.  (A chunk against a long cache stays on 8 waves: there the
   // second copy of every K/V tile per CU costs more than the overlap gains.)
-  const bool small = D == 128 && NW == 8 && PREFILL_SMALL_NW4 && lens == nullptr && n_cu > 0 &&
+  const bool small = D == 128 && NW == 8 && lens == nullptr && n_cu > 0 &&
                      nblocks <= n_cu;
   if (small) nblocks = geometry(4);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
