@@ -86,6 +86,11 @@ struct Params {
   // NW / hp - 1, so that every workgroup of a causal prefill holds early and
   // late queries alike (used when the whole grid runs in one round).
   int strided;
+  // causal one-round grids of 4-wave workgroups (two per CU): the first half
+  // of the grid takes the query tiles heaviest first, the second half
+  // lightest first, so that the two workgroups a CU receives together stream
+  // about the same number of key tiles in total
+  int zigzag;
 };
 
 template <int D, int QB_>
@@ -194,30 +199,44 @@ __device__ __forceinline__ void pv_body(const char* Vt, const int (&voff)[2][Geo
 
 // KM: a key-padding mask is given (p.kbits); without it the kernel is
 // compiled exactly as if the mask did not exist.
-template <int D, int NW, bool KM>
+// SK (head size 128, 8 waves, no key mask): the workgroup's key range is split
+// in two.  Waves 0-3 take the first half of its key tiles and waves 4-7 the
+// second, each with its own LDS stages, for the same 128 query rows (wave w
+// and w + 4 share theirs); at the end waves 4-7 hand their running maximum,
+// sum and unnormalised output to waves 0-3 through LDS, which merge them by
+// the same rescaling identity the online softmax uses.  Used when the grid
+// runs in one round: a causal prefill is as long as its heaviest workgroup,
+// and the split halves the serial key walk of the heavy query tiles.
+template <int D, int NW, bool KM, bool SK = false>
 // Head size 128 also runs as 4 waves (one per SIMD) with two workgroups per CU
 // (at most 256 registers per lane), for grids that would fill the chip only
 // once with 8-wave workgroups.  Head size 64 always runs as 4 waves with three
 // workgroups per CU (at most 168 registers; two with a key-padding mask, whose
 // extra registers would spill at that bound).
 __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && NW == 4) ? (KM ? 2 : 3) : 1)) void prefill_kernel(Params p) {
+  static_assert(!SK || (D == 128 && NW == 8 && !KM), "key split: head size 128, 8 waves, no mask");
   using geo = Geo<D>;
   constexpr int TILE = geo::TILE;
   constexpr int KS = geo::KS;
   constexpr int DB = geo::DB;
   constexpr int QW = 32 * QB;  // queries per wave
-  // interior tiles take the fused step (see fused_step) in the 8-wave head-
-  // size-128 kernel without a key mask; the other forms keep every step apart
-  constexpr bool FUSED = QB == 1 && D == 128 && NW == 8 && !KM;
+  // interior tiles take the fused step (see fused_step) at head size 128
+  // without a key mask; the other forms keep every step apart
+  constexpr bool FUSED = QB == 1 && D == 128 && !KM;
   // four separate LDS objects, so the compiler can tell that the DMA copies
-  // into one stage never alias reads of another
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+  // into one stage never alias reads of another (with a key split, each holds
+  // one stage per half)
+  constexpr int NH = SK ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char k0s[NH * TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[NH * TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[NH * TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[NH * TILE];
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int w_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int half = SK ? (w_all >> 2) : 0;  // key half (SK)
+  const int w = SK ? (w_all & 3) : w_all;  // query wave; copying wave of its half
+  constexpr int NWQ = SK ? 4 : NW;         // query waves (and copying waves per stage)
   const int lane = tid & 63;
   const int ln = lane & 31;
   const int hl = lane >> 5;
@@ -225,7 +244,10 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   // workgroup -> (q tile, batch, K/V head, head subgroup); heavy tiles first
   const int inner = p.B * p.Nkv * p.n_hsub;
   const int bid = blockIdx.x;
-  const int qt = p.causal ? (p.n_qtiles - 1 - bid / inner) : (bid / inner);
+  const int qidx = bid / inner;
+  const int qt = !p.causal ? qidx
+                 : (p.zigzag && qidx >= p.n_qtiles / 2) ? qidx - p.n_qtiles / 2
+                                                        : p.n_qtiles - 1 - qidx;
   int rest = bid % inner;
   const int hsub = rest % p.n_hsub;
   rest /= p.n_hsub;
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   const int q_off = p.lens ? n_keys - p.S : 0;
 
   const int head = g * p.G + hsub * p.hp + (w % p.hp);
-  const int nblk = NW / p.hp;  // query blocks of QW rows per workgroup
+  const int nblk = NWQ / p.hp;  // query blocks of QW rows per workgroup
   // first query row of this wave (and its position); the workgroup's rows
   // span [q0, q1)
   const int qa_row = p.strided ? (qt + (w / p.hp) * p.n_qtiles) * QW
@@ -288,16 +310,24 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
     t_end = __builtin_amdgcn_readfirstlane(t_end);
   }
   const int nt = t_end - t_lo;
+  // Every wave runs n_it iterations (one barrier each).  Its half of the
+  // workgroup copies and computes the nt_h tiles from t_base: all nt tiles,
+  // or with a key split the first ceil(nt/2) (waves 0-3) or the rest (4-7).
+  const int n_it = SK ? (nt + 1) / 2 : nt;
+  const int t_base = t_lo + half * n_it;
+  const int nt_h = SK ? (half ? nt - n_it : n_it) : nt;
 
-  char* const K0 = k0s;
-  char* const K1 = k1s;
-  char* const V0 = v0s;
-  char* const V1 = v1s;
+  char* const K0 = k0s + half * TILE;
+  char* const K1 = k1s + half * TILE;
+  char* const V0 = v0s + half * TILE;
+  char* const V1 = v1s + half * TILE;
 
   // start the copies first, they overlap the set-up below
-  load_tile<D, NW>(Kh, t_lo * BN, K0, w, lane);
-  load_tile<D, NW>(Vh, t_lo * BN, V0, w, lane);
-  if (nt > 1) load_tile<D, NW>(Kh, (t_lo + 1) * BN, K1, w, lane);
+  if (nt_h > 0) {
+    load_tile<D, NWQ>(Kh, t_base * BN, K0, w, lane);
+    load_tile<D, NWQ>(Vh, t_base * BN, V0, w, lane);
+  }
+  if (nt_h > 1) load_tile<D, NWQ>(Kh, (t_base + 1) * BN, K1, w, lane);
 
   // Q^T operand fragments: query column ln of block qb, d = 16*ks + 8*hl + i
   bf16x8 qf[QB][KS];
@@ -540,27 +570,27 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   f32x16 sa[QB][2], sb[QB][2];
   wait_dma();
   __syncthreads();
-  if (live(t_lo)) {
+  if (nt_h > 0 && live(t_base)) {
     qk_tile<D, QB>(K0, koff, qf, sa);
-    if (masked(t_lo)) mask_tile(t_lo, sa);
+    if (masked(t_base)) mask_tile(t_base, sa);
     max_rescale(sa);
   }
   auto iteration = [&](int i, f32x16 (&s_cur)[QB][2], f32x16 (&s_next)[QB][2], bool fused) {
-    const int t = t_lo + i;
+    const int t = t_base + i;
     char* const Kcur = (i & 1) ? K1 : K0;   // holds K(t), free after the barrier
     char* const Knext = (i & 1) ? K0 : K1;  // holds K(t+1)
     char* const Vcur = (i & 1) ? V1 : V0;   // holds V(t)
     char* const Vnext = (i & 1) ? V0 : V1;  // gets V(t+1)
     wait_dma();
     __syncthreads();
-    if (i + 2 < nt) load_tile<D, NW>(Kh, (t + 2) * BN, Kcur, w, lane);
-    if (i + 1 < nt) load_tile<D, NW>(Vh, (t + 1) * BN, Vnext, w, lane);
+    if (i + 2 < nt_h) load_tile<D, NWQ>(Kh, (t + 2) * BN, Kcur, w, lane);
+    if (i + 1 < nt_h) load_tile<D, NWQ>(Vh, (t + 1) * BN, Vnext, w, lane);
     if (fused) {
       fused_step(Knext, Vcur, s_cur, s_next);
     } else {
-      const bool nx = i + 1 < nt && live(t + 1);
+      const bool nx = i + 1 < nt_h && live(t + 1);
       if (nx) qk_tile<D, QB>(Knext, koff, qf, s_next);
-      if (live(t)) exp_pv(s_cur, Vcur);
+      if (i < nt_h && live(t)) exp_pv(s_cur, Vcur);
       if (nx) {
         if (masked(t + 1)) mask_tile(t + 1, s_next);
         max_rescale(s_next);
@@ -586,8 +616,8 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
     // loop of their own (one loop body holding both step forms would not fit
     // the registers), from the first even iteration of the range; every loop
     // runs one barrier per iteration, so the waves stay in step.
-    const int f_lo = max(tl_lo, tf_lo - 1) - t_lo;
-    const int f_hi = min(min(tl_hi, tf_hi - 1) - t_lo, nt - 2);
+    const int f_lo = max(tl_lo, tf_lo - 1) - t_base;
+    const int f_hi = min(min(tl_hi, tf_hi - 1) - t_base, nt_h - 2);
     const int fa = (max(f_lo, 0) + 1) & ~1;
     const int npairs = (FUSED && f_hi >= fa) ? (f_hi - fa + 1) / 2 : 0;
     const int a_end = npairs > 0 ? fa : 0;
@@ -599,12 +629,43 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
       iteration(i, sa, sb, true);
       iteration(i + 1, sb, sa, true);
     }
-    for (; i + 1 < nt; i += 2) {
+    for (; i + 1 < n_it; i += 2) {
       iteration(i, sa, sb, false);
       iteration(i + 1, sb, sa, false);
     }
   }
-  if (i < nt) iteration(i, sa, sb, false);
+  if (i < n_it) iteration(i, sa, sb, false);
+
+  if constexpr (SK) {
+    // merge the two key halves: every copy has landed and every stage read
+    // once all waves pass this barrier (the last iteration issues none)
+    __syncthreads();
+    // wave w + 4's unnormalised output (64 values per lane) at value-major
+    // float offsets in k0s (query waves 0, 1) or k1s (2, 3); its (m, l) in v0s
+    float* xo = reinterpret_cast<float*>((w < 2 ? k0s : k1s) + (w & 1) * TILE);
+    float* xml = reinterpret_cast<float*>(v0s) + w * 128;
+    if (half) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = oacc[0][db][r];
+      xml[lane] = m_run[0];
+      xml[64 + lane] = l_run[0];
+    }
+    __syncthreads();
+    if (half) return;
+    const float mb = xml[lane], lb = xml[64 + lane];
+    const float M = fmaxf(m_run[0], mb);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float ra = exp2_fast(m_run[0] - Mu), rb = exp2_fast(mb - Mu);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[0][db][r] = __builtin_fmaf(rb, xo[(db * 16 + r) * 64 + lane], oacc[0][db][r] * ra);
+    l_run[0] = __builtin_fmaf(rb, lb, l_run[0] * ra);
+    m_run[0] = M;
+  }
 
   if (!wave_live) return;
   // epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
@@ -680,6 +741,13 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   const bool small = D == 128 && NW == 8 && lens == nullptr && n_cu > 0 &&
                      nblocks <= n_cu;
   if (small) nblocks = geometry(4);
+  // A causal one-round grid without a key mask whose heads hold at least 4096
+  // keys splits each workgroup's key range between two sets of four waves
+  // instead (SK form: the grid of the 4-wave form, 8 waves per workgroup, so
+  // it runs in two rounds).  The split halves the serial key walk of the
+  // heaviest workgroups; on shorter heads the second round's start-up costs
+  // more than that saves.
+  const bool split = small && causal && kbits == nullptr && S >= 4096;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // A causal prefill whose grid runs in one round lasts as long as its
   // heaviest workgroup: with consecutive query blocks the last tile of a head
@@ -689,7 +757,13 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   // form is faster with consecutive blocks.
   p.strided = !small && causal && window == 0 && lens == nullptr && p.n_qtiles > 1 &&
               nblocks <= n_cu;
+  p.zigzag = small && !split && causal && (p.n_qtiles % 2 == 0);
   if constexpr (D == 128 && NW == 8) {
+    if (split) {
+      hipLaunchKernelGGL((prefill_kernel<D, 8, false, true>), dim3((unsigned)nblocks), dim3(512), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
     if (small) {
       if (kbits)
         hipLaunchKernelGGL((prefill_kernel<D, 4, true>), dim3((unsigned)nblocks), dim3(256), 0,
