@@ -504,6 +504,59 @@ def _rope_padding(torch, dev, tch, steps, warmup):
                       "algorithmic_bytes": nbytes}), flush=True)
     del x, table
 
+    # RoPE fused into the attention call against the two passes it replaces, on the
+    # 32768-token prefill (keys already rotated) and on the decode workload
+    q, k, v = workloads.prefill_inputs(B, H, H, S, Dh, "bf16", seed=0)
+    tq, tk, tv = (workloads.to_torch(a, "bf16", dev) for a in (q, k, v))
+    del q, k, v
+    table = tch.rope_table(S, Dh, device=dev)
+    tch.attn_rope(tk, tk, table, style=1)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    qr = torch.empty_like(tq)
+    scale = 1.0 / math.sqrt(Dh)
+    ms_fused = _time(torch, lambda: tch.attn_prefill_rope(tq, tk, tv, O, L, table, style=1,
+                                                          scale=scale), steps, warmup)
+
+    def two_passes():
+        tch.attn_rope(tq, qr, table, style=1)
+        tch.attn_prefill(qr, tk, tv, O, L, scale=scale)
+    ms_two = _time(torch, two_passes, steps, warmup)
+    flop, _ = workloads.prefill_work(B, H, H, S, Dh, True, 0, 2)
+    print(json.dumps({"path": "attn_prefill_rope", "workload": f"B={B} H={H} S={S} Dh={Dh} bf16 "
+                      "causal, q rotated in the kernel (half layout)", "ms": round(ms_fused, 4),
+                      "TFLOP/s": round(flop / ms_fused / 1e9, 1),
+                      "two_passes_ms": round(ms_two, 4),
+                      "two_passes": "attn_rope on q, then attn_prefill"}), flush=True)
+    del tq, tk, tv, O, L, qr, table
+    dc = workloads.WORKLOADS[DECODE]
+    lens, q, kc, vc = workloads.decode_inputs(dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"], dc["Tcap"],
+                                              dc["len_lo"], dc["len_hi"])
+    tq, tkc, tvc = (workloads.to_torch(a, "bf16", dev) for a in (q, kc, vc))
+    del kc, vc
+    tl = torch.from_numpy(lens).to(dev)
+    table = tch.rope_table(dc["Tcap"], dc["Dh"], device=dev)
+    Od = torch.empty_like(tq)
+    Ld = torch.empty((dc["B"], dc["Nq"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(tch.attn_decode_workspace_bytes(dc["B"], dc["Nq"], dc["Nkv"], dc["Dh"],
+                                                     dc["Tcap"], tch.ATTN_BF16),
+                     dtype=torch.uint8, device=dev)
+    pos = (tl - 1).reshape(-1, 1).contiguous()
+    qr = torch.empty_like(tq)
+    ms_fused = _time(torch, lambda: tch.attn_decode_rope(tq, tkc, tvc, tl, Od, Ld, table,
+                                                         workspace=ws, style=1), steps, warmup)
+
+    def two_passes_d():
+        tch.attn_rope(tq[:, :, None], qr[:, :, None], table, positions=pos, style=1)
+        tch.attn_decode(qr, tkc, tvc, tl, Od, Ld, ws)
+    ms_two = _time(torch, two_passes_d, steps, warmup)
+    _, dbytes = workloads.decode_work(lens, dc["Nq"], dc["Nkv"], dc["Dh"], 2)
+    print(json.dumps({"path": "attn_decode_rope", "workload": f"{DECODE}, q rotated in the kernel",
+                      "ms": round(ms_fused, 4), "GB/s": round(dbytes / ms_fused / 1e6, 1),
+                      "two_passes_ms": round(ms_two, 4),
+                      "two_passes": "attn_rope on q, then attn_decode"}), flush=True)
+    del tq, tkc, tvc, Od, Ld, ws, qr, table
+
     # rotating append: a 2048-token chunk of 8 K/V heads into a 32768-row cache
     Nkv, T = 8, 32768
     table = tch.rope_table(T, Dh, device=dev)

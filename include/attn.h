@@ -375,6 +375,45 @@ int attn_kv_append_rope(const void* Knew, const void* Vnew, void* Kcache, void* 
                         int B, int Nkv, int Snew, int Dh, int Tcap, int rolling, int style,
                         int dtype, void* stream);
 
+/*
+ * Attention with the queries rotated as they are loaded (RoPE fused into the
+ * attention step: the textbook's "Как в attention попадает позиция" and
+ * step 4 of "Прямой проход по шагам" -- q and k are turned before their dot
+ * product).  The keys must already be rotated: by attn_kv_append_rope on
+ * their way into a cache, or by attn_rope for a plain prefill.  Each entry
+ * point takes the arguments of its unrotated form (with a key-padding mask,
+ * NULL for none), plus
+ *   table, P   the angle table from attn_rope_cos_sin ([P, Dh] fp32, DEVICE)
+ *   positions  DEVICE int32, or NULL: the rotation position of each query
+ *              row -- [B, S] (prefill), [B, Sq] (chunked prefill), [B] (decode)
+ *   start      DEVICE int32 [B], or NULL (prefill forms only): with positions
+ *              NULL, query row i of sequence b is at start[b] + i
+ *   style      0: pairs (x[2m], x[2m+1]); 1: halves (x[m], x[m + Dh/2])
+ * Without positions and start a query row is turned at its own position:
+ * row i of a prefill at i, row i of a chunk at lens[b] - Sq + i, a decode
+ * step's query at lens[b] - 1 (a rolling-buffer cache passes its positions).
+ * Positions are clamped to [0, P - 1].  The rotation is the one attn_rope
+ * computes (fp32, rounded once to the input type), so the result is that of
+ * attn_rope on q followed by the unrotated call, without the extra pass over
+ * q.  Errors: those of the unrotated form, and ATTN_EINVAL for a NULL table,
+ * P < 1, an odd Dh or a bad style.
+ */
+int attn_prefill_rope(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                      void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh, int causal,
+                      int window, float scale, const float* table, int P,
+                      const int32_t* positions, const int32_t* start, int style, int dtype,
+                      void* stream);
+int attn_prefill_cache_rope(const void* Q, const void* Kcache, const void* Vcache,
+                            const int32_t* lens, const uint64_t* key_bits, void* O, float* LSE,
+                            int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
+                            float scale, const float* table, int P, const int32_t* positions,
+                            const int32_t* start, int style, int dtype, void* stream);
+int attn_decode_rope(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
+                     const uint64_t* key_bits, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                     int window, float scale, const float* table, int P,
+                     const int32_t* positions, int style, float* LSE, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream);
+
 /* attn_strerror -- static description of an attn_status value. */
 const char* attn_strerror(int status);
 

@@ -472,3 +472,32 @@ def test_decode_noalloc_limit_covers_the_decode_workload():
     header = open(HEADER).read()
     assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in header
     assert tch.ATTN_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+@no_gpu
+@pytest.mark.parametrize("entry", ["attn_prefill_rope", "attn_prefill_cache_rope", "attn_decode_rope"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), tch.ATTN_EINVAL),
+    (dict(P=0), tch.ATTN_EINVAL),
+    (dict(style=2), tch.ATTN_EINVAL),
+    (dict(Dh=65), tch.ATTN_EINVAL),      # rotation pairs need an even head size
+    (dict(Nq=6, Nkv=4), tch.ATTN_EGQA),  # then the checks of the unrotated form
+    (dict(Q=None), tch.ATTN_EINVAL),
+])
+def test_rope_entry_points_reject(entry, kw, code):
+    a = dict(Q=FAKE, table=FAKE, P=100, style=0, Dh=128, Nq=8, Nkv=2)
+    a.update(kw)
+    L = tch.lib()
+    if entry == "attn_prefill_rope":
+        st = L.attn_prefill_rope(a["Q"], FAKE, FAKE, None, FAKE, None, 1, a["Nq"], a["Nkv"], 16,
+                                 a["Dh"], 1, 0, 0.125, a["table"], a["P"], None, None, a["style"],
+                                 tch.ATTN_BF16, None)
+    elif entry == "attn_prefill_cache_rope":
+        st = L.attn_prefill_cache_rope(a["Q"], FAKE, FAKE, FAKE, None, FAKE, None, 2, a["Nq"],
+                                       a["Nkv"], 16, a["Dh"], 64, 0, 0.125, a["table"], a["P"],
+                                       None, None, a["style"], tch.ATTN_BF16, None)
+    else:
+        st = L.attn_decode_rope(a["Q"], FAKE, FAKE, FAKE, None, FAKE, 2, a["Nq"], a["Nkv"], a["Dh"],
+                                64, 0, 0.125, a["table"], a["P"], None, a["style"], None, FAKE,
+                                1 << 30, tch.ATTN_BF16, None)
+    assert st == code

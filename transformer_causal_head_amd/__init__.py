@@ -30,6 +30,12 @@ Entry points (same names as the C ABI):
     attn_rope(X, Y, table, positions=None, start=None, style=0, stream=None)
     attn_kv_append_rope(Knew, Vnew, Kcache, Vcache, pos, table, positions=None, rolling=0,
                         style=0, stream=None)
+    attn_prefill_rope(Q, K, V, O, LSE, table, key_bits=None, positions=None, start=None,
+                      style=0, causal=1, window=0, scale=None, stream=None)
+    attn_prefill_cache_rope(Q, Kcache, Vcache, lens, O, LSE, table, key_bits=None,
+                            positions=None, start=None, style=0, window=0, scale=None, stream=None)
+    attn_decode_rope(q, Kcache, Vcache, lens, O, LSE, table, workspace=None, key_bits=None,
+                     positions=None, style=0, window=0, scale=None, stream=None)
     attn_strerror(status)
 Key bits are held in int64 tensors [B, ceil(T / 64)] (the C ABI's uint64 words).
 Conveniences that allocate outputs with torch:
@@ -65,7 +71,8 @@ EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_win
            "attn_kv_append", "attn_decode_append", "attn_backward", "attn_backward_workspace_bytes",
            "attn_pack_key_mask", "attn_prefill_padded", "attn_prefill_cache_padded",
            "attn_decode_padded", "attn_rope_cos_sin", "attn_rope", "attn_kv_append_rope",
-           "attn_decode_noalloc", "attn_strerror")
+           "attn_decode_noalloc", "attn_prefill_rope", "attn_prefill_cache_rope",
+           "attn_decode_rope", "attn_strerror")
 ROPE_STYLES = {"pairs": 0, "half": 1}
 
 _lib = None
@@ -134,6 +141,15 @@ def lib():
         L.attn_kv_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           i32, i32, i32, vp]
         L.attn_kv_append_rope.restype = i32
+        L.attn_prefill_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        f32, vp, i32, vp, vp, i32, i32, vp]
+        L.attn_prefill_rope.restype = i32
+        L.attn_prefill_cache_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                              i32, i32, f32, vp, i32, vp, vp, i32, i32, vp]
+        L.attn_prefill_cache_rope.restype = i32
+        L.attn_decode_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                       vp, i32, vp, i32, vp, vp, ctypes.c_size_t, i32, vp]
+        L.attn_decode_rope.restype = i32
         L.attn_strerror.argtypes = [i32]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -355,6 +371,78 @@ def attn_decode_append(q, knew, vnew, Kcache, Vcache, lens, slot, O, LSE=None, w
                                   _dtype_code(q), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode_append")
+
+
+def _check_rope(table, Dh, positions, start, shape, style):
+    import torch
+    _check_table(table, Dh)
+    if positions is not None and (positions.dtype != torch.int32
+                                  or tuple(positions.shape) != tuple(shape)):
+        raise ValueError(f"positions must be int32 {list(shape)}")
+    if start is not None and (start.dtype != torch.int32 or tuple(start.shape) != (shape[0],)):
+        raise ValueError("start must be int32 [B]")
+    return _rope_style(style)
+
+
+def attn_prefill_rope(Q, K, V, O, LSE, table, key_bits=None, positions=None, start=None, style=0,
+                      causal=1, window=0, scale=None, stream=None):
+    """attn_prefill with Q rotated at load (K already rotated): table [P, Dh] fp32,
+    positions int32 [B, S] or start int32 [B] or neither (row i at position i)."""
+    B, Nq, Nkv, S, Dh = _check_prefill(Q, K, V, O, LSE)
+    _check_bits(key_bits, B, S)
+    st_code = _check_rope(table, Dh, positions, start, (B, S), style)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    st = lib().attn_prefill_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(key_bits), _ptr(O), _ptr(LSE), B,
+                                 Nq, Nkv, S, Dh, int(causal), int(window), float(scale),
+                                 _ptr(table), table.shape[0], _ptr(positions), _ptr(start), st_code,
+                                 _dtype_code(Q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill_rope")
+
+
+def attn_prefill_cache_rope(Q, Kcache, Vcache, lens, O, LSE, table, key_bits=None, positions=None,
+                            start=None, style=0, window=0, scale=None, stream=None):
+    """attn_prefill_cache with the chunk's queries rotated at load (row i of sequence b
+    at positions[b, i], start[b] + i, or lens[b] - Sq + i)."""
+    import torch
+    B, Nq, Sq, Dh = Q.shape
+    Nkv, Tcap = Kcache.shape[1], Kcache.shape[2]
+    if tuple(Kcache.shape) != (B, Nkv, Tcap, Dh) or Kcache.shape != Vcache.shape:
+        raise ValueError("cache shapes must be [B, Nkv, Tcap, Dh]")
+    if O.shape != Q.shape or lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+        raise ValueError("O must match Q; lens must be int32 [B]")
+    if not (Q.dtype == Kcache.dtype == Vcache.dtype == O.dtype):
+        raise ValueError("Q, caches and O must share one dtype")
+    _check_lse(LSE, (B, Nq, Sq))
+    _check_bits(key_bits, B, Tcap)
+    st_code = _check_rope(table, Dh, positions, start, (B, Sq), style)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    st = lib().attn_prefill_cache_rope(_ptr(Q), _ptr(Kcache), _ptr(Vcache), _ptr(lens),
+                                       _ptr(key_bits), _ptr(O), _ptr(LSE), B, Nq, Nkv, Sq, Dh, Tcap,
+                                       int(window), float(scale), _ptr(table), table.shape[0],
+                                       _ptr(positions), _ptr(start), st_code, _dtype_code(Q),
+                                       _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_prefill_cache_rope")
+
+
+def attn_decode_rope(q, Kcache, Vcache, lens, O, LSE, table, workspace=None, key_bits=None,
+                     positions=None, style=0, window=0, scale=None, stream=None):
+    """attn_decode_window with q rotated at load (at positions[b], or lens[b] - 1)."""
+    B, Nq, Nkv, Dh, Tcap = _check_decode(q, Kcache, Vcache, lens, O, LSE)
+    _check_bits(key_bits, B, Tcap)
+    st_code = _check_rope(table, Dh, positions, None, (B,), style)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_rope(_ptr(q), _ptr(Kcache), _ptr(Vcache), _ptr(lens), _ptr(key_bits),
+                                _ptr(O), B, Nq, Nkv, Dh, Tcap, int(window), float(scale),
+                                _ptr(table), table.shape[0], _ptr(positions), st_code, _ptr(LSE),
+                                _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_rope")
 
 
 def attn_pack_key_mask(mask, key_bits, stream=None):

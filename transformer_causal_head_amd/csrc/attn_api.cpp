@@ -27,9 +27,16 @@ bool mfma_head_fits(long long rows, int Dh) { return rows * Dh * 2 <= 0x7fffffff
 
 }  // namespace
 
+// rotation arguments of the _rope entry points: a table, its rows, a style
+static int validate_rope(const float* table, int P, int Dh, int style) {
+  if (!table || !positive(P) || Dh % 2 != 0 || (style != 0 && style != 1)) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
 static int prefill_impl(const void* Q, const void* K, const void* V, const uint64_t* kbits,
                         void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh, int causal,
-                        int window, float scale, int dtype, void* stream) {
+                        int window, float scale, int dtype, void* stream,
+                        const attn::RopeQ* rope = nullptr) {
   if (!Q || !K || !V || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
@@ -43,15 +50,17 @@ static int prefill_impl(const void* Q, const void* K, const void* V, const uint6
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
-                                              kbits, causal, window, scale, s));
+                                              kbits, causal, window, scale, s, rope));
   return from_hip(attn::launch_rows_general(Q, K, V, O, LSE, B, Nq, Nkv, S, Dh, S, nullptr,
-                                            kbits, causal, window, scale, dtype == ATTN_BF16, s));
+                                            kbits, causal, window, scale, dtype == ATTN_BF16, s,
+                                            rope));
 }
 
 static int prefill_cache_impl(const void* Q, const void* Kcache, const void* Vcache,
                               const int32_t* lens, const uint64_t* kbits, void* O, float* LSE,
                               int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
-                              float scale, int dtype, void* stream) {
+                              float scale, int dtype, void* stream,
+                              const attn::RopeQ* rope = nullptr) {
   if (!Q || !Kcache || !Vcache || !lens || !O) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
@@ -63,9 +72,10 @@ static int prefill_cache_impl(const void* Q, const void* Kcache, const void* Vca
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::prefill_bf16_supported(Dh))
     return from_hip(attn::launch_prefill_bf16(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh,
-                                              Tcap, lens, kbits, 1, window, scale, s));
+                                              Tcap, lens, kbits, 1, window, scale, s, rope));
   return from_hip(attn::launch_rows_general(Q, Kcache, Vcache, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
-                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s));
+                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s,
+                                            rope));
 }
 
 extern "C" {
@@ -127,7 +137,8 @@ static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
                        const int32_t* lens, const uint64_t* kbits, void* O, int B, int Nq,
                        int Nkv, int Dh, int Tcap,
                        int window, float scale, float* LSE, void* workspace,
-                       size_t workspace_bytes, int dtype, void* stream) {
+                       size_t workspace_bytes, int dtype, void* stream,
+                       const attn::RopeQ* rope = nullptr) {
   int st = decode_check(q, Kcache, Vcache, lens, O, B, Nq, Nkv, Dh, Tcap, scale, dtype);
   if (st != ATTN_OK) return st;
   if (window < 0) window = 0;
@@ -136,10 +147,12 @@ static int decode_impl(const void* q, const void* Kcache, const void* Vcache,
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return ATTN_EWORKSPACE;
     return from_hip(attn::launch_decode_bf16(q, Kcache, Vcache, lens, O, LSE, B, Nq, Nkv, Dh,
-                                             Tcap, window, scale, kbits, workspace, s));
+                                             Tcap, window, scale, kbits, workspace, s, nullptr,
+                                             nullptr, nullptr, rope));
   }
   return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap,
-                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s));
+                                            lens, kbits, 1, window, scale, dtype == ATTN_BF16, s,
+                                            rope));
 }
 
 int attn_decode(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
@@ -212,6 +225,42 @@ int attn_decode_append(const void* q, const void* knew, const void* vnew, void* 
   if (e != hipSuccess) return ATTN_EHIP;
   return from_hip(attn::launch_rows_general(q, Kcache, Vcache, O, LSE, B, Nq, Nkv, 1, Dh, Tcap, lens,
                                             nullptr, 1, window, scale, dtype == ATTN_BF16, s));
+}
+
+int attn_prefill_rope(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                      void* O, float* LSE, int B, int Nq, int Nkv, int S, int Dh, int causal,
+                      int window, float scale, const float* table, int P,
+                      const int32_t* positions, const int32_t* start, int style, int dtype,
+                      void* stream) {
+  const int st = validate_rope(table, P, Dh, style);
+  if (st != ATTN_OK) return st;
+  const attn::RopeQ rope{table, P, positions, start, style};
+  return prefill_impl(Q, K, V, key_bits, O, LSE, B, Nq, Nkv, S, Dh, causal, window, scale, dtype,
+                      stream, &rope);
+}
+
+int attn_prefill_cache_rope(const void* Q, const void* Kcache, const void* Vcache,
+                            const int32_t* lens, const uint64_t* key_bits, void* O, float* LSE,
+                            int B, int Nq, int Nkv, int Sq, int Dh, int Tcap, int window,
+                            float scale, const float* table, int P, const int32_t* positions,
+                            const int32_t* start, int style, int dtype, void* stream) {
+  const int st = validate_rope(table, P, Dh, style);
+  if (st != ATTN_OK) return st;
+  const attn::RopeQ rope{table, P, positions, start, style};
+  return prefill_cache_impl(Q, Kcache, Vcache, lens, key_bits, O, LSE, B, Nq, Nkv, Sq, Dh, Tcap,
+                            window, scale, dtype, stream, &rope);
+}
+
+int attn_decode_rope(const void* q, const void* Kcache, const void* Vcache, const int32_t* lens,
+                     const uint64_t* key_bits, void* O, int B, int Nq, int Nkv, int Dh, int Tcap,
+                     int window, float scale, const float* table, int P,
+                     const int32_t* positions, int style, float* LSE, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream) {
+  const int st = validate_rope(table, P, Dh, style);
+  if (st != ATTN_OK) return st;
+  const attn::RopeQ rope{table, P, positions, nullptr, style};
+  return decode_impl(q, Kcache, Vcache, lens, key_bits, O, B, Nq, Nkv, Dh, Tcap, window, scale, LSE,
+                     workspace, workspace_bytes, dtype, stream, &rope);
 }
 
 int attn_pack_key_mask(const uint8_t* mask, int B, int T, uint64_t* key_bits, void* stream) {

@@ -98,6 +98,7 @@ struct DecParams {
   int window;     // > 0: only keys lens[b] - window .. lens[b] - 1 are visible
   int mw;         // merge: wavefronts per (sequence, query head) row, 1 to 16
   float c;        // scale * log2(e)
+  RopeQ rope;     // query rotation at load (RoPE); table == nullptr: none
 };
 
 // 16-byte chunk c of K row r sits at chunk position c ^ kswz(r) (the operand
@@ -143,7 +144,8 @@ __device__ __forceinline__ void wait_vm() {
 // NB blocks of 16 query heads per K/V head (G <= 16 * NB).  KM: a key-padding
 // mask is given (p.kbits); without it the kernel is compiled as if it did not
 // exist.  APP: the new token's K and V rows are appended in the same launch.
-template <int D, int NB, bool KM, bool APP = false>
+// RQ: the queries are rotated at load (RoPE, p.rope).
+template <int D, int NB, bool KM, bool APP = false, bool RQ = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   using geo = DGeo<D>;
   constexpr int STAGE = geo::STAGE;
@@ -255,6 +257,22 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       }
     }
 
+  // RoPE: the angle row of the query's position is loaded with q, before
+  // the cache copies; the rotation itself waits until those are issued
+  constexpr int NCS = RQ ? KS : 1;  // f32x4 cos and sin vectors per lane
+  f32x4 rc[NCS], rs[NCS];
+  if constexpr (RQ) {
+    const int pos = p.rope.positions ? p.rope.positions[b] : p.lens[b] - 1;
+    const float* cs = p.rope.table + (size_t)min(max(pos, 0), p.rope.P - 1) * D;
+    // pairs layout: elements 32*ks + 8*grp + i use angles 16*ks + 4*grp + i/2;
+    // halves: elements 32*ks + 8*grp + i (ks < KS/2) use angles 32*ks + 8*grp + i
+#pragma unroll
+    for (int u = 0; u < NCS; ++u) {
+      const int m = p.rope.style == 0 ? 16 * u + 4 * grp : 32 * (u >> 1) + 8 * grp + 4 * (u & 1);
+      rc[u] = *reinterpret_cast<const f32x4*>(cs + m);
+      rs[u] = *reinterpret_cast<const f32x4*>(cs + D / 2 + m);
+    }
+  }
   // copies in flight, oldest first: q, then K(0), V(0), K(1), V(1).  A step's
   // copies are PER_STEP vector-memory instructions, so vmcnt(PER_STEP) before
   // step s means step s has landed while step s + 1 is still in flight.
@@ -265,6 +283,42 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   load_rows<D, false>(Vh, c0 + s0 * STEP, last, V0, lane);
   load_rows<D, true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
   load_rows<D, false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
+  if constexpr (RQ) {
+    // RoPE at load: lane (grp, l16) holds elements 32*ks + 8*grp + i of its
+    // query head's row; a pair (2m, 2m+1) sits inside one fragment, a pair
+    // (m, m + D/2) in fragments ks and ks + KS/2 of the same lane
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (p.rope.style == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 x = qf[nb][ks];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float c = rc[ks][k], sn = rs[ks][k];
+            const float a = (float)x[2 * k], bb = (float)x[2 * k + 1];
+            x[2 * k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
+            x[2 * k + 1] = (__bf16)__builtin_fmaf(a, sn, bb * c);
+          }
+          qf[nb][ks] = x;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks) {
+          bf16x8 x = qf[nb][ks], y = qf[nb][ks + KS / 2];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float c = rc[2 * ks + (k >> 2)][k & 3], sn = rs[2 * ks + (k >> 2)][k & 3];
+            const float a = (float)x[k], bb = (float)y[k];
+            x[k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
+            y[k] = (__bf16)__builtin_fmaf(a, sn, bb * c);
+          }
+          qf[nb][ks] = x;
+          qf[nb][ks + KS / 2] = y;
+        }
+      }
+    }
+  }
 
   // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
   // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
@@ -659,10 +713,10 @@ DecodePlan decode_plan(int B, int Nq, int Nkv, int Tcap, int window) {
   return d;
 }
 
-template <int D, int NB, bool KM, bool APP = false>
+template <int D, int NB, bool KM, bool APP = false, bool RQ = false>
 hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM, APP>), dim3(p.n_slots, p.Nkv, p.B), dim3(64),
-                     0, stream, p);
+  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM, APP, RQ>), dim3(p.n_slots, p.Nkv, p.B),
+                     dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Nq;
@@ -675,6 +729,9 @@ hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
 template <int D, int NB>
 hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
   if (p.knew) return launch_decode_km<D, NB, false, true>(p, stream);  // append (no key mask)
+  if (p.rope.table)
+    return p.kbits ? launch_decode_km<D, NB, true, false, true>(p, stream)
+                   : launch_decode_km<D, NB, false, false, true>(p, stream);
   return p.kbits ? launch_decode_km<D, NB, true>(p, stream) : launch_decode_km<D, NB, false>(p, stream);
 }
 }  // namespace
@@ -689,7 +746,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
                               void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
                               int window, float scale, const uint64_t* kbits, void* ws,
                               hipStream_t stream, const void* knew, const void* vnew,
-                              const int32_t* slot) {
+                              const int32_t* slot, const RopeQ* rope) {
   const DecodePlan d = decode_plan(B, Nq, Nkv, Tcap, window);
   DecParams p;
   p.knew = static_cast<const __bf16*>(knew);
@@ -718,6 +775,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   p.ws_ml = p.ws_o + parts * Dh;
   p.window = window;
   p.c = kLog2e * scale;
+  p.rope = rope ? *rope : RopeQ{nullptr, 0, nullptr, nullptr, 0};
   if (Nkv > 65535 || B > 65535) return hipErrorInvalidConfiguration;
   const bool two = p.G > 16;
   switch (Dh) {

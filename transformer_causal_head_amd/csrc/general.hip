@@ -35,6 +35,7 @@ struct RowParams {
   int causal, window;
   float scale;
   long long n_rows;
+  RopeQ rope;  // query rotation at load (RoPE); table == nullptr: none
 };
 
 template <typename T>
@@ -68,6 +69,29 @@ __global__ __launch_bounds__(256) void rows_kernel(RowParams p) {
     const int d = lane + 64 * u;
     q[u] = d < p.Dh ? to_float(Q[qoff + d]) : 0.f;
     o[u] = 0.f;
+  }
+  if (p.rope.table != nullptr) {
+    // RoPE at load: element d pairs with d ^ 1 (pairs layout) or d +- Dh/2
+    // (halves); the partner is read again from Q, the rotated value rounded
+    // to the input type as a separate rotation pass would store it
+    const int half = p.Dh / 2;
+    const int rpos = p.rope.positions ? p.rope.positions[(size_t)b * p.S + i]
+                   : p.rope.start ? p.rope.start[b] + i
+                   : (p.S == 1 && p.lens ? n - 1 : pos);
+    const float* cs = p.rope.table + (size_t)min(max(rpos, 0), p.rope.P - 1) * p.Dh;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d < p.Dh) {
+        const bool first = p.rope.style == 0 ? (d & 1) == 0 : d < half;
+        const int e = p.rope.style == 0 ? (d ^ 1) : (first ? d + half : d - half);
+        const int m = p.rope.style == 0 ? d / 2 : (first ? d : d - half);
+        const float c = cs[m], s = cs[half + m];
+        const float x = q[u], y = to_float(Q[qoff + e]);
+        const float r = first ? __builtin_fmaf(x, c, -y * s) : __builtin_fmaf(y, s, x * c);
+        q[u] = to_float(from_float<T>(r));
+      }
+    }
   }
   float m = -INFINITY, l = 0.f;
   const uint64_t* kw = p.kbits ? p.kbits + (size_t)b * p.kwords : nullptr;
@@ -110,7 +134,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
                                float* LSE, int B, int Nq, int Nkv, int S, int Dh,
                                int kv_rows, const int32_t* lens, const uint64_t* kbits,
                                int causal, int window, float scale, int is_bf16,
-                               hipStream_t stream) {
+                               hipStream_t stream, const RopeQ* rope) {
   RowParams p;
   p.Q = Q;
   p.K = K;
@@ -130,6 +154,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
   p.window = window;
   p.scale = scale;
   p.n_rows = (long long)B * Nq * S;
+  p.rope = rope ? *rope : RopeQ{nullptr, 0, nullptr, nullptr, 0};
   const long long nblocks = (p.n_rows + 3) / 4;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (is_bf16)

@@ -7,6 +7,22 @@
 
 namespace attn {
 
+// Rotation of the queries (RoPE) applied by the attention kernels as they
+// load q: table [P, Dh] fp32 (cos in columns 0 .. Dh/2 - 1, sin after),
+// style 0 pairs (x[2m], x[2m+1]), 1 halves (x[m], x[m + Dh/2]).  Query row i
+// of sequence b is turned at positions[b * rows + i] when positions is given,
+// else at start[b] + i when start is given, else at the row's own position
+// (i for a prefill, lens[b] - rows + i against a cache, lens[b] - 1 for a
+// decode step), clamped to [0, P - 1].  Same fp32 arithmetic and rounding to
+// the input type as launch_rope, so the attention sees the same q bits.
+struct RopeQ {
+  const float* table;
+  int P;
+  const int32_t* positions;
+  const int32_t* start;
+  int style;
+};
+
 // Key-padding masks are passed as bits: word j / 64 of a sequence's row holds
 // key j at bit j % 64 (1 = a real token); a row of T keys has this many words.
 inline int key_mask_words(int T) { return (T + 63) / 64; }
@@ -20,7 +36,7 @@ bool prefill_bf16_supported(int Dh);
 hipError_t launch_prefill_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int B, int Nq, int Nkv, int S, int Dh, int kv_rows,
                                const int32_t* lens, const uint64_t* kbits, int causal, int window,
-                               float scale, hipStream_t stream);
+                               float scale, hipStream_t stream, const RopeQ* rope = nullptr);
 
 // General row kernel: one wavefront per output row (b, h, i), any Dh in
 // 1..256, bf16 (is_bf16 = 1) or fp32.  Same row/key convention as the MFMA
@@ -30,7 +46,7 @@ hipError_t launch_rows_general(const void* Q, const void* K, const void* V, void
                                float* LSE, int B, int Nq, int Nkv, int S, int Dh,
                                int kv_rows, const int32_t* lens, const uint64_t* kbits,
                                int causal, int window, float scale, int is_bf16,
-                               hipStream_t stream);
+                               hipStream_t stream, const RopeQ* rope = nullptr);
 
 // bf16 split-K decode (partials + log-sum-exp merge), head size 64, 128 or
 // 256, up to 32 query heads per K/V head.  The query of sequence b sees keys
@@ -45,7 +61,8 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
                               void* O, float* LSE, int B, int Nq, int Nkv, int Dh, int Tcap,
                               int window, float scale, const uint64_t* kbits, void* ws,
                               hipStream_t stream, const void* knew = nullptr,
-                              const void* vnew = nullptr, const int32_t* slot = nullptr);
+                              const void* vnew = nullptr, const int32_t* slot = nullptr,
+                              const RopeQ* rope = nullptr);
 
 // The allocation-free decode's fixed device scratch: its size, and its address
 // on the current device (looked up on the first call per device).

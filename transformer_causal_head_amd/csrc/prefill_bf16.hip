@@ -86,6 +86,8 @@ struct Params {
   // NW / hp - 1, so that every workgroup of a causal prefill holds early and
   // late queries alike (used when the whole grid runs in one round).
   int strided;
+  // query rotation at load (RoPE), table == nullptr: none
+  RopeQ rope;
   // causal one-round grids of 4-wave workgroups (two per CU): the first half
   // of the grid takes the query tiles heaviest first, the second half
   // lightest first, so that the two workgroups a CU receives together stream
@@ -337,6 +339,51 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.Q + q_base + (size_t)qrow * D + hl * 8);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = src[ks * 2];
+  }
+  if (p.rope.table != nullptr) {
+    // RoPE at load: this lane holds elements 16*ks + 8*hl + i of its query
+    // row; a pair (2m, 2m+1) sits inside one fragment, a pair (m, m + D/2)
+    // in fragments ks and ks + KS/2 of the same lane
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = min(qa_row + qb * 32 + ln, p.S - 1);
+      const int pos = p.rope.positions ? p.rope.positions[(size_t)b * p.S + qrow]
+                                       : (p.rope.start ? p.rope.start[b] : q_off) + qrow;
+      const float* cs = p.rope.table + (size_t)min(max(pos, 0), p.rope.P - 1) * D;
+      if (p.rope.style == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 8 * ks + 4 * hl);
+          const f32x4 s = *reinterpret_cast<const f32x4*>(cs + D / 2 + 8 * ks + 4 * hl);
+          bf16x8 x = qf[qb][ks];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float a = (float)x[2 * k], bb = (float)x[2 * k + 1];
+            x[2 * k] = (__bf16)__builtin_fmaf(a, c[k], -bb * s[k]);
+            x[2 * k + 1] = (__bf16)__builtin_fmaf(a, s[k], bb * c[k]);
+          }
+          qf[qb][ks] = x;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks) {
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + 16 * ks + 8 * hl);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 16 * ks + 8 * hl + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + D / 2 + 16 * ks + 8 * hl);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + D / 2 + 16 * ks + 8 * hl + 4);
+          bf16x8 x = qf[qb][ks], y = qf[qb][ks + KS / 2];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float c = k < 4 ? c0[k] : c1[k - 4], s = k < 4 ? s0[k] : s1[k - 4];
+            const float a = (float)x[k], bb = (float)y[k];
+            x[k] = (__bf16)__builtin_fmaf(a, c, -bb * s);
+            y[k] = (__bf16)__builtin_fmaf(a, s, bb * c);
+          }
+          qf[qb][ks] = x;
+          qf[qb][ks + KS / 2] = y;
+        }
+      }
+    }
   }
 
   // LDS byte offsets inside a tile
@@ -696,7 +743,7 @@ template <int D>
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
                           int B, int Nq, int Nkv, int S, int kv_rows, const int32_t* lens,
                           const uint64_t* kbits, int causal, int window, float scale,
-                          hipStream_t stream) {
+                          hipStream_t stream, const RopeQ* rope) {
   constexpr int NW = waves_for<D>();
   // one head of K (or V) is addressed through a 31-bit buffer range
   if ((long long)kv_rows * D * 2 > 0x7fffffffLL || (long long)S * D * 2 > 0x7fffffffLL)
@@ -719,6 +766,7 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.window = window;
   p.c = scale * kLog2e;
   p.G = Nq / Nkv;
+  p.rope = rope ? *rope : RopeQ{nullptr, 0, nullptr, nullptr, 0};
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -791,17 +839,17 @@ bool prefill_bf16_supported(int Dh) { return Dh == 64 || Dh == 128 || Dh == 256;
 hipError_t launch_prefill_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int B, int Nq, int Nkv, int S, int Dh, int kv_rows,
                                const int32_t* lens, const uint64_t* kbits, int causal, int window,
-                               float scale, hipStream_t stream) {
+                               float scale, hipStream_t stream, const RopeQ* rope) {
   switch (Dh) {
     case 64:
       return launch_prefill<64>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
-                                window, scale, stream);
+                                window, scale, stream, rope);
     case 128:
       return launch_prefill<128>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
-                                 window, scale, stream);
+                                 window, scale, stream, rope);
     case 256:
       return launch_prefill<256>(Q, K, V, O, LSE, B, Nq, Nkv, S, kv_rows, lens, kbits, causal,
-                                 window, scale, stream);
+                                 window, scale, stream, rope);
     default:
       return hipErrorInvalidValue;
   }
