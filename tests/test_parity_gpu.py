@@ -251,6 +251,12 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
     check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, Tcap, lens), storage_allowance=True)
 
 
+# wavefronts of the even split's partial grid (its workspace slots are
+# B * Nkv + EVEN_WAVES); it serves up to 64 sequences at head sizes up to 128
+# when the chunk mode's grid would have at least EVEN_WAVES / 2 items
+EVEN_WAVES = 1024
+
+
 def _decode_chunk(B, Nkv, Tcap, G):
     # the host's choice of keys per chunk, restated: the longest candidate that
     # gives at least 2048 (sequence, K/V head, chunk) items at full length,
@@ -272,19 +278,37 @@ def _decode_chunk(B, Nkv, Tcap, G):
     (16, 32, 2, 16384, 384),    # 16 query heads per K/V head: 1024 items
     (9, 32, 1, 3000, 224),      # MQA, the floor for wide groups
     (64, 32, 1, 32768, 1792),   # MQA with 32 query heads
+    (80, 32, 8, 3000, 896),     # more than 64 sequences: chunk mode without a mask
 ])
-def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch):
+@pytest.mark.parametrize("masked", [False, True])
+def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch, masked):
     # every chunk length the host can pick, with lengths on and around chunk
-    # edges; the workspace size shows which chunk length was taken
+    # edges; the workspace size shows which chunk length was taken.  Without a
+    # key-padding mask the larger grids of up to 64 sequences run the even
+    # split (the workspace also holds its slots); an all-true mask keeps the
+    # same case in chunk mode.
     assert _decode_chunk(B, Nkv, Tcap, Nq // Nkv) == ch
     ws = tch.attn_decode_workspace_bytes(B, Nq, Nkv, 128, Tcap, tch.ATTN_BF16)
-    assert ws == B * Nq * -(-Tcap // ch) * (128 + 2) * 4
+    slots = B * Nkv * -(-Tcap // ch)
+    if B <= 64 and slots >= EVEN_WAVES // 2:
+        slots = max(slots, B * Nkv + EVEN_WAVES)
+    assert ws == slots * (Nq // Nkv) * (128 + 2) * 4
     rng = np.random.default_rng(Tcap + B)
     lens = rng.integers(1, Tcap, B, endpoint=True)
     lens[:8] = [1, 31, 32, 33, ch - 1, ch, ch + 1, Tcap]
     lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, 128, Tcap, 1, Tcap, seed=ch,
                                                 lens=lens)
-    O, L = run_decode(q, kc, vc, lens_a, "bf16")
+    if masked:
+        dev = device()
+        tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+        tl = torch.from_numpy(np.asarray(lens_a, dtype=np.int32)).to(dev)
+        Ot, Lt = tch.decode(tq, tk, tv, tl, key_mask=torch.ones(B, Tcap, dtype=torch.bool, device=dev))
+        torch.cuda.synchronize()
+        O = workloads.to_f64(workloads.from_torch(Ot, "bf16"), "bf16")
+        L = Lt.cpu().numpy().astype(np.float64)
+        del tq, tk, tv
+    else:
+        O, L = run_decode(q, kc, vc, lens_a, "bf16")
     rows = [(b, h) for b in range(8) for h in (0, Nq - 1)]
     rows += [(int(b), int(h)) for b, h in zip(rng.integers(8, B, 32), rng.integers(0, Nq, 32))]
     Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), _LazyF64(kc), _LazyF64(vc), lens_a,
@@ -292,6 +316,50 @@ def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch):
     Os = np.stack([O[b, h] for b, h in rows])
     Ls = np.array([L[b, h] for b, h in rows])
     say(f"chunk {ch}: errors {check(Os, Ls, Or, Lr, 'bf16', (B, Nkv, Tcap, ch), storage_allowance=True)}")
+
+
+def _even_lens(kind, B, Tcap, rng):
+    if kind == "short":          # many whole segments inside one wavefront's range
+        return rng.integers(1, 100, B, endpoint=True)
+    if kind == "one_long":       # one segment split over many more than 64 ranges
+        lens = np.ones(B, dtype=np.int64)
+        lens[B // 2] = Tcap
+        return lens
+    return rng.integers(1, Tcap, B, endpoint=True)
+
+
+@pytest.mark.parametrize("Dh,B,Nq,Nkv,Tcap,kind,window", [
+    (128, 64, 32, 8, 100, "short", 0),        # 50 of the 1024 wavefronts in use
+    (128, 64, 32, 8, 3000, "ragged", 0),
+    (128, 64, 32, 8, 5000, "ragged", 100),    # window: segments start mid-step
+    (128, 37, 32, 1, 4000, "ragged", 0),      # 32 query heads per K/V head (two blocks)
+    (128, 16, 4, 1, 60000, "one_long", 0),    # a row's pieces run past one merge round
+    (128, 16, 32, 1, 60000, "one_long", 0),
+    (64, 45, 16, 4, 2500, "ragged", 0),
+    (64, 64, 32, 2, 3000, "ragged", 777),
+])
+def test_decode_even_split(Dh, B, Nq, Nkv, Tcap, kind, window):
+    # up to 64 sequences without a key-padding mask: the visible steps of all
+    # (sequence, K/V head) pairs are cut into equal wavefront ranges; ranges
+    # that hold several segments, segments split over many ranges, windows,
+    # and totals too small to fill the grid
+    rng = np.random.default_rng(Tcap + B + Dh)
+    lens = _even_lens(kind, B, Tcap, rng)
+    lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, seed=B + Dh,
+                                                lens=lens)
+    dev = device()
+    tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, kc, vc))
+    tl = torch.from_numpy(np.asarray(lens_a, dtype=np.int32)).to(dev)
+    Ot, Lt = tch.decode(tq, tk, tv, tl, window=window)
+    torch.cuda.synchronize()
+    O = workloads.to_f64(workloads.from_torch(Ot, "bf16"), "bf16")
+    L = Lt.cpu().numpy().astype(np.float64)
+    rows = [(b, h) for b in range(B) for h in (0, Nq - 1)]
+    Or, Lr = oracle.decode_ref(workloads.to_f64(q, "bf16"), _LazyF64(kc), _LazyF64(vc), lens_a,
+                               window=window, rows=rows)
+    Os = np.stack([O[b, h] for b, h in rows])
+    Ls = np.array([L[b, h] for b, h in rows])
+    say(f"even split {kind}: errors {check(Os, Ls, Or, Lr, 'bf16', (Dh, B, Nq, Nkv, Tcap, window), storage_allowance=True)}")
 
 
 @pytest.mark.parametrize("Dh,B,Nq,Nkv,Tcap,lens", [

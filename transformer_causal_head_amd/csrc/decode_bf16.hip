@@ -37,6 +37,15 @@
 //     ds_read_b64_tr_b16; row-XOR swizzles keep both conflict free.  More than
 //     16 query heads per K/V head (up to 32: MQA) take a second N block that
 //     reuses every K and V fragment.
+//   * Even split (small grids: at most 64 sequences and few chunk items): the
+//     visible steps of all (sequence, K/V head) pairs are laid end to end and
+//     cut into equal ranges, one per wavefront of a fixed grid of 1280 (five
+//     per CU).  Per-sequence chunks leave a grid of mixed-length items (every
+//     sequence's last chunk is short, sequences end at different chunks) that
+//     the dispatcher spreads unevenly when they all run at once; equal ranges
+//     finish together.  A range crossing a (sequence, K/V head) boundary
+//     writes one partial per piece, piece (segment s, wavefront w) to slot
+//     s + w, so the merge finds a segment's pieces in one contiguous run.
 //   * Every K and V byte is read once per K/V head and shared by its G query
 //     heads.  Rows at or past the length are never used: copy addresses clamp
 //     to the last valid row and those keys get probability 0.
@@ -54,6 +63,14 @@ namespace {
 constexpr int STEP = 32;             // keys per pipeline step
 constexpr float TAU = 8.f;
 constexpr int kNonTemporal = 2;      // cache-policy bit of the copy instructions
+// even split: wavefronts of the partial grid -- four per CU, all resident at
+// once (more would leave a second round for the rest)
+constexpr int kEvenWaves = 1024;
+// shortest chunk (and shortest even-split range): 640 keys, 224 with 16 or
+// more query heads per K/V head -- shorter ones cost more in partials to
+// write and merge than their extra parallelism gains
+constexpr int kFloorKeys = 640;
+constexpr int kFloorKeysWide = 224;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -97,6 +114,8 @@ struct DecParams {
   int ch;         // keys per chunk (a multiple of STEP)
   int window;     // > 0: only keys lens[b] - window .. lens[b] - 1 are visible
   int mw;         // merge: wavefronts per (sequence, query head) row, 1 to 16
+  int ev_nw;      // even split: wavefronts of the partial grid (0: one per chunk)
+  int ev_min;     // even split: fewest steps per wavefront range
   float c;        // scale * log2(e)
   RopeQ rope;     // query rotation at load (RoPE); table == nullptr: none
 };
@@ -114,6 +133,36 @@ template <int D>
 __device__ __forceinline__ int vswz(int r) {
   if constexpr (D == 64) return ((r & 1) << 1) ^ (((r >> 1) & 1) << 2) ^ (((r >> 2) & 1) << 1);
   else return ((r << 1) & 14) | ((r >> 3) & 1);
+}
+
+// Even split: lane j < B describes sequence j -- its visible length n, first
+// visible key lo, and ns, the steps of 32 keys that hold visible keys (step
+// indices lo/32 .. (n-1)/32) -- and incl is the inclusive prefix sum of ns
+// over the lanes.  Segment (b, g) covers global steps Nkv*(incl_b - ns_b) +
+// g*ns_b onwards; tot is the total, nwe the wavefronts in use (ranges of at
+// least p.ev_min steps, at most p.ev_nw of them).  Both kernels compute it the
+// same way from the lengths, so they agree on every range.
+struct EvenTable {
+  int n, lo, ns, incl, nwe;
+  long long tot;
+};
+__device__ __forceinline__ EvenTable even_table(const DecParams& p, int lane) {
+  EvenTable t = {0, 0, 0, 0, 1, 0};
+  if (lane < p.B) {
+    t.n = max(0, min(p.lens[lane], p.Tcap));
+    t.lo = p.window > 0 ? max(0, t.n - p.window) : 0;
+    t.ns = t.n > 0 ? (t.n - 1) / STEP - t.lo / STEP + 1 : 0;
+  }
+  int v = t.ns;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  t.incl = v;
+  t.tot = (long long)__shfl(v, 63, 64) * p.Nkv;
+  t.nwe = (int)max(1LL, min((long long)p.ev_nw, t.tot / p.ev_min));
+  return t;
 }
 
 // Rows [k0, k0+32) of one head -> one LDS stage: NPIECE copies of RP whole
@@ -144,9 +193,12 @@ __device__ __forceinline__ void wait_vm() {
 // NB blocks of 16 query heads per K/V head (G <= 16 * NB).  KM: a key-padding
 // mask is given (p.kbits); without it the kernel is compiled as if it did not
 // exist.  APP: the new token's K and V rows are appended in the same launch.
-// RQ: the queries are rotated at load (RoPE, p.rope).
-template <int D, int NB, bool KM, bool APP = false, bool RQ = false>
+// RQ: the queries are rotated at load (RoPE, p.rope).  EV: even split (the
+// grid is p.ev_nw wavefronts, each taking one range of the steps of all
+// (sequence, K/V head) pairs laid end to end); chunk mode otherwise.
+template <int D, int NB, bool KM, bool APP = false, bool RQ = false, bool EV = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
+  static_assert(!EV || !KM, "even split: no key-padding mask");
   using geo = DGeo<D>;
   constexpr int STAGE = geo::STAGE;
   constexpr int KS = geo::KS;
@@ -164,53 +216,119 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   lds_char* const V0 = (lds_char*)v0s;
   lds_char* const V1 = (lds_char*)v1s;
 
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int n = min(p.lens[b], p.Tcap);
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;  // first visible key
-  // workgroup x takes the x-th chunk from the one holding key lo
-  const int chunk = lo / p.ch + blockIdx.x;
-  const int c0 = chunk * p.ch;
-
+  const int lane = threadIdx.x & 63;
+  // The work item: steps s0 .. nsteps-1 of 32 keys from key c0 of (sequence b,
+  // K/V head g), keys lo .. n-1 visible, rows clamped to `last`; its partial
+  // goes to slot `slot` (G rows of the workspace from slot * G).
+  int b, g, n, lo, c0, s0 = 0, nsteps = 0, last = 0;
+  size_t slot;
+  EvenTable tab;
+  long long ev_a = 0, ev_e = 0;  // even split: this wavefront's global steps still to run
+  int ev_w = 0;
   // append: lane l < NC holds 16 bytes of the new K row, NC <= l < 2 NC of the
-  // new V row (loaded before any copy, so the copy waits cover it).  Workgroup
-  // 0 of (sequence, K/V head) writes them to cache row slot[b]; the chunk that
-  // holds that row (if the query sees it) copies the cache as usual and then
-  // overwrites that row of its LDS stage with them, so no workgroup uses the
-  // row being written.
+  // new V row (loaded before any copy, so the copy waits cover it).  One
+  // `writer` wavefront per (sequence, K/V head) -- chunk 0, or the wavefront
+  // whose range starts the segment -- writes them to cache row slot[b]; the
+  // work item that holds that row (if the query sees it) copies the cache as
+  // usual and then overwrites that row of its LDS stage with them, so no
+  // wavefront uses the row being written.
   constexpr int NCH = D / 8;
   u32x4 new_row = {};
   int alt_row = -1;
-  if constexpr (APP) {
-    const size_t nrow = ((size_t)b * p.Nkv + g) * D;
-    const int l = threadIdx.x;
-    if (l < NCH)
-      new_row = *reinterpret_cast<const u32x4*>(p.knew + nrow + l * 8);
-    else if (l < 2 * NCH)
-      new_row = *reinterpret_cast<const u32x4*>(p.vnew + nrow + (l - NCH) * 8);
-    const int sl = p.slot[b];
-    if (sl >= max(lo, c0) && sl < min(n, c0 + p.ch)) alt_row = sl;
-  }
+  bool writer = false;
+  // the new rows of (b, g); the item's keys run from k_lo to k_hi
+  auto load_new = [&](int k_lo, int k_hi) {
+    if constexpr (APP) {
+      const size_t nrow = ((size_t)b * p.Nkv + g) * D;
+      if (lane < NCH)
+        new_row = *reinterpret_cast<const u32x4*>(p.knew + nrow + lane * 8);
+      else if (lane < 2 * NCH)
+        new_row = *reinterpret_cast<const u32x4*>(p.vnew + nrow + (lane - NCH) * 8);
+      const int sl = p.slot[b];
+      alt_row = sl >= max(lo, k_lo) && sl < min(n, k_hi) ? sl : -1;
+    }
+  };
   auto write_new_row = [&]() {
     if constexpr (APP) {
       const int sl = p.slot[b];
-      const int l = threadIdx.x;
-      if (blockIdx.x == 0 && sl >= 0 && sl < p.Tcap && l < 2 * NCH) {
-        __bf16* dst = (l < NCH ? p.Kw : p.Vw) + (((size_t)b * p.Nkv + g) * p.Tcap + sl) * D;
-        *reinterpret_cast<u32x4*>(dst + (l % NCH) * 8) = new_row;
+      if (writer && sl >= 0 && sl < p.Tcap && lane < 2 * NCH) {
+        __bf16* dst = (lane < NCH ? p.Kw : p.Vw) + (((size_t)b * p.Nkv + g) * p.Tcap + sl) * D;
+        *reinterpret_cast<u32x4*>(dst + (lane % NCH) * 8) = new_row;
       }
     }
   };
-  if (c0 >= n) {
-    write_new_row();
-    return;
+
+  // even split: take the segment (b, g) from its step s_in to the end of the
+  // segment or of this wavefront's range
+  auto enter = [&](int s_in) {
+    n = __builtin_amdgcn_readlane(tab.n, b);
+    lo = __builtin_amdgcn_readlane(tab.lo, b);
+    const int ns_b = __builtin_amdgcn_readlane(tab.ns, b);
+    const int cnt = (int)min((long long)(ns_b - s_in), ev_e - ev_a);
+    c0 = 0;
+    s0 = lo / STEP + s_in;
+    nsteps = s0 + cnt;
+    // rows past the piece clamp to its last row: the copies issued past its
+    // end then re-read one row instead of the next wavefront's keys
+    last = min(n, nsteps * STEP) - 1;
+    slot = (size_t)b * p.Nkv + g + ev_w;
+    ev_a += cnt;
+    writer = s_in == 0;
+    load_new(s0 * STEP, nsteps * STEP);
+  };
+  if constexpr (EV) {
+    tab = even_table(p, lane);
+    ev_w = blockIdx.x;
+    if constexpr (APP) {
+      // a sequence with no visible key has no range: wavefront 0 writes its
+      // new rows (nothing reads them in this launch)
+      if (ev_w == 0) {
+        for (uint64_t zb = __builtin_amdgcn_ballot_w64(lane < p.B && tab.ns == 0); zb; zb &= zb - 1) {
+          const int bz = __builtin_ctzll(zb);
+          const int sl = p.slot[bz];
+          if (sl < 0 || sl >= p.Tcap) continue;
+          for (int gz = 0; gz < p.Nkv; ++gz) {
+            if (lane < 2 * NCH) {
+              const size_t head = (size_t)bz * p.Nkv + gz;
+              const u32x4 v = *reinterpret_cast<const u32x4*>((lane < NCH ? p.knew : p.vnew) +
+                                                              head * D + (lane % NCH) * 8);
+              __bf16* dst = (lane < NCH ? p.Kw : p.Vw) + (head * p.Tcap + sl) * D;
+              *reinterpret_cast<u32x4*>(dst + (lane % NCH) * 8) = v;
+            }
+          }
+        }
+      }
+    }
+    if (ev_w >= tab.nwe) return;
+    ev_a = (long long)ev_w * tab.tot / tab.nwe;
+    ev_e = (long long)(ev_w + 1) * tab.tot / tab.nwe;
+    if (ev_a >= ev_e) return;
+    // the segment holding step ev_a: sequence b is the first whose steps end
+    // past it (every lane at or past B holds the total)
+    b = __builtin_popcountll(__builtin_amdgcn_ballot_w64((long long)tab.incl * p.Nkv <= ev_a));
+    const int ns_b = __builtin_amdgcn_readlane(tab.ns, b);
+    const long long off = ev_a - (long long)(__builtin_amdgcn_readlane(tab.incl, b) - ns_b) * p.Nkv;
+    g = (int)(off / ns_b);
+    enter((int)(off - (long long)g * ns_b));
+  } else {
+    g = blockIdx.y;
+    b = blockIdx.z;
+    n = min(p.lens[b], p.Tcap);
+    lo = p.window > 0 ? max(0, n - p.window) : 0;  // first visible key
+    // workgroup x takes the x-th chunk from the one holding key lo
+    c0 = (lo / p.ch + blockIdx.x) * p.ch;
+    slot = ((size_t)b * p.Nkv + g) * p.n_slots + blockIdx.x;
+    writer = blockIdx.x == 0;
+    load_new(c0, c0 + p.ch);
+    if (c0 >= n) {
+      write_new_row();
+      return;
+    }
+    s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
+    nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
+    last = min(n, c0 + p.ch) - 1;
   }
 
-  int s0 = lo > c0 ? (lo - c0) / STEP : 0;  // first step holding a visible key
-  int nsteps = (min(p.ch, n - c0) + STEP - 1) / STEP;
-  const int last = min(n, c0 + p.ch) - 1;
-
-  const int lane = threadIdx.x;
   // key-padding flags: lane j holds the 32 flags of step s_flags + j (a chunk
   // has at most 64 steps), read in the loop with v_readlane
   const int s_flags = s0;
@@ -236,316 +354,337 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int G = p.G;
+  // chunk mode runs this body once; the even split once per segment piece
+  for (;;) {
 
-  const size_t kvh = ((size_t)b * p.Nkv + g) * (size_t)p.Tcap * D;
-  const __bf16* Kh = p.K + kvh;
-  const __bf16* Vh = p.V + kvh;
+    const size_t kvh = ((size_t)b * p.Nkv + g) * (size_t)p.Tcap * D;
+    const __bf16* Kh = p.K + kvh;
+    const __bf16* Vh = p.V + kvh;
 
-  // q^T operand: lane (grp, l16) of block nb holds
-  // q[head g*G + 16*nb + l16][32*ks + 8*grp + i]
-  bf16x8 qf[NB][KS];
+    // q^T operand: lane (grp, l16) of block nb holds
+    // q[head g*G + 16*nb + l16][32*ks + 8*grp + i]
+    bf16x8 qf[NB][KS];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int hh = 16 * nb + l16;
-      if (hh < G) {
-        const __bf16* src = p.q + ((size_t)b * p.Nq + (size_t)g * G + hh) * D + ks * 32 + grp * 8;
-        qf[nb][ks] = *reinterpret_cast<const bf16x8*>(src);
-      } else {
-        qf[nb][ks] = bf16x8{};
-      }
-    }
-
-  // RoPE: the angle row of the query's position is loaded with q, before
-  // the cache copies; the rotation itself waits until those are issued
-  constexpr int NCS = RQ ? KS : 1;  // f32x4 cos and sin vectors per lane
-  f32x4 rc[NCS], rs[NCS];
-  if constexpr (RQ) {
-    const int pos = p.rope.positions ? p.rope.positions[b] : p.lens[b] - 1;
-    const float* cs = p.rope.table + (size_t)min(max(pos, 0), p.rope.P - 1) * D;
-    // pairs layout: elements 32*ks + 8*grp + i use angles 16*ks + 4*grp + i/2;
-    // halves: elements 32*ks + 8*grp + i (ks < KS/2) use angles 32*ks + 8*grp + i
-#pragma unroll
-    for (int u = 0; u < NCS; ++u) {
-      const int m = p.rope.style == 0 ? 16 * u + 4 * grp : 32 * (u >> 1) + 8 * grp + 4 * (u & 1);
-      rc[u] = *reinterpret_cast<const f32x4*>(cs + m);
-      rs[u] = *reinterpret_cast<const f32x4*>(cs + D / 2 + m);
-    }
-  }
-  // copies in flight, oldest first: q, then K(0), V(0), K(1), V(1).  A step's
-  // copies are PER_STEP vector-memory instructions, so vmcnt(PER_STEP) before
-  // step s means step s has landed while step s + 1 is still in flight.
-  // Copies are issued for two steps past the chunk's end too (all rows clamp
-  // to its last row and mostly hit L2), so that count holds on every path and
-  // the compiler adds no full drain of its own.
-  load_rows<D, true>(Kh, c0 + s0 * STEP, last, K0, lane);
-  load_rows<D, false>(Vh, c0 + s0 * STEP, last, V0, lane);
-  load_rows<D, true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
-  load_rows<D, false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
-  if constexpr (RQ) {
-    // RoPE at load: lane (grp, l16) holds elements 32*ks + 8*grp + i of its
-    // query head's row; a pair (2m, 2m+1) sits inside one fragment, a pair
-    // (m, m + D/2) in fragments ks and ks + KS/2 of the same lane
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (p.rope.style == 0) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 x = qf[nb][ks];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float c = rc[ks][k], sn = rs[ks][k];
-            const float a = (float)x[2 * k], bb = (float)x[2 * k + 1];
-            x[2 * k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
-            x[2 * k + 1] = (__bf16)__builtin_fmaf(a, sn, bb * c);
-          }
-          qf[nb][ks] = x;
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS / 2; ++ks) {
-          bf16x8 x = qf[nb][ks], y = qf[nb][ks + KS / 2];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float c = rc[2 * ks + (k >> 2)][k & 3], sn = rs[2 * ks + (k >> 2)][k & 3];
-            const float a = (float)x[k], bb = (float)y[k];
-            x[k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
-            y[k] = (__bf16)__builtin_fmaf(a, sn, bb * c);
-          }
-          qf[nb][ks] = x;
-          qf[nb][ks + KS / 2] = y;
-        }
-      }
-    }
-  }
-
-  // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
-  // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
-  int voff[2][DB];
-  {
-    const int ip = l16 >> 2, u = l16 & 3;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int r = 16 * hf + 4 * grp + ip;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        voff[hf][db] = r * geo::RB + (((2 * db + (u >> 1)) ^ vswz<D>(r)) << 4) + (u & 1) * 8;
-    }
-  }
-  // K operand offsets: row 16*kb + l16, 16-byte chunk 4*ks + grp (the K
-  // swizzle does not depend on row bit 4, so one offset serves both kb)
-  int koff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    koff[ks] = l16 * geo::RB + (((4 * ks + grp) ^ kswz<D>(l16)) << 4);
-
-  f32x4 o[NB][DB];
-  float m_run[NB], l_run[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
-  }
-
-  // Where the registers allow (Dh x query-head blocks <= 256), a step's V^T
-  // operands are read right after its K operands, and its PV products run in
-  // finish_pv() after the copies that refill its stage have been issued: the
-  // products read only registers, so the copies need not queue behind them.
-  constexpr bool EARLY_V = D * NB <= 256;
-  bf16x8 va[EARLY_V ? DB : 1];
-  bf16x8 pf[NB];
-  bool pv_pending = false;
-  auto finish_pv = [&]() {
-    if constexpr (EARLY_V) {
-      if (pv_pending) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf[nb], o[nb][db], 0, 0, 0);
-        pv_pending = false;
-      }
-    }
-  };
-  auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
-    const int k0 = c0 + s * STEP;
-    // flags of keys k0 .. k0 + 31 (k0 is a multiple of 32); a step of padding
-    // keys only changes nothing
-    uint32_t kw = ~0u;
-    if constexpr (KM) {
-      kw = __builtin_amdgcn_readlane(kw_lane, s - s_flags);
-      if (kw == 0) return;
-    }
-    // S^T = K q^T; accumulator register r of block kb: key k0 + 16*kb + 4*grp + r,
-    // query column l16 of head block nb
-    f32x4 sc[NB][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb][kb] = f32x4{};
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(lds_bf16x8*)(kst + kb * 16 * geo::RB + koff[ks]);
+        const int hh = 16 * nb + l16;
+        if (hh < G) {
+          const __bf16* src = p.q + ((size_t)b * p.Nq + (size_t)g * G + hh) * D + ks * 32 + grp * 8;
+          qf[nb][ks] = *reinterpret_cast<const bf16x8*>(src);
+        } else {
+          qf[nb][ks] = bf16x8{};
+        }
+      }
+
+    // RoPE: the angle row of the query's position is loaded with q, before
+    // the cache copies; the rotation itself waits until those are issued
+    constexpr int NCS = RQ ? KS : 1;  // f32x4 cos and sin vectors per lane
+    f32x4 rc[NCS], rs[NCS];
+    if constexpr (RQ) {
+      const int pos = p.rope.positions ? p.rope.positions[b] : p.lens[b] - 1;
+      const float* cs = p.rope.table + (size_t)min(max(pos, 0), p.rope.P - 1) * D;
+      // pairs layout: elements 32*ks + 8*grp + i use angles 16*ks + 4*grp + i/2;
+      // halves: elements 32*ks + 8*grp + i (ks < KS/2) use angles 32*ks + 8*grp + i
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], sc[nb][kb], 0, 0, 0);
+      for (int u = 0; u < NCS; ++u) {
+        const int m = p.rope.style == 0 ? 16 * u + 4 * grp : 32 * (u >> 1) + 8 * grp + 4 * (u & 1);
+        rc[u] = *reinterpret_cast<const f32x4*>(cs + m);
+        rs[u] = *reinterpret_cast<const f32x4*>(cs + D / 2 + m);
       }
     }
-    // V^T operands of this step, read now where the registers allow: they
-    // return while the softmax runs
-    auto read_v = [&](int db) {
-      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    if constexpr (EARLY_V) {
+    // copies in flight, oldest first: q, then K(0), V(0), K(1), V(1).  A step's
+    // copies are PER_STEP vector-memory instructions, so vmcnt(PER_STEP) before
+    // step s means step s has landed while step s + 1 is still in flight.
+    // Copies are issued for two steps past the chunk's end too (all rows clamp
+    // to its last row and mostly hit L2), so that count holds on every path and
+    // the compiler adds no full drain of its own.
+    load_rows<D, true>(Kh, c0 + s0 * STEP, last, K0, lane);
+    load_rows<D, false>(Vh, c0 + s0 * STEP, last, V0, lane);
+    load_rows<D, true>(Kh, c0 + (s0 + 1) * STEP, last, K1, lane);
+    load_rows<D, false>(Vh, c0 + (s0 + 1) * STEP, last, V1, lane);
+    if constexpr (RQ) {
+      // RoPE at load: lane (grp, l16) holds elements 32*ks + 8*grp + i of its
+      // query head's row; a pair (2m, 2m+1) sits inside one fragment, a pair
+      // (m, m + D/2) in fragments ks and ks + KS/2 of the same lane
 #pragma unroll
-      for (int db = 0; db < DB; ++db) va[db] = read_v(db);
-    }
-    if (k0 + STEP > n || k0 < lo || (KM && kw != ~0u)) {
+      for (int nb = 0; nb < NB; ++nb) {
+        if (p.rope.style == 0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 x = qf[nb][ks];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + kb * 16 + grp * 4 + r;
-          bool hide = key >= n || key < lo;
-          if (KM) hide = hide || !((kw >> (kb * 16 + grp * 4 + r)) & 1);
-          if (hide) {
+            for (int k = 0; k < 4; ++k) {
+              const float c = rc[ks][k], sn = rs[ks][k];
+              const float a = (float)x[2 * k], bb = (float)x[2 * k + 1];
+              x[2 * k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
+              x[2 * k + 1] = (__bf16)__builtin_fmaf(a, sn, bb * c);
+            }
+            qf[nb][ks] = x;
+          }
+        } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) sc[nb][kb][r] = -INFINITY;
+          for (int ks = 0; ks < KS / 2; ++ks) {
+            bf16x8 x = qf[nb][ks], y = qf[nb][ks + KS / 2];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float c = rc[2 * ks + (k >> 2)][k & 3], sn = rs[2 * ks + (k >> 2)][k & 3];
+              const float a = (float)x[k], bb = (float)y[k];
+              x[k] = (__bf16)__builtin_fmaf(a, c, -bb * sn);
+              y[k] = (__bf16)__builtin_fmaf(a, sn, bb * c);
+            }
+            qf[nb][ks] = x;
+            qf[nb][ks + KS / 2] = y;
           }
         }
+      }
     }
+
+    // transposing-read offsets: A operand of O^T += V^T P^T, d = 16*db + l16,
+    // keys 4*grp + i (first read) and 16 + 4*grp + i (second read)
+    int voff[2][DB];
+    {
+      const int ip = l16 >> 2, u = l16 & 3;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = 16 * hf + 4 * grp + ip;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          voff[hf][db] = r * geo::RB + (((2 * db + (u >> 1)) ^ vswz<D>(r)) << 4) + (u & 1) * 8;
+      }
+    }
+    // K operand offsets: row 16*kb + l16, 16-byte chunk 4*ks + grp (the K
+    // swizzle does not depend on row bit 4, so one offset serves both kb)
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      koff[ks] = l16 * geo::RB + (((4 * ks + grp) ^ kswz<D>(l16)) << 4);
+
+    f32x4 o[NB][DB];
+    float m_run[NB], l_run[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      f32x4 (&t)[2] = sc[nb];
-      float mx = fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
-                       fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // every step run holds a visible key unless a key-padding mask hides it
-      const float m_cand = mx * p.c;
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + TAU)) {
-        const float m_new = fmaxf(m_run[nb], m_cand);
-        const float alpha = exp2_fast(m_run[nb] - m_new);
-        m_run[nb] = m_new;
-        l_run[nb] *= alpha;
+      m_run[nb] = -INFINITY;
+      l_run[nb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
-      }
-      const float m_use = (KM && m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = exp2_fast(__builtin_fmaf(t[kb][r], p.c, -m_use));
-          t[kb][r] = e;
-          rs += e;
-        }
-      l_run[nb] += rs;
-      u32x4 pk;
-      pk[0] = pack_bf16x2(t[0][0], t[0][1]);
-      pk[1] = pack_bf16x2(t[0][2], t[0][3]);
-      pk[2] = pack_bf16x2(t[1][0], t[1][1]);
-      pk[3] = pack_bf16x2(t[1][2], t[1][3]);
-      pf[nb] = __builtin_bit_cast(bf16x8, pk);
+      for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{};
     }
-    if constexpr (EARLY_V) {
-      pv_pending = true;  // the products run in finish_pv()
+
+    // Where the registers allow (Dh x query-head blocks <= 256), a step stops
+    // once its K and V^T operands are in registers; its softmax and PV
+    // products run in finish_pv(), after the copies that refill its stage have
+    // been issued: they read only registers, so the copies need not queue
+    // behind them (and a wave keeps more bytes in flight).
+    constexpr bool EARLY_V = D * NB <= 256;
+    bf16x8 va[EARLY_V ? DB : 1];
+    bf16x8 pf[NB];
+    // S^T = K q^T of the current step; accumulator register r of block kb:
+    // key k0 + 16*kb + 4*grp + r, query column l16 of head block nb
+    f32x4 sc[NB][2];
+    bool pv_pending = false;
+    int pend_k0 = 0;
+    uint32_t pend_kw = ~0u;
+    // hide keys outside [lo, n) (and padding), fold the step into the running
+    // (m, l, o) and leave P^T in pf
+    auto softmax = [&](int k0, uint32_t kw) {
+      if (k0 + STEP > n || k0 < lo || (KM && kw != ~0u)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + kb * 16 + grp * 4 + r;
+            bool hide = key >= n || key < lo;
+            if (KM) hide = hide || !((kw >> (kb * 16 + grp * 4 + r)) & 1);
+            if (hide) {
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) sc[nb][kb][r] = -INFINITY;
+            }
+          }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 (&t)[2] = sc[nb];
+        float mx = fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
+                         fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // every step run holds a visible key unless a key-padding mask hides it
+        const float m_cand = mx * p.c;
+        if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + TAU)) {
+          const float m_new = fmaxf(m_run[nb], m_cand);
+          const float alpha = exp2_fast(m_run[nb] - m_new);
+          m_run[nb] = m_new;
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
+        }
+        const float m_use = (KM && m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = exp2_fast(__builtin_fmaf(t[kb][r], p.c, -m_use));
+            t[kb][r] = e;
+            rs += e;
+          }
+        l_run[nb] += rs;
+        u32x4 pk;
+        pk[0] = pack_bf16x2(t[0][0], t[0][1]);
+        pk[1] = pack_bf16x2(t[0][2], t[0][3]);
+        pk[2] = pack_bf16x2(t[1][0], t[1][1]);
+        pk[3] = pack_bf16x2(t[1][2], t[1][3]);
+        pf[nb] = __builtin_bit_cast(bf16x8, pk);
+      }
+    };
+    auto finish_pv = [&]() {
+      if constexpr (EARLY_V) {
+        if (pv_pending) {
+          softmax(pend_k0, pend_kw);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pf[nb], o[nb][db], 0, 0, 0);
+          pv_pending = false;
+        }
+      }
+    };
+    auto step = [&](int s, const lds_char* kst, const lds_char* vst) {
+      const int k0 = c0 + s * STEP;
+      // flags of keys k0 .. k0 + 31 (k0 is a multiple of 32); a step of padding
+      // keys only changes nothing
+      uint32_t kw = ~0u;
+      if constexpr (KM) {
+        kw = __builtin_amdgcn_readlane(kw_lane, s - s_flags);
+        if (kw == 0) return;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sc[nb][kb] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *(lds_bf16x8*)(kst + kb * 16 * geo::RB + koff[ks]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            sc[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], sc[nb][kb], 0, 0, 0);
+        }
+      }
+      auto read_v = [&](int db) {
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vst + voff[0][db]));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vst + voff[1][db]));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      if constexpr (EARLY_V) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[db] = read_v(db);
+        pend_k0 = k0;
+        pend_kw = kw;
+        pv_pending = true;  // softmax and products run in finish_pv()
+      } else {
+        softmax(k0, kw);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = read_v(db);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
+        }
+      }
+    };
+
+    // Steps in pairs from s0: the first of a pair uses stage 0, the second stage
+    // 1.  Before step s the copies of steps s and s + 1 are outstanding; once
+    // step s has read its stage, the copies of step s + 2 go into it.
+    // APP: after step s's copies have landed, put the new row into its stage.
+    // When the new row is the chunk's last row, the stage rows after it were
+    // copied from that same cache row (copies clamp to `last`), i.e. from the
+    // bytes workgroup 0 is overwriting: they get the new row too.  Their
+    // weights are 0, but 0 times a stale NaN or Inf would still be NaN.
+    auto substitute = [&](int s, lds_char* kst, lds_char* vst) {
+      if constexpr (APP) {
+        const int r = alt_row - (c0 + s * STEP);
+        const int l = lane;
+        if (r >= 0 && r < STEP && l < 2 * NCH) {  // r is wave-uniform
+          const bool isk = l < NCH;
+          const int c = isk ? l : l - NCH;
+          const int r_end = alt_row == last ? STEP : r + 1;
+          typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+          for (int rr = r; rr < r_end; ++rr) {
+            const int off = (rr / geo::RP) * 1024 +
+                            ((rr % geo::RP) * NCH + (c ^ (isk ? kswz<D>(rr) : vswz<D>(rr)))) * 16;
+            *(lds_u32x4*)((isk ? kst : vst) + off) = new_row;
+          }
+        }
+        // the step's operand reads use other pointer types: keep them after the store
+        __asm__ __volatile__("" ::: "memory");
+      }
+    };
+
+    // The loop starts with the copies of step s + 2, not with a read of stage
+    // 0: entered at such a read, the loop merges the states of its entry and
+    // its back edge there, and the compiler can no longer tell which copies may
+    // still target stage 0; it then drains every copy in flight.
+    if (s0 < nsteps) {
+      wait_vm<PER_STEP>();
+      substitute(s0, K0, V0);
+      step(s0, K0, V0);
+      for (int s = s0;; s += 2) {
+        wait_lds_reads();  // step s has read stage 0
+        load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
+        load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
+        finish_pv();
+        wait_vm<PER_STEP>();
+        if (s + 1 >= nsteps) break;
+        substitute(s + 1, K1, V1);
+        step(s + 1, K1, V1);
+        wait_lds_reads();  // step s + 1 has read stage 1
+        load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
+        load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
+        finish_pv();
+        wait_vm<PER_STEP>();
+        if (s + 2 >= nsteps) break;
+        substitute(s + 2, K0, V0);
+        step(s + 2, K0, V0);
+      }
+    }
+    wait_vm<0>();  // no copy may still target LDS when the wave ends
+    write_new_row();
+
+    // partial of this chunk: O^T register r of block db is d = 16*db + 4*grp + r
+    // of query column l16
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float l_tot = l_run[nb];
+      l_tot += __shfl_xor(l_tot, 16, 64);
+      l_tot += __shfl_xor(l_tot, 32, 64);
+      const int hh = 16 * nb + l16;
+      if (hh < G) {
+        const size_t part = slot * G + hh;
+        float* dst = p.ws_o + part * D + 4 * grp;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[nb][db];
+        if (grp == 0) {
+          p.ws_ml[part * 2 + 0] = m_run[nb];
+          p.ws_ml[part * 2 + 1] = l_tot;
+        }
+      }
+    }
+    if constexpr (!EV) {
+      break;
     } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 a = read_v(db);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb], o[nb][db], 0, 0, 0);
+      if (ev_a >= ev_e) break;
+      // next segment: the next K/V head, else the next sequence with steps
+      if (++g == p.Nkv) {
+        g = 0;
+        b = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane > b && tab.ns > 0));
       }
+      enter(0);
     }
-  };
-
-  // Steps in pairs from s0: the first of a pair uses stage 0, the second stage
-  // 1.  Before step s the copies of steps s and s + 1 are outstanding; once
-  // step s has read its stage, the copies of step s + 2 go into it.
-  // APP: after step s's copies have landed, put the new row into its stage.
-  // When the new row is the chunk's last row, the stage rows after it were
-  // copied from that same cache row (copies clamp to `last`), i.e. from the
-  // bytes workgroup 0 is overwriting: they get the new row too.  Their
-  // weights are 0, but 0 times a stale NaN or Inf would still be NaN.
-  auto substitute = [&](int s, lds_char* kst, lds_char* vst) {
-    if constexpr (APP) {
-      const int r = alt_row - (c0 + s * STEP);
-      const int l = threadIdx.x;
-      if (r >= 0 && r < STEP && l < 2 * NCH) {  // r is wave-uniform
-        const bool isk = l < NCH;
-        const int c = isk ? l : l - NCH;
-        const int r_end = alt_row == last ? STEP : r + 1;
-        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-        for (int rr = r; rr < r_end; ++rr) {
-          const int off = (rr / geo::RP) * 1024 +
-                          ((rr % geo::RP) * NCH + (c ^ (isk ? kswz<D>(rr) : vswz<D>(rr)))) * 16;
-          *(lds_u32x4*)((isk ? kst : vst) + off) = new_row;
-        }
-      }
-      // the step's operand reads use other pointer types: keep them after the store
-      __asm__ __volatile__("" ::: "memory");
-    }
-  };
-
-  // The loop starts with the copies of step s + 2, not with a read of stage
-  // 0: entered at such a read, the loop merges the states of its entry and
-  // its back edge there, and the compiler can no longer tell which copies may
-  // still target stage 0; it then drains every copy in flight.
-  if (s0 < nsteps) {
-    wait_vm<PER_STEP>();
-    substitute(s0, K0, V0);
-    step(s0, K0, V0);
-    for (int s = s0;; s += 2) {
-      wait_lds_reads();  // step s has read stage 0
-      load_rows<D, true>(Kh, c0 + (s + 2) * STEP, last, K0, lane);
-      load_rows<D, false>(Vh, c0 + (s + 2) * STEP, last, V0, lane);
-      finish_pv();
-      wait_vm<PER_STEP>();
-      if (s + 1 >= nsteps) break;
-      substitute(s + 1, K1, V1);
-      step(s + 1, K1, V1);
-      wait_lds_reads();  // step s + 1 has read stage 1
-      load_rows<D, true>(Kh, c0 + (s + 3) * STEP, last, K1, lane);
-      load_rows<D, false>(Vh, c0 + (s + 3) * STEP, last, V1, lane);
-      finish_pv();
-      wait_vm<PER_STEP>();
-      if (s + 2 >= nsteps) break;
-      substitute(s + 2, K0, V0);
-      step(s + 2, K0, V0);
-    }
-  }
-  wait_vm<0>();  // no copy may still target LDS when the wave ends
-  write_new_row();
-
-  // partial of this chunk: O^T register r of block db is d = 16*db + 4*grp + r
-  // of query column l16
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l_tot = l_run[nb];
-    l_tot += __shfl_xor(l_tot, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    const int hh = 16 * nb + l16;
-    if (hh < G) {
-      const size_t part = (((size_t)b * p.Nkv + g) * p.n_slots + blockIdx.x) * G + hh;
-      float* dst = p.ws_o + part * D + 4 * grp;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[nb][db];
-      if (grp == 0) {
-        p.ws_ml[part * 2 + 0] = m_run[nb];
-        p.ws_ml[part * 2 + 1] = l_tot;
-      }
-    }
-  }
+  }  // segments
 }
 
 // Merge the chunk partials of one (sequence, query head) row: slot x holds a
@@ -559,7 +698,11 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
 // from LDS, in wavefront order.  The kernel is latency-bound (a row's partials
 // are a few KB): a wavefront requests eight partial outputs at a time, the
 // first eight together with their (m, l), before the weights are known.
-template <int D, bool KM>
+//
+// EV: the partials of the even split; segment (b, g) holds the pieces of the
+// wavefronts whose ranges meet its steps, wavefront w's piece at slot
+// b*Nkv + g + w.
+template <int D, bool KM, bool EV = false>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
   constexpr int PL = D / 64;  // head-dims per lane
   typedef float fvec __attribute__((ext_vector_type(PL)));
@@ -577,12 +720,26 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
   if (valid) {
     const int b = row / p.Nq;
     const int h = row % p.Nq;
-    const int n = min(p.lens[b], p.Tcap);
-    const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
-    // partial slot x holds chunk c_lo + x; chunks c_lo .. nc-1 wrote one
-    const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
-    ns = max(0, nc - c_lo);
-    part0 = ((size_t)b * p.Nkv + h / G) * p.n_slots * G + h % G;  // slot x: part0 + x*G
+    if constexpr (EV) {
+      const EvenTable t = even_table(p, lane);
+      const int ns_b = __builtin_amdgcn_readlane(t.ns, b);
+      if (ns_b > 0) {
+        // wavefront holding global step x: the last w with w*tot/nwe <= x
+        const long long first = (long long)(__builtin_amdgcn_readlane(t.incl, b) - ns_b) * p.Nkv +
+                                (long long)(h / G) * ns_b;
+        const int wf = (int)(((first + 1) * t.nwe - 1) / t.tot);
+        const int wl = (int)(((first + ns_b) * t.nwe - 1) / t.tot);
+        ns = wl - wf + 1;
+        part0 = ((size_t)b * p.Nkv + h / G + wf) * G + h % G;  // slot x: part0 + x*G
+      }
+    } else {
+      const int n = min(p.lens[b], p.Tcap);
+      const int nc = n > 0 ? (n + p.ch - 1) / p.ch : 0;
+      // partial slot x holds chunk c_lo + x; chunks c_lo .. nc-1 wrote one
+      const int c_lo = p.window > 0 ? max(0, n - p.window) / p.ch : 0;
+      ns = max(0, nc - c_lo);
+      part0 = ((size_t)b * p.Nkv + h / G) * p.n_slots * G + h % G;  // slot x: part0 + x*G
+    }
   }
   const int x0 = part * ns / mw, x1 = (part + 1) * ns / mw;  // this wavefront's slots
 
@@ -683,7 +840,7 @@ int decode_bf16_chunk(int B, int Nkv, int L, int G) {
   // chunks of a few steps, whose partials cost more to write and merge than
   // the extra items gain (one sequence of 32768 tokens: 60 us at 96-key
   // chunks, 30 us at 640)
-  const int floor_ch = G >= 16 ? 224 : 640;
+  const int floor_ch = G >= 16 ? kFloorKeysWide : kFloorKeys;
   const long long heads = (long long)B * Nkv;
   for (int ch : kChunks)
     if (ch <= floor_ch || heads * ((L + ch - 1) / ch) >= min_items) return ch;
@@ -695,50 +852,82 @@ namespace {
 // partial slots one merge wavefront folds at most (one or two rounds of eight
 // requests; 6, 12 and 24 measured within 1 % of each other)
 constexpr int kMergeSlots = 12;
-// chunk length and partial slots per (sequence, K/V head)
+// merge: enough wavefronts per row that each folds at most kMergeSlots slots
+// (one or two rounds of eight requests)
+int merge_waves(long long slots) {
+  int mw = 1;
+  while (mw < 16 && (slots + mw - 1) / mw > kMergeSlots) mw *= 2;
+  return mw;
+}
+// chunk length and partial slots per (sequence, K/V head); whether the even
+// split may serve the shape (without a key-padding mask or an append), its
+// merge wavefronts per row, and the workspace slots (G rows each) both need
 struct DecodePlan {
   int ch, n_slots, mw;
+  bool ev;
+  int ev_mw;
+  long long slots;
 };
-DecodePlan decode_plan(int B, int Nq, int Nkv, int Tcap, int window) {
+DecodePlan decode_plan(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
   const int L = (window > 0 && window < Tcap) ? window : Tcap;
   DecodePlan d;
   d.ch = decode_bf16_chunk(B, Nkv, L, Nq / Nkv);
   const int all = (Tcap + d.ch - 1) / d.ch;
   // a window of L keys starting anywhere touches at most ceil(L / ch) + 1 chunks
   d.n_slots = L < Tcap ? std::min(all, (L + d.ch - 1) / d.ch + 1) : all;
-  // merge: enough wavefronts per row that each folds at most kMergeSlots
-  // slots (one or two rounds of eight requests)
-  d.mw = 1;
-  while (d.mw < 16 && (d.n_slots + d.mw - 1) / d.mw > kMergeSlots) d.mw *= 2;
+  d.mw = merge_waves(d.n_slots);
+  d.slots = (long long)B * Nkv * d.n_slots;
+  // the even split takes up to 64 sequences (one lane each in its table) and
+  // grids of at least kEvenWaves / 2 chunk items: below that every chunk runs
+  // at once anyway, and the table each wavefront builds first (a dependent
+  // load of the lengths before its first copy) costs more than the balance
+  // gains (one sequence of 32768 keys, 8 K/V heads: 31 us against 28).  Head
+  // size 256 keeps chunk mode (the segment loop spills its registers).
+  d.ev = Dh <= 128 && B <= 64 && d.slots >= kEvenWaves / 2;
+  // the even split's merge folds runs of about as many pieces as the chunk
+  // mode's (a row's share of the grid is the same); longer runs just loop
+  d.ev_mw = d.mw;
+  if (d.ev) d.slots = std::max(d.slots, (long long)B * Nkv + kEvenWaves);
   return d;
 }
 
-template <int D, int NB, bool KM, bool APP = false, bool RQ = false>
+template <int D, int NB, bool KM, bool APP = false, bool RQ = false, bool EV = false>
 hipError_t launch_decode_km(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM, APP, RQ>), dim3(p.n_slots, p.Nkv, p.B),
-                     dim3(64), 0, stream, p);
+  const dim3 grid = EV ? dim3(p.ev_nw) : dim3(p.n_slots, p.Nkv, p.B);
+  hipLaunchKernelGGL((decode_partial_kernel<D, NB, KM, APP, RQ, EV>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Nq;
   const int wpb = p.mw < 4 ? 4 : p.mw;  // wavefronts per block
   const int rpb = wpb / p.mw;           // rows per block
-  hipLaunchKernelGGL((decode_merge_kernel<D, KM>), dim3((rows + rpb - 1) / rpb), dim3(64 * wpb), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D, KM, EV>), dim3((rows + rpb - 1) / rpb), dim3(64 * wpb),
+                     0, stream, p);
   return hipGetLastError();
 }
 template <int D, int NB>
 hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
-  if (p.knew) return launch_decode_km<D, NB, false, true>(p, stream);  // append (no key mask)
-  if (p.rope.table)
-    return p.kbits ? launch_decode_km<D, NB, true, false, true>(p, stream)
-                   : launch_decode_km<D, NB, false, false, true>(p, stream);
-  return p.kbits ? launch_decode_km<D, NB, true>(p, stream) : launch_decode_km<D, NB, false>(p, stream);
+  if (p.knew) {  // append (no key mask)
+    if constexpr (D <= 128) {
+      if (p.ev_nw) return launch_decode_km<D, NB, false, true, false, true>(p, stream);
+    }
+    return launch_decode_km<D, NB, false, true>(p, stream);
+  }
+  if (p.kbits)
+    return p.rope.table ? launch_decode_km<D, NB, true, false, true>(p, stream)
+                        : launch_decode_km<D, NB, true>(p, stream);
+  if constexpr (D <= 128) {
+    if (p.ev_nw)
+      return p.rope.table ? launch_decode_km<D, NB, false, false, true, true>(p, stream)
+                          : launch_decode_km<D, NB, false, false, false, true>(p, stream);
+  }
+  return p.rope.table ? launch_decode_km<D, NB, false, false, true>(p, stream)
+                      : launch_decode_km<D, NB, false>(p, stream);
 }
 }  // namespace
 
 size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
-  const DecodePlan d = decode_plan(B, Nq, Nkv, Tcap, window);
-  const size_t parts = (size_t)B * Nq * d.n_slots;  // B * Nkv * n_slots * G
+  const DecodePlan d = decode_plan(B, Nq, Nkv, Dh, Tcap, window);
+  const size_t parts = (size_t)d.slots * (Nq / Nkv);
   return parts * Dh * sizeof(float) + parts * 2 * sizeof(float);
 }
 
@@ -747,7 +936,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
                               int window, float scale, const uint64_t* kbits, void* ws,
                               hipStream_t stream, const void* knew, const void* vnew,
                               const int32_t* slot, const RopeQ* rope) {
-  const DecodePlan d = decode_plan(B, Nq, Nkv, Tcap, window);
+  const DecodePlan d = decode_plan(B, Nq, Nkv, Dh, Tcap, window);
   DecParams p;
   p.knew = static_cast<const __bf16*>(knew);
   p.vnew = static_cast<const __bf16*>(vnew);
@@ -769,8 +958,11 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   p.Tcap = Tcap;
   p.ch = d.ch;
   p.n_slots = d.n_slots;
-  p.mw = d.mw;
-  const size_t parts = (size_t)B * Nq * p.n_slots;
+  const bool ev = d.ev && kbits == nullptr;
+  p.ev_nw = ev ? kEvenWaves : 0;
+  p.ev_min = (p.G >= 16 ? kFloorKeysWide : kFloorKeys) / STEP;
+  p.mw = ev ? d.ev_mw : d.mw;
+  const size_t parts = (size_t)d.slots * (Nq / Nkv);
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * Dh;
   p.window = window;
