@@ -459,11 +459,12 @@ def _head_sizes(torch, dev, tch, steps, warmup):
 
 def _backward(torch, dev, tch, steps, warmup):
     """One JSON line per shape: attn_backward (dQ, dK, dV from O, LSE and dO) on the prefill
-    workload and on GQA / head-size-64 variants.  Algorithmic FLOPs are 2.5 times the
+    workload and on GQA / head-size-64 / head-size-256 variants (the last at the 16384-token
+    shape of the head-size-256 prefill line).  Algorithmic FLOPs are 2.5 times the
     forward's: five products per visible pair (S = Q K^T, dP = dO V^T, dV, dK, dQ); the
     kernels recompute S and dP once more (seven products), which is not counted."""
     for B, Nq, Nkv, S, Dh in ((1, 32, 32, 32768, 128), (1, 32, 8, 32768, 128),
-                              (1, 32, 32, 32768, 64)):
+                              (1, 32, 32, 32768, 64), (1, 32, 32, 16384, 256)):
         q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=0)
         tq, tk, tv = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v))
         del q, k, v

@@ -65,7 +65,11 @@ def _inputs(B, Nq, Nkv, S, Dh, dtype, seed):
     (1, 4, 4, 700, 128, True, 100),     # window
     (1, 4, 2, 130, 128, False, 0),      # non-causal
     (2, 4, 1, 257, 64, True, 0),
-    (1, 2, 2, 200, 256, True, 30),
+    (1, 2, 2, 200, 256, True, 30),      # head size 256 (MFMA): window
+    (2, 2, 2, 65, 256, True, 0),
+    (1, 4, 4, 300, 256, True, 0),       # ragged, several key blocks
+    (1, 8, 2, 257, 256, True, 0),       # GQA 4
+    (1, 4, 1, 129, 256, False, 0),      # MQA, non-causal
 ])
 def test_backward_bf16(B, Nq, Nkv, S, Dh, causal, window):
     q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, "bf16", seed=S + Dh)
@@ -97,7 +101,7 @@ def test_backward_deterministic():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("Nkv,Dh", [(32, 128), (8, 128), (32, 64)])
+@pytest.mark.parametrize("Nkv,Dh", [(32, 128), (8, 128), (32, 64), (8, 256)])
 def test_backward_repeat_bitwise_long(Nkv, Dh):
     # dK / dV at head size 128 pass the weights from one wavefront to another
     # through LDS; three calls on an 8192-token causal input give the same bits
@@ -174,3 +178,34 @@ def test_backward_full_size_sampled_rows(Nkv):
         assert np.all(ratio <= BF16_REL), f"{name}: worst row-relative error {ratio.max():.3g}"
         out.append(f"{name} {ratio.max():.2e}")
     say(f"backward full size Nkv={Nkv}, row-relative: " + " ".join(out))
+
+
+@pytest.mark.timeout(300)
+def test_backward_head256_sampled_rows():
+    # head size 256 on the MFMA kernels at a long shape (16384-token causal
+    # GQA 32/8, the head-size-256 prefill shape of the benchmark): seeded dQ
+    # rows plus rows 0 and S-1, and dK / dV rows of keys in the last tile,
+    # against the oracle's row form, held as in the 32768-token test above
+    B, Nq, Nkv, S, Dh = 1, 32, 8, 16384, 256
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=2)
+    dO = workloads.draw((B, Nq, S, Dh), "bf16", 2, 3)
+    dev = device()
+    tq, tk, tv, tdo = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v, dO))
+    O, L = tch.prefill(tq, tk, tv)
+    dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo)
+    torch.cuda.synchronize()
+    qr = workloads.sample_rows(B, Nq, S, 10, seed=7, forced_rows=(0, S - 1))
+    kr = [(0, 0, S - 1), (0, Nkv // 2, S - 33), (0, Nkv - 1, S - 64)]
+    idx = lambda rows: tuple(torch.tensor(c, device=dev) for c in zip(*rows))
+    got = [workloads.to_f64(workloads.from_torch(t[idx(r)], "bf16"), "bf16")
+           for t, r in ((dQ, qr), (dK, kr), (dV, kr))]
+    del tq, tk, tv, tdo, O, L, dQ, dK, dV
+    ref = oracle.backward_rows_ref(_Lazy(q), _Lazy(k), _Lazy(v), _Lazy(dO), qr, kr)
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        scale_row = np.maximum(np.abs(r).max(axis=1, keepdims=True), 1e-2 * np.abs(r).max())
+        ratio = np.abs(g - r) / scale_row
+        assert np.all(np.isfinite(g)), name
+        assert np.all(ratio <= BF16_REL), f"{name}: worst row-relative error {ratio.max():.3g}"
+        out.append(f"{name} {ratio.max():.2e}")
+    say("backward head size 256, row-relative: " + " ".join(out))

@@ -1,6 +1,5 @@
-// Backward pass of prefill attention on bf16 MFMA (head size 64 or 128; at
-// 256 the K and V fragments plus both accumulators of the dK/dV kernel exceed
-// the register file, and that size takes the general kernels).  Same mathematics as the general row kernels in backward.hip (the
+// Backward pass of prefill attention on bf16 MFMA (head size 64, 128 or 256).
+// Same mathematics as the general row kernels in backward.hip (the
 // weights recomputed from the stored LSE, the softmax Jacobian p (delta - p)
 // of the textbook's "Почему делить на корень из d_h"), split into two kernels
 // so that every gradient has a single owner and no float atomics are needed
@@ -12,8 +11,10 @@
 //                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
 //                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
 //                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
-//   dkv_kernel -- (head size 64; head size 128 uses dkv_pipe_kernel below,
-//                 which puts dV and dK on different wavefronts)
+//   dkv_kernel -- (head sizes 64 and 256; head size 128 uses dkv_pipe_kernel
+//                 below, which puts dV and dK on different wavefronts; at 256
+//                 one wavefront per SIMD holds the K and V fragments and both
+//                 accumulators, 512 registers with a few spilled)
 //                 one wavefront per 32 keys of one K/V head, streaming the Q and
 //                 dO tiles of every query head of its group over the queries
 //                 that see those keys:
@@ -347,17 +348,6 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
       }
       // register r: query q0 + 32*mb + 8*(r/4) + 4*hl + r%4, key kw0 + ln;
       // the LSE and Delta of those rows are 4 consecutive floats per r/4
-      float lse2[16], dlt[16];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(At + mb * 32 + a * 8 + hl * 4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + a * 8 + hl * 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          lse2[a * 4 + u] = l4[u] * kLog2e;
-          dlt[a * 4 + u] = d4[u];
-        }
-      }
       if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -369,13 +359,21 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 pp, ss;
+        f32x4 l4[2], d4[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          l4[a] = *reinterpret_cast<const f32x4*>(At + mb * 32 + (2 * kk + a) * 8 + hl * 4);
+          d4[a] = *reinterpret_cast<const f32x4*>(At + BN + mb * 32 + (2 * kk + a) * 8 + hl * 4);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r0 = kk * 8 + 2 * j;
-          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2[r0]));
-          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2[r0 + 1]));
+          const f32x4 lv = l4[j >> 1], dv4 = d4[j >> 1];
+          const int u = (2 * j) & 3;
+          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lv[u] * kLog2e));
+          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lv[u + 1] * kLog2e));
           pp[j] = pack_bf16x2(p0, p1);
-          ss[j] = pack_bf16x2(p0 * (dp[r0] - dlt[r0]), p1 * (dp[r0 + 1] - dlt[r0 + 1]));
+          ss[j] = pack_bf16x2(p0 * (dp[r0] - dv4[u]), p1 * (dp[r0 + 1] - dv4[u + 1]));
         }
         pf[kk] = __builtin_bit_cast(bf16x8, pp);
         sf[kk] = __builtin_bit_cast(bf16x8, ss);
@@ -703,7 +701,7 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
 
 template <int D>
 hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
-  constexpr int NWQ = 8;  // dQ waves per workgroup
+  constexpr int NWQ = D == 256 ? 4 : 8;  // dQ waves per workgroup (256: 404 registers, one per SIMD)
   constexpr int NWK = 4;                 // dK/dV waves per workgroup (one per SIMD)
   if ((long long)p.S * D * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
   p.hp = (p.G % 4 == 0 && NWQ % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
@@ -730,7 +728,7 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
 
 }  // namespace
 
-bool backward_bf16_supported(int Dh) { return Dh == 64 || Dh == 128; }
+bool backward_bf16_supported(int Dh) { return Dh == 64 || Dh == 128 || Dh == 256; }
 
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
@@ -761,6 +759,7 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
   switch (Dh) {
     case 64: return launch_bwd<64>(p, stream);
     case 128: return launch_bwd<128>(p, stream);
+    case 256: return launch_bwd<256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

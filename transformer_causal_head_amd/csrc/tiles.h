@@ -95,9 +95,12 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // the A (or B) operand of a 32x32x16 product over the head dimension.
 template <int D>
 __device__ __forceinline__ void row_operand_offsets(int ln, int hl, int (&off)[Geo<D>::KS]) {
+  // the swizzle changes chunk bits 0..3 only: in 512-byte rows the upper 16
+  // chunks sit at the lower 16's offsets + 256 (a constant the reads fold in)
+  constexpr int H = D == 256 ? Geo<D>::KS / 2 : Geo<D>::KS;
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::KS; ++ks)
-    off[ks] = ln * Geo<D>::RB + (((2 * ks + hl) ^ swz<D>(ln)) << 4);
+    off[ks] = ks < H ? ln * Geo<D>::RB + (((2 * ks + hl) ^ swz<D>(ln)) << 4) : off[ks - H] + 256;
 }
 // Transposed operand: two ds_read_b64_tr_b16 per 32-wide block db give the A
 // operand of a product whose k index runs along the tile's rows (16 rows per
@@ -107,12 +110,15 @@ template <int D>
 __device__ __forceinline__ void tr_operand_offsets(int lane, int (&off)[2][Geo<D>::DB]) {
   const int gq = lane >> 4, j = lane & 15;
   const int h = gq >> 1, dpart = gq & 1, ip = j >> 2, u = j & 3;
+  constexpr int H = D == 256 ? Geo<D>::DB / 2 : Geo<D>::DB;  // as in row_operand_offsets
 #pragma unroll
   for (int ih = 0; ih < 2; ++ih) {
     const int r = 8 * ih + 4 * h + ip;
 #pragma unroll
     for (int db = 0; db < Geo<D>::DB; ++db)
-      off[ih][db] = r * Geo<D>::RB + (((4 * db + 2 * dpart + (u >> 1)) ^ swz<D>(r)) << 4) + (u & 1) * 8;
+      off[ih][db] = db < H ? r * Geo<D>::RB + (((4 * db + 2 * dpart + (u >> 1)) ^ swz<D>(r)) << 4) +
+                                 (u & 1) * 8
+                           : off[ih][db - H] + 256;
   }
 }
 // one transposed A operand (32 head dims of block db x 16 rows of slice kk)
