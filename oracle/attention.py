@@ -332,7 +332,7 @@ def softmax_vjp(P, dP):
     return P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
 
 
-def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
+def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None, key_mask=None):
     """Gradients of the prefill attention output with respect to Q, K and V.
 
     Q: [B,Nq,S,Dh], K, V: [B,Nkv,S,Dh], dO = dL/dO: [B,Nq,S,Dh].  Returns
@@ -345,7 +345,10 @@ def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
     contributions (textbook, "Как K/V-головы доходят до голов Q": the shared
     head is repeated, so its gradient is the sum over the repeats).  The
     weights are recomputed from the inputs here, as the textbook's
-    FlashAttention section says the backward pass does.
+    FlashAttention section says the backward pass does.  ``key_mask``:
+    optional [B, S] booleans, False for padding keys (the forward's mask, so
+    a hidden key has weight 0 and receives no gradient, and a query row that
+    sees no key has O = 0 and gradient 0).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -364,7 +367,8 @@ def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
         for h in range(Nq):
             g = kv_head_of(h, Nq, Nkv)
             _, _, P = head_attention(Q[b, h], rows, K[b, g], V[b, g], causal, window, scale,
-                                     return_probs=True)
+                                     return_probs=True,
+                                     key_ok=None if key_mask is None else key_mask[b])
             dV[b, g] += P.T @ dO[b, h]
             dP = dO[b, h] @ V[b, g].T
             dA = softmax_vjp(P, dP)
@@ -373,7 +377,8 @@ def backward_ref(Q, K, V, dO, causal=True, window=0, scale=None):
     return dQ, dK, dV
 
 
-def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0, scale=None):
+def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0, scale=None,
+                      key_mask=None):
     """Selected rows of the gradients of ``backward_ref``, for inputs too long
     for the full score matrices.
 
@@ -383,7 +388,8 @@ def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0,
     dP_i = V dO_i and dA_i = softmax_vjp(P_i, dP_i); dQ_i = scale * dA_i K,
     and key j collects P_ij dO_i into dV_j and scale * dA_ij Q_i into dK_j
     from every query row i of the group's heads that sees it.  Arrays may be
-    memory-mapped or lazily widened; only the rows used are read.
+    memory-mapped or lazily widened; only the rows used are read.  ``key_mask``
+    as in ``backward_ref``: a padding key is seen by no query row.
     Returns (dQ_rows [len(q_rows), Dh], dK_rows, dV_rows [len(kv_rows), Dh]).
     """
     B, Nq, S, Dh = Q.shape
@@ -403,7 +409,8 @@ def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0,
         if (b, h, i) not in rows:
             Kb, Vb = head_kv(b, kv_head_of(h, Nq, Nkv))
             q = np.asarray(Q[b, h, i], dtype=np.float64)[None, :]
-            _, _, P = head_attention(q, [i], Kb, Vb, causal, window, scale, return_probs=True)
+            _, _, P = head_attention(q, [i], Kb, Vb, causal, window, scale, return_probs=True,
+                                     key_ok=None if key_mask is None else key_mask[b])
             dP = np.asarray(dO[b, h, i], dtype=np.float64)[None, :] @ Vb.T
             rows[(b, h, i)] = (P[0], softmax_vjp(P, dP)[0])
         return rows[(b, h, i)]
@@ -422,6 +429,8 @@ def backward_rows_ref(Q, K, V, dO, q_rows=(), kv_rows=(), causal=True, window=0,
             seen &= j <= i_all
         if window > 0:
             seen &= (i_all - j) < window
+        if key_mask is not None and not key_mask[b][j]:
+            seen[:] = False
         for h in range(g * group, (g + 1) * group):
             for i in np.flatnonzero(seen):
                 P, dA = row_grads(b, h, int(i))

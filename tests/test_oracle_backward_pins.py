@@ -149,3 +149,88 @@ def test_backward_rows_equal_full_backward(causal, window):
     np.testing.assert_allclose(rq, [dQ[t] for t in qr], atol=1e-13)
     np.testing.assert_allclose(rk, [dK[t] for t in kr], atol=1e-13)
     np.testing.assert_allclose(rv, [dV[t] for t in kr], atol=1e-13)
+
+
+def _loss_masked(Q, K, V, dO, key_mask, window, scale):
+    O, _ = attention_ref(Q, K, V, causal=True, window=window, scale=scale, key_mask=key_mask)
+    return float(np.sum(O * dO))
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window", [
+    (2, 2, 1, 6, 3, 0),
+    (2, 4, 2, 5, 2, 3),
+])
+def test_backward_with_key_mask_matches_finite_differences(B, Nq, Nkv, S, Dh, window):
+    # textbook, "Паддинг": the padding mask joins the causal mask and the window.
+    # Row 0 is left-padded by two tokens, so its first two queries see no key at
+    # all (O = 0 there, and no gradient flows through them); row 1 has a padding
+    # key in the middle.
+    key_mask = np.ones((B, S), dtype=bool)
+    key_mask[0, :2] = False
+    key_mask[1, 2] = False
+    Q, K, V = _rand((B, Nq, S, Dh), 31), _rand((B, Nkv, S, Dh), 32), _rand((B, Nkv, S, Dh), 33)
+    dO = _rand((B, Nq, S, Dh), 34)
+    scale = 0.7
+    dQ, dK, dV = backward_ref(Q, K, V, dO, causal=True, window=window, scale=scale,
+                              key_mask=key_mask)
+    h = 1e-6
+    for X, dX in ((Q, dQ), (K, dK), (V, dV)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            keep = X[idx]
+            X[idx] = keep + h
+            lp = _loss_masked(Q, K, V, dO, key_mask, window, scale)
+            X[idx] = keep - h
+            lm = _loss_masked(Q, K, V, dO, key_mask, window, scale)
+            X[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(dX, num, rtol=1e-6, atol=1e-8)
+    # padding keys receive nothing; queries that see no key pass nothing
+    assert np.all(dK[0, :, :2] == 0) and np.all(dV[0, :, :2] == 0)
+    assert np.all(dK[1, :, 2] == 0) and np.all(dV[1, :, 2] == 0)
+    assert np.all(dQ[0, :, :2] == 0)
+
+
+def test_backward_with_key_mask_matches_torch_autograd():
+    # an independent library routine: torch's float64 autograd through
+    # scaled_dot_product_attention with the causal and padding masks combined
+    # (every query sees at least one key, where the library's result is defined)
+    import torch.nn.functional as F
+    B, Nq, Nkv, S, Dh = 2, 4, 2, 9, 8
+    key_mask = np.ones((B, S), dtype=bool)
+    key_mask[0, 3:5] = False
+    key_mask[1, 7] = False
+    Q, K, V = _rand((B, Nq, S, Dh), 41), _rand((B, Nkv, S, Dh), 42), _rand((B, Nkv, S, Dh), 43)
+    dO = _rand((B, Nq, S, Dh), 44)
+    dQ, dK, dV = backward_ref(Q, K, V, dO, causal=True, key_mask=key_mask)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    ok = (j <= i)[None, None] & torch.tensor(key_mask)[:, None, None, :]
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=ok, enable_gqa=True)
+    out.backward(torch.tensor(dO))
+    np.testing.assert_allclose(dQ, tq.grad.numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dK, tk.grad.numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=0, atol=1e-10)
+
+
+def test_backward_all_true_key_mask_is_no_mask_and_rows_agree():
+    from oracle import backward_rows_ref
+    B, Nq, Nkv, S, Dh = 2, 4, 2, 9, 5
+    Q, K, V = _rand((B, Nq, S, Dh), 51), _rand((B, Nkv, S, Dh), 52), _rand((B, Nkv, S, Dh), 53)
+    dO = _rand((B, Nq, S, Dh), 54)
+    ones = np.ones((B, S), dtype=bool)
+    a = backward_ref(Q, K, V, dO, window=4)
+    b = backward_ref(Q, K, V, dO, window=4, key_mask=ones)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    key_mask = ones.copy()
+    key_mask[0, :3] = False
+    key_mask[1, 5] = False
+    dQ, dK, dV = backward_ref(Q, K, V, dO, window=4, key_mask=key_mask)
+    qr = [(0, 0, 0), (0, 1, 2), (0, 3, 7), (1, 2, 5), (1, 0, 8)]
+    kr = [(0, 0, 1), (0, 1, 3), (1, 1, 5), (1, 0, 8)]
+    rq, rk, rv = backward_rows_ref(Q, K, V, dO, qr, kr, window=4, key_mask=key_mask)
+    np.testing.assert_allclose(rq, [dQ[t] for t in qr], atol=1e-13)
+    np.testing.assert_allclose(rk, [dK[t] for t in kr], atol=1e-13)
+    np.testing.assert_allclose(rv, [dV[t] for t in kr], atol=1e-13)
