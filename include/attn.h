@@ -230,7 +230,8 @@ int attn_kv_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcach
 
 /*
  * attn_backward_workspace_bytes -- bytes of device workspace attn_backward
- * needs (one fp32 per query row).  Pure host function; 0 for invalid arguments.
+ * and attn_backward_padded need (two fp32 per query row: dO . O and the LSE
+ * in log2 units).  Pure host function; 0 for invalid arguments.
  */
 size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int dtype);
 
@@ -252,8 +253,9 @@ size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int 
  *   workspace / workspace_bytes     device scratch of at least
  *                                   attn_backward_workspace_bytes(...) bytes
  * dQ, dK, dV are written in the element type of the inputs (accumulation in
- * fp32); they are overwritten, not accumulated into.  bf16 with Dh 64 or 128
- * runs the MFMA kernels, which need S * Dh * 2 < 2^31 (else ATTN_EUNSUPPORTED).
+ * fp32); they are overwritten, not accumulated into.  bf16 with Dh 64, 128 or
+ * 256 runs the MFMA kernels, which need S * Dh * 2 < 2^31 (else
+ * ATTN_EUNSUPPORTED).
  * Errors: ATTN_EINVAL, ATTN_EGQA, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP.
  */
 int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -261,6 +263,21 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int Nq, int Nkv, int S, int Dh,
                   int causal, int window, float scale,
                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * attn_backward_padded -- attn_backward for a forward pass that ran with a
+ * key-padding mask (attn_prefill_padded, textbook "Паддинг"): the same
+ * key_bits [B, ceil(S / 64)] uint64, DEVICE, bit j % 64 of word j / 64 set
+ * for a real key j.  A padding key has weight 0 in every row, so its dK and
+ * dV rows are 0; a query row that saw no key (LSE = -inf, O = 0) passes no
+ * gradient and gets dQ = 0.  key_bits == NULL is attn_backward.  Every other
+ * argument, the workspace and the errors are those of attn_backward.
+ */
+int attn_backward_padded(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                         const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
+                         void* dV, int B, int Nq, int Nkv, int S, int Dh, int causal,
+                         int window, float scale, void* workspace, size_t workspace_bytes,
+                         int dtype, void* stream);
 
 /*
  * attn_decode_append -- one decode step that also appends the new token's K

@@ -270,11 +270,16 @@ def test_kv_append_rejects(kw, code):
     assert _append(**kw) == code
 
 
-def _backward(**kw):
+def _backward(padded=False, **kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, LSE=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, B=1,
              Nq=4, Nkv=2, S=16, Dh=128, causal=1, window=0, scale=0.125, ws=FAKE,
              ws_bytes=1 << 20, dtype=tch.ATTN_BF16, stream=None)
     a.update(kw)
+    if padded:  # the padded form rejects exactly what the plain one does
+        return tch.lib().attn_backward_padded(
+            a["Q"], a["K"], a["V"], FAKE, a["O"], a["dO"], a["LSE"], a["dQ"], a["dK"], a["dV"],
+            a["B"], a["Nq"], a["Nkv"], a["S"], a["Dh"], a["causal"], a["window"], a["scale"],
+            a["ws"], a["ws_bytes"], a["dtype"], a["stream"])
     return tch.lib().attn_backward(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["LSE"], a["dQ"],
                                    a["dK"], a["dV"], a["B"], a["Nq"], a["Nkv"], a["S"], a["Dh"],
                                    a["causal"], a["window"], a["scale"], a["ws"], a["ws_bytes"],
@@ -295,12 +300,13 @@ def _backward(**kw):
     (dict(ws_bytes=4), tch.ATTN_EWORKSPACE),
     (dict(S=8388608), tch.ATTN_EUNSUPPORTED),
 ])
-def test_backward_rejects(kw, code):
-    assert _backward(**kw) == code
+@pytest.mark.parametrize("padded", [False, True])
+def test_backward_rejects(kw, code, padded):
+    assert _backward(padded=padded, **kw) == code
 
 
 def test_backward_workspace_query():
-    assert tch.attn_backward_workspace_bytes(2, 8, 2, 100, 128, tch.ATTN_BF16) == 2 * 8 * 100 * 4
+    assert tch.attn_backward_workspace_bytes(2, 8, 2, 100, 128, tch.ATTN_BF16) == 2 * 2 * 8 * 100 * 4
     assert tch.attn_backward_workspace_bytes(2, 8, 3, 100, 128, tch.ATTN_BF16) == 0
 
 

@@ -209,3 +209,63 @@ def test_backward_head256_sampled_rows():
         assert np.all(ratio <= BF16_REL), f"{name}: worst row-relative error {ratio.max():.3g}"
         out.append(f"{name} {ratio.max():.2e}")
     say("backward head size 256, row-relative: " + " ".join(out))
+
+
+def _key_mask(B, S, pattern, seed):
+    m = np.ones((B, S), dtype=bool)
+    if pattern == "left":       # left padding: the first queries of a row see no key
+        for b in range(B):
+            m[b, :min(S - 1, 3 + 17 * b)] = False
+    elif pattern == "mid":      # a run of padding inside the sequence
+        m[:, S // 3:S // 3 + 40] = False
+    elif pattern == "random":   # about 10 % of the keys hidden anywhere
+        m = np.random.default_rng(seed).random((B, S)) > 0.1
+    return m
+
+
+def _grads_padded(q, k, v, dO, dtype, mask, window):
+    dev = device()
+    tq, tk, tv, tdo = (workloads.to_torch(x, dtype, dev) for x in (q, k, v, dO))
+    tm = torch.from_numpy(mask).to(dev)
+    O, L = tch.prefill(tq, tk, tv, causal=True, window=window, key_mask=tm)
+    dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo, causal=True, window=window, key_mask=tm)
+    torch.cuda.synchronize()
+    return [workloads.to_f64(workloads.from_torch(t, dtype), dtype) for t in (dQ, dK, dV)]
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window,pattern,dtype", [
+    (2, 4, 2, 300, 128, 0, "left", "bf16"),     # queries that see no key: dQ = 0
+    (2, 4, 4, 257, 128, 0, "mid", "bf16"),      # whole 64-key tiles of padding
+    (1, 8, 2, 400, 128, 100, "random", "bf16"),
+    (2, 4, 1, 200, 64, 0, "random", "bf16"),
+    (1, 4, 4, 300, 256, 0, "left", "bf16"),
+    (1, 8, 2, 160, 256, 30, "mid", "bf16"),
+    (2, 4, 2, 90, 80, 0, "left", "bf16"),       # head size 80: row kernels
+    (1, 2, 1, 70, 64, 7, "random", "f32"),      # fp32: row kernels
+])
+def test_backward_padded(B, Nq, Nkv, S, Dh, window, pattern, dtype):
+    mask = _key_mask(B, S, pattern, seed=S)
+    q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, dtype, seed=S + Dh + 1)
+    got = _grads_padded(q, k, v, dO, dtype, mask, window)
+    ref = oracle.backward_ref(*(workloads.to_f64(x, dtype) for x in (q, k, v, dO)),
+                              causal=True, window=window, key_mask=mask)
+    _check(got, ref, dtype, ("padded", pattern, B, Nq, Nkv, S, Dh, window))
+    # exact zeros where the definition gives them: padding keys receive no
+    # gradient, queries that saw no key pass none
+    dQ, dK, dV = got
+    for b in range(B):
+        hidden = ~mask[b]
+        assert np.all(dK[b][:, hidden] == 0) and np.all(dV[b][:, hidden] == 0)
+        blind = np.flatnonzero(np.cumsum(mask[b]) == 0)  # causal: no real key at or before i
+        assert np.all(dQ[b][:, blind] == 0)
+
+
+@pytest.mark.parametrize("Dh", [64, 128, 256])
+def test_backward_all_true_mask_is_the_unpadded_backward(Dh):
+    # an all-true mask takes the same kernels and paths: identical bits
+    B, Nq, Nkv, S = 2, 8, 2, 333
+    q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, "bf16", seed=Dh + 9)
+    a = _grads(q, k, v, dO, "bf16", True, 0)
+    b = _grads_padded(q, k, v, dO, "bf16", np.ones((B, S), dtype=bool), 0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

@@ -19,6 +19,8 @@ Entry points (same names as the C ABI):
                        window=0, scale=None, stream=None)
     attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
                   workspace=None, stream=None)
+    attn_backward_padded(Q, K, V, key_bits, O, dO, LSE, dQ, dK, dV, causal=1, window=0,
+                         scale=None, workspace=None, stream=None)
     attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype)
     attn_pack_key_mask(mask, key_bits, stream=None)
     attn_prefill_padded(Q, K, V, key_bits, O, LSE, causal=1, window=0, scale=None, stream=None)
@@ -68,7 +70,8 @@ ATTN_F32 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_cache", "attn_decode", "attn_decode_window",
            "attn_decode_workspace_bytes", "attn_decode_window_workspace_bytes",
-           "attn_kv_append", "attn_decode_append", "attn_backward", "attn_backward_workspace_bytes",
+           "attn_kv_append", "attn_decode_append", "attn_backward", "attn_backward_padded",
+           "attn_backward_workspace_bytes",
            "attn_pack_key_mask", "attn_prefill_padded", "attn_prefill_cache_padded",
            "attn_decode_padded", "attn_rope_cos_sin", "attn_rope", "attn_kv_append_rope",
            "attn_decode_noalloc", "attn_prefill_rope", "attn_prefill_cache_rope",
@@ -120,6 +123,9 @@ def lib():
         L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                     i32, i32, f32, vp, ctypes.c_size_t, i32, vp]
         L.attn_backward.restype = i32
+        L.attn_backward_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                           i32, i32, i32, i32, f32, vp, ctypes.c_size_t, i32, vp]
+        L.attn_backward_padded.restype = i32
         L.attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                          i32, f32, vp, vp, ctypes.c_size_t, i32, vp]
         L.attn_decode_append.restype = i32
@@ -544,9 +550,7 @@ def attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype):
     return int(lib().attn_backward_workspace_bytes(B, Nq, Nkv, S, Dh, dtype))
 
 
-def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
-                  workspace=None, stream=None):
-    """Gradients of attn_prefill; shapes as attn_prefill, dQ like Q, dK/dV like K."""
+def _check_backward(Q, K, V, O, dO, LSE, dQ, dK, dV):
     B, Nq, S, Dh = Q.shape
     Nkv = K.shape[1]
     if tuple(K.shape) != (B, Nkv, S, Dh) or K.shape != V.shape:
@@ -560,6 +564,13 @@ def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=Non
     if LSE is None:
         raise ValueError("LSE is required")
     _check_lse(LSE, (B, Nq, S))
+    return B, Nq, Nkv, S, Dh
+
+
+def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=None,
+                  workspace=None, stream=None):
+    """Gradients of attn_prefill; shapes as attn_prefill, dQ like Q, dK/dV like K."""
+    B, Nq, Nkv, S, Dh = _check_backward(Q, K, V, O, dO, LSE, dQ, dK, dV)
     if scale is None:
         scale = 1.0 / math.sqrt(Dh)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -571,15 +582,38 @@ def attn_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, causal=1, window=0, scale=Non
         raise AttnError(st, "attn_backward")
 
 
-def backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None):
-    """Allocate dQ, dK, dV and the workspace with torch and run attn_backward."""
+def attn_backward_padded(Q, K, V, key_bits, O, dO, LSE, dQ, dK, dV, causal=1, window=0,
+                         scale=None, workspace=None, stream=None):
+    """attn_backward for a forward pass with a key-padding mask: key_bits int64
+    [B, ceil(S/64)] on the GPU, as attn_prefill_padded took."""
+    B, Nq, Nkv, S, Dh = _check_backward(Q, K, V, O, dO, LSE, dQ, dK, dV)
+    if key_bits is not None:
+        _check_bits(key_bits, B, S)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().attn_backward_padded(_ptr(Q), _ptr(K), _ptr(V), _ptr(key_bits), _ptr(O), _ptr(dO),
+                                    _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), B, Nq, Nkv, S, Dh,
+                                    int(causal), int(window), float(scale), _ptr(workspace),
+                                    ws_bytes, _dtype_code(Q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_backward_padded")
+
+
+def backward(q, k, v, O, LSE, dO, causal=True, window=0, scale=None, key_mask=None):
+    """Allocate dQ, dK, dV and the workspace with torch and run attn_backward (with a
+    key_mask, bool / uint8 [B, S], attn_backward_padded)."""
     import torch
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B, Nq, S, Dh = q.shape
     n = attn_backward_workspace_bytes(B, Nq, k.shape[1], S, Dh, _dtype_code(q))
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    attn_backward(q, k, v, O, dO, LSE, dQ, dK, dV, causal=int(causal), window=window, scale=scale,
-                  workspace=ws)
+    if key_mask is not None:
+        attn_backward_padded(q, k, v, pack_key_mask(key_mask), O, dO, LSE, dQ, dK, dV,
+                             causal=int(causal), window=window, scale=scale, workspace=ws)
+    else:
+        attn_backward(q, k, v, O, dO, LSE, dQ, dK, dV, causal=int(causal), window=window,
+                      scale=scale, workspace=ws)
     return dQ, dK, dV
 
 

@@ -325,10 +325,11 @@ size_t attn_backward_workspace_bytes(int B, int Nq, int Nkv, int S, int Dh, int 
   return attn::backward_workspace(B, Nq, S);
 }
 
-int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                  const float* LSE, void* dQ, void* dK, void* dV, int B, int Nq, int Nkv, int S,
-                  int Dh, int causal, int window, float scale, void* workspace,
-                  size_t workspace_bytes, int dtype, void* stream) {
+static int backward_impl(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                         const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
+                         void* dV, int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
+                         float scale, void* workspace, size_t workspace_bytes, int dtype,
+                         void* stream) {
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return ATTN_EINVAL;
   int st = validate_common(B, Nq, Nkv, Dh, dtype);
   if (st != ATTN_OK) return st;
@@ -344,10 +345,27 @@ int attn_backward(const void* Q, const void* K, const void* V, const void* O, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16 && attn::backward_bf16_supported(Dh))
     return from_hip(attn::launch_backward_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S, Dh,
-                                               causal, window, scale, workspace, s));
+                                               causal, window, scale, workspace, key_bits, s));
   return from_hip(attn::launch_backward_general(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S,
                                                 Dh, causal, window, scale, workspace,
-                                                dtype == ATTN_BF16, s));
+                                                dtype == ATTN_BF16, key_bits, s));
+}
+
+int attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* LSE, void* dQ, void* dK, void* dV, int B, int Nq, int Nkv, int S,
+                  int Dh, int causal, int window, float scale, void* workspace,
+                  size_t workspace_bytes, int dtype, void* stream) {
+  return backward_impl(Q, K, V, nullptr, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S, Dh, causal,
+                       window, scale, workspace, workspace_bytes, dtype, stream);
+}
+
+int attn_backward_padded(const void* Q, const void* K, const void* V, const uint64_t* key_bits,
+                         const void* O, const void* dO, const float* LSE, void* dQ, void* dK,
+                         void* dV, int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
+                         float scale, void* workspace, size_t workspace_bytes, int dtype,
+                         void* stream) {
+  return backward_impl(Q, K, V, key_bits, O, dO, LSE, dQ, dK, dV, B, Nq, Nkv, S, Dh, causal,
+                       window, scale, workspace, workspace_bytes, dtype, stream);
 }
 
 const char* attn_strerror(int status) {

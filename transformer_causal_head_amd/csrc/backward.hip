@@ -35,6 +35,9 @@ struct BwdParams {
   const void* dO;
   const float* LSE;
   float* delta;
+  float* lse2;    // delta pass output (may be null): LSE * log2(e), +inf where LSE = -inf
+  const uint64_t* kbits;  // key-padding mask (one bit per key, kwords words per sequence) or null
+  int kwords;
   void* dQ;
   void* dK;
   void* dV;
@@ -43,7 +46,11 @@ struct BwdParams {
   float scale;
 };
 
-// Delta_i = dO_i . O_i, one wavefront per (b, h, i) row.
+// Delta_i = dO_i . O_i, one wavefront per (b, h, i) row.  With p.lse2 it
+// also stores the row's LSE in log2 units for the MFMA kernels, with a row
+// that saw no key (LSE = -inf, possible under a key-padding mask) mapped to
+// +inf, so that the weights recomputed from it, 2^(s c - lse2), are 0 there
+// instead of 2^(+inf).
 template <typename T>
 __global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
@@ -54,7 +61,18 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
   float acc = 0.f;
   for (int d = lane; d < p.Dh; d += 64) acc = __builtin_fmaf(to_float(O[d]), to_float(dO[d]), acc);
   acc = wave_sum(acc);
-  if (lane == 0) p.delta[row] = acc;
+  if (lane == 0) {
+    p.delta[row] = acc;
+    if (p.lse2 != nullptr) {
+      const float l = p.LSE[row];
+      p.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+  }
+}
+
+// key j of sequence b not hidden by the key-padding mask
+__device__ __forceinline__ bool key_kept(const BwdParams& p, int b, int j) {
+  return p.kbits == nullptr || ((p.kbits[(size_t)b * p.kwords + (j >> 6)] >> (j & 63)) & 1);
 }
 
 // visible keys of query i: [lo, hi)
@@ -93,7 +111,10 @@ __global__ __launch_bounds__(256) void dq_rows_kernel(BwdParams p) {
   const float dlt = p.delta[row];
   int lo, hi;
   key_range(p, i, lo, hi);
+  // a row that saw no key (LSE = -inf) has O = 0 and passes no gradient
+  if (lse == -INFINITY) hi = lo;
   for (int j = lo; j < hi; ++j) {
+    if (!key_kept(p, b, j)) continue;
     const size_t r = kvoff + (size_t)j * p.Dh;
     float sq = 0.f, sv = 0.f;
 #pragma unroll
@@ -149,9 +170,11 @@ __global__ __launch_bounds__(256) void dkv_rows_kernel(BwdParams p) {
     dk[u] = 0.f;
     dv[u] = 0.f;
   }
-  // queries that see key j: i >= j (causal), i - j < window
+  // queries that see key j: i >= j (causal), i - j < window; none if the key
+  // is padding
   const int i_lo = p.causal ? j : 0;
-  const int i_hi = (p.causal && p.window > 0) ? min(p.S, j + p.window) : p.S;
+  const int i_hi = !key_kept(p, b, j) ? i_lo
+                   : (p.causal && p.window > 0) ? min(p.S, j + p.window) : p.S;
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
     const size_t qrow0 = ((size_t)b * p.Nq + h) * p.S;
@@ -205,14 +228,18 @@ hipError_t launch_general(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t backward_workspace(int B, int Nq, int S) { return (size_t)B * Nq * S * sizeof(float); }
+// Delta, then the rows' LSE in log2 units (the MFMA kernels read both)
+size_t backward_workspace(int B, int Nq, int S) { return 2 * (size_t)B * Nq * S * sizeof(float); }
 
-hipError_t launch_backward_delta(const void* O, const void* dO, float* delta, long long rows, int Dh,
-                                 int is_bf16, hipStream_t stream) {
+hipError_t launch_backward_delta(const void* O, const void* dO, const float* LSE, float* delta,
+                                 float* lse2, long long rows, int Dh, int is_bf16,
+                                 hipStream_t stream) {
   BwdParams p{};
   p.O = O;
   p.dO = dO;
+  p.LSE = LSE;
   p.delta = delta;
+  p.lse2 = lse2;
   p.B = 1;
   p.Nq = 1;
   p.S = (int)rows;
@@ -228,8 +255,9 @@ hipError_t launch_backward_delta(const void* O, const void* dO, float* delta, lo
 hipError_t launch_backward_general(const void* Q, const void* K, const void* V, const void* O,
                                    const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                    int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
-                                   float scale, void* ws, int is_bf16, hipStream_t stream) {
-  BwdParams p;
+                                   float scale, void* ws, int is_bf16, const uint64_t* kbits,
+                                   hipStream_t stream) {
+  BwdParams p{};
   p.Q = Q;
   p.K = K;
   p.V = V;
@@ -248,6 +276,8 @@ hipError_t launch_backward_general(const void* Q, const void* K, const void* V, 
   p.causal = causal;
   p.window = window;
   p.scale = scale;
+  p.kbits = kbits;
+  p.kwords = key_mask_words(S);
   return is_bf16 ? launch_general<__bf16>(p, stream) : launch_general<float>(p, stream);
 }
 

@@ -10,6 +10,8 @@
 //                   S^T  = K Q^T     (A: K tile rows,  B: Q in VGPRs)
 //                   dP^T = V dO^T    (A: V tile rows,  B: dO in VGPRs)
 //                   dS^T = P^T (dP^T - Delta),  P^T = exp2(S^T c - LSE log2 e)
+//                 (LSE log2 e comes from the Delta pass, +inf for a row that
+//                 saw no key under a key-padding mask, so its weights are 0)
 //                   dQ^T += K^T dS^T (A: K tile read transposed, B: dS^T)
 //   dkv_kernel -- (head sizes 64 and 256; head size 128 uses dkv_pipe_kernel
 //                 below, which puts dV and dK on different wavefronts; at 256
@@ -42,8 +44,10 @@ struct BwdMfmaParams {
   const __bf16* K;
   const __bf16* V;
   const __bf16* dO;
-  const float* LSE;
+  const float* lse2;   // the rows' LSE in log2 units, +inf for a row that saw no key
   const float* delta;
+  const uint64_t* kbits;  // key-padding mask (kwords words per sequence) or null
+  int kwords;
   __bf16* dQ;
   __bf16* dK;
   __bf16* dV;
@@ -68,7 +72,9 @@ __device__ __forceinline__ bool visible(const BwdMfmaParams& p, int q, int k) {
 
 // ---------------------------------------------------------------------------
 // dQ: one wavefront = 32 query rows of one head; workgroup as in the forward
-template <int D, int NW>
+// KM: a key-padding mask is given (p.kbits); without it the kernels are
+// compiled as if it did not exist.
+template <int D, int NW, bool KM>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
   using geo = Geo<D>;
   constexpr int KS = geo::KS;
@@ -125,8 +131,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
       df[ks] = ds[ks * 2];
     }
   }
-  const float lse2 = p.LSE[q_row0 + qi] * kLog2e;
+  const float lse2 = p.lse2[q_row0 + qi];
   const float dlt = p.delta[q_row0 + qi];
+  const uint64_t* const kr = KM ? p.kbits + (size_t)b * p.kwords : nullptr;
 
   int roff[KS];
   row_operand_offsets<D>(ln, hl, roff);
@@ -162,7 +169,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
       load_tile<D, NW>(Vh, (t + 1) * BN, Vn, w, lane);
     }
     if (t < tl_lo || t > tl_hi) return;
-    const bool need_mask = t < tf_lo || t > tf_hi;
+    // key-padding flags of the tile's 64 keys (one mask word); a tile of
+    // padding only contributes nothing
+    const uint64_t kword = KM ? kr[t] : ~0ull;
+    if (KM && kword == 0) return;
+    const bool need_mask = t < tf_lo || t > tf_hi || (KM && kword != ~0ull);
     const int k0 = t * BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -179,10 +190,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
       }
       // register r: key k0 + 32*kb + 8*(r/4) + 4*hl + r%4, query qa + ln
       if (need_mask) {
+        // this lane's flags: register r holds key k0 + 32*kb + 8*(r/4) + 4*hl + r%4
+        const uint32_t kwl = (uint32_t)(kword >> (kb * 32)) >> (hl * 4);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (!visible(p, qa + ln, key)) s[r] = -INFINITY;
+          bool hide = !visible(p, qa + ln, key);
+          if (KM) hide = hide || !((kwl >> ((r >> 2) * 8 + (r & 3))) & 1);
+          if (hide) s[r] = -INFINITY;
         }
       }
       bf16x8 dsf[2];
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: one wavefront = 32 keys of one K/V head; workgroup = NW waves of
 // consecutive keys; loops over (query head of the group, query tile).
-template <int D, int NW>
+template <int D, int NW, bool KM>
 __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
   using geo = Geo<D>;
   constexpr int KS = geo::KS;
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     load_tile<D, NW>(head_ref<D>(p.Q + row0 * D, p.S), q0, qdst, w, lane);
     load_tile<D, NW>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, w, lane);
     if (w < 2) {
-      const float* src = (w == 0 ? p.LSE : p.delta) + row0;
+      const float* src = (w == 0 ? p.lse2 : p.delta) + row0;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.S * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(adst + w * BN), 4, (q0 + lane) * 4,
@@ -291,8 +306,18 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
   };
   if (n_items > 0) issue(0, q0s, o0s, a0s);
 
-  // K and V as B operands: key column ln, head dims 16*ks + 8*hl + i
+  // key-padding flag of this lane's key; a wave whose 32 keys are all
+  // padding has no gradient to form
+  bool key_ok = true, any_key = true, all_keys = true;
   const int kj = min(kw0 + ln, p.S - 1);
+  if constexpr (KM) {
+    key_ok = (p.kbits[(size_t)b * p.kwords + (kj >> 6)] >> (kj & 63)) & 1;
+    const uint64_t key_bal = __builtin_amdgcn_ballot_w64(key_ok);
+    any_key = __builtin_amdgcn_readfirstlane(key_bal != 0);
+    all_keys = __builtin_amdgcn_readfirstlane(key_bal == ~0ull);
+  }
+
+  // K and V as B operands: key column ln, head dims 16*ks + 8*hl + i
   bf16x8 kf[KS], vf[KS];
   {
     const bf16x8* ks_ = reinterpret_cast<const bf16x8*>(p.K + (kv_row0 + kj) * D + hl * 8);
@@ -325,11 +350,11 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
     __syncthreads();
     if (it + 1 < n_items) issue(it + 1, Qn, On, An);
     // does this wave see any (query, key) pair of the tile?  all of them?
-    bool live = wave_live && q0 < p.S;
+    bool live = wave_live && q0 < p.S && any_key;
     if (p.causal) live = live && q0 + BN - 1 >= kw0;
     if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
     if (!live) return;
-    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
+    bool full = q0 + BN <= p.S && kw1 - kw0 == 32 && all_keys;
     if (p.causal) full = full && q0 >= kw1 - 1;
     if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
 
@@ -352,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
+          if (!visible(p, q, kw0 + ln) || (KM && !key_ok)) s[r] = -INFINITY;
         }
       }
       bf16x8 pf[2], sf[2];
@@ -370,8 +395,8 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
           const int r0 = kk * 8 + 2 * j;
           const f32x4 lv = l4[j >> 1], dv4 = d4[j >> 1];
           const int u = (2 * j) & 3;
-          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lv[u] * kLog2e));
-          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lv[u + 1] * kLog2e));
+          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lv[u]));
+          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lv[u + 1]));
           pp[j] = pack_bf16x2(p0, p1);
           ss[j] = pack_bf16x2(p0 * (dp[r0] - dv4[u]), p1 * (dp[r0 + 1] - dv4[u + 1]));
         }
@@ -432,7 +457,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(BwdMfmaParams p) {
 // by that stage count, so every transposing read names a fixed LDS object and
 // the compiler keeps the copies in flight across it.  Same products and
 // roundings as the other forms: the results are bit for bit theirs.
-template <int D>
+template <int D, bool KM>
 __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
   using geo = Geo<D>;
   constexpr int NR = 4;  // waves per role
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
     const size_t row0 = item_row0(it);
     const int q0 = item_q0(it);
     load_tile<D, NR>(head_ref<D>(p.dO + row0 * D, p.S), q0, odst, wl, lane);
-    if (wl == 0) load_vec(p.LSE + row0, q0, ldst);
+    if (wl == 0) load_vec(p.lse2 + row0, q0, ldst);
   };
   auto issue_k = [&](int it, char* qdst, float* ddst) {  // dK waves: Q and Delta
     const size_t row0 = item_row0(it);
@@ -503,17 +528,26 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
     if (wl == 0) load_vec(p.delta + row0, q0, ddst);
   };
   // does the wave pair see any (query, key) pair of item it?  all of them?
+  // key-padding flag of this lane's key (waves w and w + 4 share keys)
+  bool key_ok = true, any_key = true, all_keys = true;
+  const int kj = min(kw0 + ln, p.S - 1);
+  if constexpr (KM) {
+    key_ok = (p.kbits[(size_t)b * p.kwords + (kj >> 6)] >> (kj & 63)) & 1;
+    const uint64_t key_bal = __builtin_amdgcn_ballot_w64(key_ok);
+    any_key = __builtin_amdgcn_readfirstlane(key_bal != 0);
+    all_keys = __builtin_amdgcn_readfirstlane(key_bal == ~0ull);
+  }
   auto live_of = [&](int it) {
     if (it >= n_items) return false;
     const int q0 = item_q0(it);
-    bool live = wave_live && q0 < p.S;
+    bool live = wave_live && q0 < p.S && any_key;
     if (p.causal) live = live && q0 + BN - 1 >= kw0;
     if (p.window > 0) live = live && q0 - (kw1 - 1) < p.window;
     return live;
   };
   auto full_of = [&](int it) {
     const int q0 = item_q0(it);
-    bool full = q0 + BN <= p.S && kw1 - kw0 == 32;
+    bool full = q0 + BN <= p.S && kw1 - kw0 == 32 && all_keys;
     if (p.causal) full = full && q0 >= kw1 - 1;
     if (p.window > 0) full = full && q0 + BN - 1 - kw0 < p.window;
     return full;
@@ -522,7 +556,6 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
 
   // K fragments (dV waves, for S) or V fragments (dK waves, for dP) as B
   // operands: key column ln, head dims 16*ks + 8*hl + i
-  const int kj = min(kw0 + ln, p.S - 1);
   bf16x8 bf[KS];
   {
     const bf16x8* src =
@@ -573,7 +606,7 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int q = q0 + mb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-            if (!visible(p, q, kw0 + ln)) s[r] = -INFINITY;
+            if (!visible(p, q, kw0 + ln) || (KM && !key_ok)) s[r] = -INFINITY;
           }
         }
 #pragma unroll
@@ -582,7 +615,7 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
           f32x4 e;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            e[u] = exp2_fast(__builtin_fmaf(s[a * 4 + u], p.c, -(l4[u] * kLog2e)));
+            e[u] = exp2_fast(__builtin_fmaf(s[a * 4 + u], p.c, -l4[u]));
           pw[(mb * 4 + a) * 64] = e;
           u32x4& dst = *reinterpret_cast<u32x4*>(&pf[mb][a >> 1]);
           dst[(a & 1) * 2 + 0] = pack_bf16x2(e[0], e[1]);
@@ -699,7 +732,7 @@ __global__ __launch_bounds__(512) void dkv_pipe_kernel(BwdMfmaParams p) {
     }
 }
 
-template <int D>
+template <int D, bool KM>
 hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   constexpr int NWQ = D == 256 ? 4 : 8;  // dQ waves per workgroup (256: 404 registers, one per SIMD)
   constexpr int NWK = 4;                 // dK/dV waves per workgroup (one per SIMD)
@@ -716,13 +749,13 @@ hipError_t launch_bwd(BwdMfmaParams p, hipStream_t stream) {
   const long long nk = pair ? (long long)((p.S + 127) / 128) * p.B * p.Nkv
                             : (long long)((p.S + NWK * 32 - 1) / (NWK * 32)) * p.B * p.Nkv;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((dq_kernel<D, NWQ>), dim3((unsigned)nq), dim3(NWQ * 64), 0, stream, p);
+  hipLaunchKernelGGL((dq_kernel<D, NWQ, KM>), dim3((unsigned)nq), dim3(NWQ * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (pair)
-    hipLaunchKernelGGL((dkv_pipe_kernel<D>), dim3((unsigned)nk), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((dkv_pipe_kernel<D, KM>), dim3((unsigned)nk), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((dkv_kernel<D, NWK>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
+    hipLaunchKernelGGL((dkv_kernel<D, NWK, KM>), dim3((unsigned)nk), dim3(NWK * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -733,17 +766,20 @@ bool backward_bf16_supported(int Dh) { return Dh == 64 || Dh == 128 || Dh == 256
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
-                                float scale, void* ws, hipStream_t stream) {
-  hipError_t e = launch_backward_delta(O, dO, static_cast<float*>(ws), (long long)B * Nq * S, Dh,
-                                       1, stream);
+                                float scale, void* ws, const uint64_t* kbits, hipStream_t stream) {
+  const long long rows = (long long)B * Nq * S;
+  float* const delta = static_cast<float*>(ws);
+  hipError_t e = launch_backward_delta(O, dO, LSE, delta, delta + rows, rows, Dh, 1, stream);
   if (e != hipSuccess) return e;
   BwdMfmaParams p;
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
   p.V = static_cast<const __bf16*>(V);
   p.dO = static_cast<const __bf16*>(dO);
-  p.LSE = LSE;
-  p.delta = static_cast<const float*>(ws);
+  p.lse2 = delta + rows;
+  p.delta = delta;
+  p.kbits = kbits;
+  p.kwords = key_mask_words(S);
   p.dQ = static_cast<__bf16*>(dQ);
   p.dK = static_cast<__bf16*>(dK);
   p.dV = static_cast<__bf16*>(dV);
@@ -757,9 +793,9 @@ hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, con
   p.scale = scale;
   p.G = Nq / Nkv;
   switch (Dh) {
-    case 64: return launch_bwd<64>(p, stream);
-    case 128: return launch_bwd<128>(p, stream);
-    case 256: return launch_bwd<256>(p, stream);
+    case 64: return kbits ? launch_bwd<64, true>(p, stream) : launch_bwd<64, false>(p, stream);
+    case 128: return kbits ? launch_bwd<128, true>(p, stream) : launch_bwd<128, false>(p, stream);
+    case 256: return kbits ? launch_bwd<256, true>(p, stream) : launch_bwd<256, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

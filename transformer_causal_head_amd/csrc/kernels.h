@@ -96,20 +96,25 @@ hipError_t launch_kv_append_rope(const void* Knew, const void* Vnew, void* Kc, v
                                  int style, int elem_bytes, hipStream_t stream);
 
 // Backward pass of prefill attention.  The workspace holds Delta
-// [B, Nq, S] fp32 (dO . O per row).
+// [B, Nq, S] fp32 (dO . O per row), then the rows' LSE in log2 units
+// [B, Nq, S] fp32 (+inf for a row that saw no key).  kbits: key-padding mask
+// [B, key_mask_words(S)] or null.
 size_t backward_workspace(int B, int Nq, int S);
 hipError_t launch_backward_general(const void* Q, const void* K, const void* V, const void* O,
                                    const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                    int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
-                                   float scale, void* ws, int is_bf16, hipStream_t stream);
-// Delta_i = dO_i . O_i for `rows` rows of Dh elements
-hipError_t launch_backward_delta(const void* O, const void* dO, float* delta, long long rows, int Dh,
-                                 int is_bf16, hipStream_t stream);
-// bf16 MFMA backward (Dh 64 or 128): Delta, then the dQ and dK/dV kernels
+                                   float scale, void* ws, int is_bf16, const uint64_t* kbits,
+                                   hipStream_t stream);
+// Delta_i = dO_i . O_i for `rows` rows of Dh elements (and, if lse2 is not
+// null, lse2_i = LSE_i log2(e), +inf where LSE_i = -inf)
+hipError_t launch_backward_delta(const void* O, const void* dO, const float* LSE, float* delta,
+                                 float* lse2, long long rows, int Dh, int is_bf16,
+                                 hipStream_t stream);
+// bf16 MFMA backward (Dh 64, 128 or 256): Delta, then the dQ and dK/dV kernels
 bool backward_bf16_supported(int Dh);
 hipError_t launch_backward_bf16(const void* Q, const void* K, const void* V, const void* O,
                                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
                                 int B, int Nq, int Nkv, int S, int Dh, int causal, int window,
-                                float scale, void* ws, hipStream_t stream);
+                                float scale, void* ws, const uint64_t* kbits, hipStream_t stream);
 
 }  // namespace attn
