@@ -252,8 +252,9 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
 
 
 # wavefronts of the even split's partial grid (its workspace slots are
-# B * Nkv + EVEN_WAVES); it serves up to 64 sequences at head sizes up to 128
-# when the chunk mode's grid would have at least EVEN_WAVES / 2 items
+# B * Nkv + EVEN_WAVES); it serves up to 64 sequences (at head size 256 only
+# with at most 16 query heads per K/V head) when the chunk mode's grid would
+# have at least EVEN_WAVES / 2 items
 EVEN_WAVES = 1024
 
 
@@ -337,6 +338,8 @@ def _even_lens(kind, B, Tcap, rng):
     (128, 16, 32, 1, 60000, "one_long", 0),
     (64, 45, 16, 4, 2500, "ragged", 0),
     (64, 64, 32, 2, 3000, "ragged", 777),
+    (256, 64, 32, 8, 3000, "ragged", 0),      # head size 256: one block of query heads
+    (256, 16, 16, 1, 20000, "one_long", 300),
 ])
 def test_decode_even_split(Dh, B, Nq, Nkv, Tcap, kind, window):
     # up to 64 sequences without a key-padding mask: the visible steps of all

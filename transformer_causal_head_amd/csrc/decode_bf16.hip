@@ -881,9 +881,10 @@ DecodePlan decode_plan(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
   // grids of at least kEvenWaves / 2 chunk items: below that every chunk runs
   // at once anyway, and the table each wavefront builds first (a dependent
   // load of the lengths before its first copy) costs more than the balance
-  // gains (one sequence of 32768 keys, 8 K/V heads: 31 us against 28).  Head
-  // size 256 keeps chunk mode (the segment loop spills its registers).
-  d.ev = Dh <= 128 && B <= 64 && d.slots >= kEvenWaves / 2;
+  // gains (one sequence of 32768 keys, 8 K/V heads: 31 us against 28).  At
+  // head size 256 only the plain form with one block of query heads fits the
+  // registers (see launch_decode_bf16).
+  d.ev = B <= 64 && d.slots >= kEvenWaves / 2 && (Dh <= 128 || Nq / Nkv <= 16);
   // the even split's merge folds runs of about as many pieces as the chunk
   // mode's (a row's share of the grid is the same); longer runs just loop
   d.ev_mw = d.mw;
@@ -919,6 +920,8 @@ hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
     if (p.ev_nw)
       return p.rope.table ? launch_decode_km<D, NB, false, false, true, true>(p, stream)
                           : launch_decode_km<D, NB, false, false, false, true>(p, stream);
+  } else if constexpr (NB == 1) {
+    if (p.ev_nw) return launch_decode_km<D, NB, false, false, false, true>(p, stream);
   }
   return p.rope.table ? launch_decode_km<D, NB, false, false, true>(p, stream)
                       : launch_decode_km<D, NB, false>(p, stream);
@@ -958,7 +961,9 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   p.Tcap = Tcap;
   p.ch = d.ch;
   p.n_slots = d.n_slots;
-  const bool ev = d.ev && kbits == nullptr;
+  // the even split at head size 256 only in its plain form (the rotating and
+  // appending forms spill there)
+  const bool ev = d.ev && kbits == nullptr && (Dh <= 128 || (rope == nullptr && knew == nullptr));
   p.ev_nw = ev ? kEvenWaves : 0;
   p.ev_min = (p.G >= 16 ? kFloorKeysWide : kFloorKeys) / STEP;
   p.mw = ev ? d.ev_mw : d.mw;
