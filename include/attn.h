@@ -15,9 +15,17 @@
  *   - All tensor pointers are DEVICE pointers to dense row-major (contiguous)
  *     buffers owned by the caller.  The library never allocates, frees,
  *     synchronises or keeps a pointer after the call returns; the caller keeps
- *     every buffer alive until the stream has passed the call.  The one
- *     buffer of its own is attn_decode_noalloc's fixed scratch array (see
- *     there).
+ *     every buffer alive until the stream has passed the call.  The library's
+ *     own device memory is attn_decode_noalloc's fixed scratch array (see
+ *     there) and up to 256 sets of 9 work counters per device, one per
+ *     stream, for the causal bf16 prefills without a window or cache whose
+ *     grid covers the chip four or more times (the last quarter of such a
+ *     grid is handed out at run time).  A
+ *     stream's launches run one after another, and each launch leaves its
+ *     set cleared for the next.  A launch into hipStreamPerThread, into a
+ *     stream being captured into a graph or belonging to another device than
+ *     the current one, or from a stream beyond the 256th takes a fixed order;
+ *     the results are the same bits either way.
  *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *     Work is enqueued asynchronously on it.
  *   - Return value: ATTN_OK (0) or a negative attn_status.  Argument errors
@@ -28,8 +36,9 @@
  *     multiple of Nkv (MHA: Nkv == Nq, MQA: Nkv == 1).
  *   - Element types: ATTN_BF16 (inputs and O in bfloat16, accumulation in
  *     fp32) or ATTN_F32.  LSE is always fp32.
- *   - The library is stateless and re-entrant, apart from that scratch array,
- *     which calls of attn_decode_noalloc on one device share.
+ *   - The library is re-entrant.  Its state is that scratch array, which
+ *     calls of attn_decode_noalloc on one device share, and the per-stream
+ *     work-counter sets (their stream map is guarded by a lock).
  */
 #ifndef TCH_ATTN_H
 #define TCH_ATTN_H

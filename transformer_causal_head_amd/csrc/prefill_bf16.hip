@@ -48,6 +48,9 @@
 //     K/V head, head-group) combinations all workgroups of one K/V head land
 //     on the same XCD and share its L2.
 
+#include <mutex>
+#include <unordered_map>
+
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -93,7 +96,38 @@ struct Params {
   // lightest first, so that the two workgroups a CU receives together stream
   // about the same number of key tiles in total
   int zigzag;
+  // Work items [0, n_static) go to workgroup blockIdx.x; the rest are drawn at
+  // run time from the counters at `queues` (8 per-XCD draw counters, then the
+  // count of workgroups done drawing) by the workgroups from n_static on.
+  // queues == nullptr: every workgroup takes item blockIdx.x.
+  unsigned* queues;
+  int n_items, n_static;
 };
+
+// The tail of a multi-round grid, drawn at run time.  The dispatcher hands
+// workgroup i to XCD i % 8, so every XCD receives the same share of the grid,
+// and the XCDs do not run at the same speed.  Queue x holds the tail items
+// that XCD x would have received (n_static + x, + 8, ...), heaviest first.  A
+// workgroup draws from its own XCD's queue while it lasts (that XCD's L2
+// holds the K/V heads of those items) and then from the others', so an XCD
+// that runs ahead takes over the last items of a slower one.  Returns the
+// item, or -1 once every queue is empty.  The workgroup that draws last
+// clears the counters for the next launch that uses them.
+__device__ int draw_item(const Params& p) {
+  const int x = __builtin_amdgcn_s_getreg(6164) & 7;  // HW_REG_XCC_ID
+  const int n = p.n_items - p.n_static;
+  int item = -1;
+  for (int k = 0; k < 8 && item < 0; ++k) {
+    const int q = (x + k) & 7;
+    const unsigned j = atomicAdd(p.queues + q, 1u);
+    if (j < (unsigned)((n - q + 7) / 8)) item = p.n_static + (int)j * 8 + q;
+  }
+  // the draws above have returned before the count below is raised
+  __asm__ volatile("" ::: "memory");
+  if (atomicAdd(p.queues + 8, 1u) == gridDim.x - (unsigned)p.n_static - 1u)
+    for (int k = 0; k < 9; ++k) atomicExch(p.queues + k, 0u);
+  return item;
+}
 
 template <int D, int QB_>
 __device__ __forceinline__ void qk_tile(const char* Kt, const int (&koff)[Geo<D>::KS],
@@ -235,6 +269,14 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   __shared__ __attribute__((aligned(1024))) char v1s[NH * TILE];
 
   const int tid = threadIdx.x;
+  __shared__ int s_item;
+  int bid = blockIdx.x;
+  if (p.queues != nullptr && bid >= p.n_static) {
+    if (tid == 0) s_item = draw_item(p);
+    __syncthreads();
+    bid = s_item;
+    if (bid < 0) return;  // a spare workgroup that found every queue empty
+  }
   const int w_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = SK ? (w_all >> 2) : 0;  // key half (SK)
   const int w = SK ? (w_all & 3) : w_all;  // query wave; copying wave of its half
@@ -245,7 +287,6 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
 
   // workgroup -> (q tile, batch, K/V head, head subgroup); heavy tiles first
   const int inner = p.B * p.Nkv * p.n_hsub;
-  const int bid = blockIdx.x;
   const int qidx = bid / inner;
   const int qt = !p.causal ? qidx
                  : (p.zigzag && qidx >= p.n_qtiles / 2) ? qidx - p.n_qtiles / 2
@@ -739,6 +780,53 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   }
 }
 
+}  // namespace
+
+// Counters of the run-time drawn grid tails: kQueueSets sets of 16 words on
+// each device that runs the library (9 used; the rest keep sets on separate
+// 64-byte lines), one set per stream that launches such grids.  Kernels of
+// one stream run one after another and the last drawing workgroup of each
+// launch clears its set, so a set never has two users at once.
+// hipStreamDestroy waits for the stream's work, so a stream created later at
+// the same handle cannot overlap a launch of the old one.  Launches into the
+// per-thread default stream (one handle, several streams), into a stream
+// being captured into a graph (a replay could overlap any launch), into a
+// stream of another device, and from streams beyond the last set take the
+// fixed order instead.
+constexpr int kQueueSets = 256;
+static __device__ __align__(256) unsigned prefill_queues[kQueueSets * 16];
+
+namespace {
+constexpr int kQueueDevices = 64;
+constexpr int kSpareGroups = 512;  // extra workgroups of a drawn grid: 64 per XCD
+
+std::mutex queue_mu;
+unsigned* queue_base[kQueueDevices];  // device address of prefill_queues
+std::unordered_map<hipStream_t, int> queue_set[kQueueDevices];
+
+// The counter set of `stream` on device dev, or null for the fixed order.
+unsigned* stream_queues(int dev, hipStream_t stream) {
+  if (dev < 0 || dev >= kQueueDevices || stream == hipStreamPerThread) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return nullptr;
+  int sdev = -1;
+  if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  std::lock_guard<std::mutex> lock(queue_mu);
+  if (queue_base[dev] == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(prefill_queues)) != hipSuccess) return nullptr;
+    queue_base[dev] = static_cast<unsigned*>(a);
+  }
+  auto& sets = queue_set[dev];
+  auto it = sets.find(stream);
+  if (it == sets.end()) {
+    if (sets.size() >= (size_t)kQueueSets) return nullptr;
+    it = sets.emplace(stream, (int)sets.size()).first;
+  }
+  return queue_base[dev] + 16 * it->second;
+}
+
 template <int D>
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, float* LSE,
                           int B, int Nq, int Nkv, int S, int kv_rows, const int32_t* lens,
@@ -806,6 +894,24 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, void* O, 
   p.strided = !small && causal && window == 0 && lens == nullptr && p.n_qtiles > 1 &&
               nblocks <= n_cu;
   p.zigzag = small && !split && causal && (p.n_qtiles % 2 == 0);
+  // A causal prefill without a window whose grid runs four or more rounds
+  // draws its last quarter of items at run time.  Those are the lightest
+  // query tiles (short key prefixes), so an XCD that takes one over from
+  // another fetches little that its L2 does not hold.  With a window, a
+  // cache or no mask the items cost about the same, each stolen one streams
+  // its whole key range from HBM, and the drawn tail measured 1 % slower on
+  // the GQA window workload.  On grids under four rounds one atomic per
+  // drawing workgroup costs more than the balance gains.
+  p.queues = nullptr;
+  p.n_items = p.n_static = (int)nblocks;
+  if (!small && causal && window == 0 && lens == nullptr && n_cu > 0 && nblocks >= 4LL * n_cu &&
+      nblocks + kSpareGroups <= 0x7fffffffLL) {
+    p.queues = stream_queues(dev, stream);
+    if (p.queues) {
+      p.n_static = (p.n_items - p.n_items / 4) & ~7;  // a multiple of 8: XCDs keep their items
+      nblocks += kSpareGroups;
+    }
+  }
   if constexpr (D == 128 && NW == 8) {
     if (split) {
       hipLaunchKernelGGL((prefill_kernel<D, 8, false, true>), dim3((unsigned)nblocks), dim3(512), 0,
