@@ -34,21 +34,21 @@ def _chunk(B, Nkv, L, G):
 
 def _waves(B, Nkv, Tcap, G, window):
     # wavefronts per row the host gives the merge: the fewest of 1..16 that
-    # leave each at most 12 slots
+    # leave each at most 16 slots (one round of requests)
     L = window if 0 < window < Tcap else Tcap
     ch = _chunk(B, Nkv, L, G)
     slots = -(-Tcap // ch)
     if L < Tcap:
         slots = min(slots, -(-L // ch) + 1)
     mw = 1
-    while mw < 16 and -(-slots // mw) > 12:
+    while mw < 16 and -(-slots // mw) > 16:
         mw *= 2
     return mw
 
 
 @pytest.mark.parametrize("Dh,B,Nq,Nkv,Tcap,lens,window,pads,block,mw", [
     (128, 2, 32, 1, 32768, [32768, 5], 0, None, None, 16),     # 147 slots; the second row has 1
-    (128, 1, 8, 1, 65000, [65000], 0, None, None, 16),         # 102 slots of 640 keys
+    (128, 1, 8, 1, 65000, [65000], 0, None, None, 8),          # 102 slots of 640 keys
     (128, 2, 32, 1, 32768, [32768, 20500], 20000, None, None, 8),  # windowed: 91 slots
     (128, 4, 32, 8, 12000, [12000, 9000, 640, 641], 0, None, None, 2),
     (128, 8, 32, 8, 32768, [32768, 1, 30000, 12345, 640, 7000, 32767, 2048], 0, None, None, 4),
@@ -57,7 +57,12 @@ def _waves(B, Nkv, Tcap, G, window):
     (256, 1, 32, 1, 32768, [31000], 0, None, None, 16),
     # key padding: chunks 5..110 see padding only, and the second row no key at all
     (128, 2, 32, 1, 32768, [32768, 30000], 0, [0, 30000], (1000, 25000), 16),
-    (128, 1, 8, 1, 65000, [65000], 0, [40000], None, 16),      # the first 62 slots dead
+    (128, 1, 8, 1, 65000, [65000], 0, [40000], None, 8),       # the first 62 slots dead
+    # 586 chunks of 224 keys: with a mask (chunk mode) each merge wavefront
+    # folds 36-37 slots in three rounds of requests; without one the even
+    # split's 512 pieces leave 32 per wavefront, two rounds
+    (128, 1, 32, 1, 131072, [131072], 0, [5], None, 16),
+    (128, 1, 32, 1, 131072, [131072], 0, None, None, 16),
 ])
 def test_decode_merge_waves(Dh, B, Nq, Nkv, Tcap, lens, window, pads, block, mw):
     assert _waves(B, Nkv, Tcap, Nq // Nkv, window) == mw

@@ -251,8 +251,9 @@ def test_decode_edge_cases(B, Nq, Nkv, Tcap, lens):
     check(O, L, Or, Lr, "bf16", (B, Nq, Nkv, Tcap, lens), storage_allowance=True)
 
 
-# wavefronts of the even split's partial grid (its workspace slots are
-# B * Nkv + EVEN_WAVES); it serves up to 64 sequences (at head size 256 only
+# wavefronts of the even split's partial grid, at most (its workspace slots
+# are B * Nkv + EVEN_WAVES; 16 or more query heads per K/V head use half as
+# many wavefronts); it serves up to 64 sequences (at head size 256 only
 # with at most 16 query heads per K/V head) when the chunk mode's grid would
 # have at least EVEN_WAVES / 2 items
 EVEN_WAVES = 1024
@@ -343,7 +344,8 @@ def _even_lens(kind, B, Tcap, rng):
 ])
 def test_decode_even_split(Dh, B, Nq, Nkv, Tcap, kind, window):
     # up to 64 sequences without a key-padding mask: the visible steps of all
-    # (sequence, K/V head) pairs are cut into equal wavefront ranges; ranges
+    # (sequence, K/V head) pairs are cut into wavefront ranges (64 : 55 for
+    # wavefronts on even and odd XCDs); ranges
     # that hold several segments, segments split over many ranges, windows,
     # and totals too small to fill the grid
     rng = np.random.default_rng(Tcap + B + Dh)

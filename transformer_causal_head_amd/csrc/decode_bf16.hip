@@ -64,8 +64,17 @@ constexpr int STEP = 32;             // keys per pipeline step
 constexpr float TAU = 8.f;
 constexpr int kNonTemporal = 2;      // cache-policy bit of the copy instructions
 // even split: wavefronts of the partial grid -- four per CU, all resident at
-// once (more would leave a second round for the rest)
+// once (more would leave a second round for the rest); two per CU with 16 or
+// more query heads per K/V head, whose steps carry twice the matrix work and
+// whose partials cost G (Dh + 2) floats per piece
 constexpr int kEvenWaves = 1024;
+constexpr int kEvenWavesWide = 512;
+// even split: range weights of the wavefronts on even and odd XCDs.  The
+// dispatcher hands wavefront w to XCD w % 8, and streaming decode runs 7-10 %
+// slower on the odd XCDs, so their ranges are shorter (64 : 55).
+constexpr long long kWeightEven = 64, kWeightOdd = 55;
+// merge: partial outputs a wavefront requests at a time
+constexpr int kMergeBatch = 16;
 // shortest chunk (and shortest even-split range): 640 keys, 224 with 16 or
 // more query heads per K/V head -- shorter ones cost more in partials to
 // write and merge than their extra parallelism gains
@@ -163,6 +172,23 @@ __device__ __forceinline__ EvenTable even_table(const DecParams& p, int lane) {
   t.tot = (long long)__shfl(v, 63, 64) * p.Nkv;
   t.nwe = (int)max(1LL, min((long long)p.ev_nw, t.tot / p.ev_min));
   return t;
+}
+// weight of wavefronts 0 .. w-1 (even w on even XCDs, odd w on odd ones)
+__device__ __forceinline__ long long range_weight(int w) {
+  return kWeightEven * ((w + 1) >> 1) + kWeightOdd * (w >> 1);
+}
+// first global step of wavefront w's range (w = nwe: the total)
+__device__ __forceinline__ long long range_start(const EvenTable& t, int w) {
+  return t.tot * range_weight(w) / range_weight(t.nwe);
+}
+// the wavefront whose range holds global step x: an estimate from the mean
+// weight of a pair of wavefronts, then corrected against the range starts
+__device__ __forceinline__ int range_of(const EvenTable& t, long long x) {
+  int w = (int)min((long long)t.nwe - 1,
+                   x * range_weight(t.nwe) / (t.tot * (kWeightEven + kWeightOdd)) * 2);
+  while (w + 1 < t.nwe && range_start(t, w + 1) <= x) ++w;
+  while (w > 0 && range_start(t, w) > x) --w;
+  return w;
 }
 
 // Rows [k0, k0+32) of one head -> one LDS stage: NPIECE copies of RP whole
@@ -300,8 +326,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       }
     }
     if (ev_w >= tab.nwe) return;
-    ev_a = (long long)ev_w * tab.tot / tab.nwe;
-    ev_e = (long long)(ev_w + 1) * tab.tot / tab.nwe;
+    ev_a = range_start(tab, ev_w);
+    ev_e = range_start(tab, ev_w + 1);
     if (ev_a >= ev_e) return;
     // the segment holding step ev_a: sequence b is the first whose steps end
     // past it (every lane at or past B holds the total)
@@ -696,8 +722,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
 // folding a contiguous run of slots under its own running max; the row's first
 // wavefront then folds the wavefronts' results, rescaled to the common max,
 // from LDS, in wavefront order.  The kernel is latency-bound (a row's partials
-// are a few KB): a wavefront requests eight partial outputs at a time, the
-// first eight together with their (m, l), before the weights are known.
+// are a few KB): a wavefront requests sixteen partial outputs at a time, the
+// first sixteen together with their (m, l), before the weights are known.
 //
 // EV: the partials of the even split; segment (b, g) holds the pieces of the
 // wavefronts whose ranges meet its steps, wavefront w's piece at slot
@@ -724,11 +750,10 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
       const EvenTable t = even_table(p, lane);
       const int ns_b = __builtin_amdgcn_readlane(t.ns, b);
       if (ns_b > 0) {
-        // wavefront holding global step x: the last w with w*tot/nwe <= x
         const long long first = (long long)(__builtin_amdgcn_readlane(t.incl, b) - ns_b) * p.Nkv +
                                 (long long)(h / G) * ns_b;
-        const int wf = (int)(((first + 1) * t.nwe - 1) / t.tot);
-        const int wl = (int)(((first + ns_b) * t.nwe - 1) / t.tot);
+        const int wf = range_of(t, first);
+        const int wl = range_of(t, first + ns_b - 1);
         ns = wl - wf + 1;
         part0 = ((size_t)b * p.Nkv + h / G + wf) * G + h % G;  // slot x: part0 + x*G
       }
@@ -756,9 +781,9 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
       m = v.x;
       l = v.y;
     }
-    fvec ov[8];
+    fvec ov[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) ov[u] = u < cnt ? load_o(cb + u) : fvec{};
+    for (int u = 0; u < kMergeBatch; ++u) ov[u] = u < cnt ? load_o(cb + u) : fvec{};
     const float Mn = fmaxf(Mw, wave_max(m));
     // every slot so far may hold padding only (M = -inf): weights 0, not NaN
     const float Mu = Mn == -INFINITY ? 0.f : Mn;
@@ -768,16 +793,16 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
     Ll = __builtin_fmaf(wgt, l, Ll * r);
     Mw = Mn;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const float wu = __shfl(wgt, u, 64);
 #pragma unroll
       for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wu, ov[u][e], acc[e]);
     }
-    for (int j = 8; j < cnt; j += 8) {
+    for (int j = kMergeBatch; j < cnt; j += kMergeBatch) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) ov[u] = j + u < cnt ? load_o(cb + j + u) : fvec{};
+      for (int u = 0; u < kMergeBatch; ++u) ov[u] = j + u < cnt ? load_o(cb + j + u) : fvec{};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kMergeBatch; ++u) {
         const float wu = __shfl(wgt, j + u, 64);
 #pragma unroll
         for (int e = 0; e < PL; ++e) acc[e] = __builtin_fmaf(wu, ov[u][e], acc[e]);
@@ -849,11 +874,11 @@ int decode_bf16_chunk(int B, int Nkv, int L, int G) {
 
 
 namespace {
-// partial slots one merge wavefront folds at most (one or two rounds of eight
-// requests; 6, 12 and 24 measured within 1 % of each other)
-constexpr int kMergeSlots = 12;
+// partial slots one merge wavefront folds at most: one round of requests
+// (12 slots in rounds of eight were 1-2 % slower on the batched decode, 4 in
+// rounds of four 6-8 % slower)
+constexpr int kMergeSlots = 16;
 // merge: enough wavefronts per row that each folds at most kMergeSlots slots
-// (one or two rounds of eight requests)
 int merge_waves(long long slots) {
   int mw = 1;
   while (mw < 16 && (slots + mw - 1) / mw > kMergeSlots) mw *= 2;
@@ -964,7 +989,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   // the even split at head size 256 only in its plain form (the rotating and
   // appending forms spill there)
   const bool ev = d.ev && kbits == nullptr && (Dh <= 128 || (rope == nullptr && knew == nullptr));
-  p.ev_nw = ev ? kEvenWaves : 0;
+  p.ev_nw = ev ? (p.G >= 16 ? kEvenWavesWide : kEvenWaves) : 0;
   p.ev_min = (p.G >= 16 ? kFloorKeysWide : kFloorKeys) / STEP;
   p.mw = ev ? d.ev_mw : d.mw;
   const size_t parts = (size_t)d.slots * (Nq / Nkv);
