@@ -181,13 +181,14 @@ __device__ __forceinline__ long long range_weight(int w) {
 __device__ __forceinline__ long long range_start(const EvenTable& t, int w) {
   return t.tot * range_weight(w) / range_weight(t.nwe);
 }
-// the wavefront whose range holds global step x: an estimate from the mean
-// weight of a pair of wavefronts, then corrected against the range starts
+// the wavefront whose range holds global step x: range_start(w) <= x exactly
+// when tot * weight(w) < (x + 1) * weight(nwe), so after an estimate (within
+// one range of the answer) the search needs products only, no division
 __device__ __forceinline__ int range_of(const EvenTable& t, long long x) {
-  int w = (int)min((long long)t.nwe - 1,
-                   x * range_weight(t.nwe) / (t.tot * (kWeightEven + kWeightOdd)) * 2);
-  while (w + 1 < t.nwe && range_start(t, w + 1) <= x) ++w;
-  while (w > 0 && range_start(t, w) > x) --w;
+  const long long lim = (x + 1) * range_weight(t.nwe);
+  int w = min(t.nwe - 1, max(0, (int)((float)x * (float)t.nwe / (float)t.tot)));
+  while (w + 1 < t.nwe && t.tot * range_weight(w + 1) < lim) ++w;
+  while (w > 0 && t.tot * range_weight(w) >= lim) --w;
   return w;
 }
 
