@@ -47,9 +47,12 @@ def test_strerror_covers_all_codes():
 
 def test_workspace_query():
     n = tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_BF16)
-    # one (m, l, o[128]) fp32 record per (sequence, query head, key chunk)
+    # one (m, l, o[128]) fp32 record per (sequence, query head, key chunk),
+    # and for the even split the first and last range of each (sequence, K/V
+    # head) as two int32
     rec = 64 * 32 * (128 + 2) * 4
-    assert n > 0 and n % rec == 0 and 1 <= n // rec <= 32768 // 32
+    seg = 64 * 8 * 2 * 4
+    assert n > seg and (n - seg) % rec == 0 and 1 <= (n - seg) // rec <= 32768 // 32
     assert tch.attn_decode_workspace_bytes(64, 32, 8, 128, 32768, tch.ATTN_F32) == 0
     assert tch.attn_decode_workspace_bytes(64, 30, 8, 128, 32768, tch.ATTN_BF16) == 0
     assert tch.attn_decode_workspace_bytes(0, 32, 8, 128, 32768, tch.ATTN_BF16) == 0
@@ -57,7 +60,7 @@ def test_workspace_query():
     # window can touch get a slot
     assert tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 0, tch.ATTN_BF16) == n
     nw = tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 1024, tch.ATTN_BF16)
-    assert nw > 0 and nw % rec == 0 and nw // rec <= 32
+    assert nw > seg and (nw - seg) % rec == 0 and (nw - seg) // rec <= 32
     assert tch.attn_decode_window_workspace_bytes(64, 32, 8, 128, 32768, 40000,
                                                   tch.ATTN_BF16) == n
 

@@ -292,9 +292,11 @@ def test_decode_chunk_sizes(B, Nq, Nkv, Tcap, ch, masked):
     assert _decode_chunk(B, Nkv, Tcap, Nq // Nkv) == ch
     ws = tch.attn_decode_workspace_bytes(B, Nq, Nkv, 128, Tcap, tch.ATTN_BF16)
     slots = B * Nkv * -(-Tcap // ch)
+    seg = 0
     if B <= 64 and slots >= EVEN_WAVES // 2:
         slots = max(slots, B * Nkv + EVEN_WAVES)
-    assert ws == slots * (Nq // Nkv) * (128 + 2) * 4
+        seg = B * Nkv * 2 * 4  # the first and last range of each (sequence, K/V head)
+    assert ws == slots * (Nq // Nkv) * (128 + 2) * 4 + seg
     rng = np.random.default_rng(Tcap + B)
     lens = rng.integers(1, Tcap, B, endpoint=True)
     lens[:8] = [1, 31, 32, 33, ch - 1, ch, ch + 1, Tcap]

@@ -118,6 +118,7 @@ struct DecParams {
   float* LSE;
   float* ws_o;    // [B, Nkv, n_slots, G, D] unnormalised partial outputs
   float* ws_ml;   // [B, Nkv, n_slots, G, 2]  (m in log2 units, l)
+  int* ws_seg;    // even split: [B, Nkv, 2] first and last range of each segment
   int B, Nq, Nkv, G, Tcap;
   int n_slots;    // chunks that can hold visible keys, per (sequence, K/V head)
   int ch;         // keys per chunk (a multiple of STEP)
@@ -180,16 +181,6 @@ __device__ __forceinline__ long long range_weight(int w) {
 // first global step of wavefront w's range (w = nwe: the total)
 __device__ __forceinline__ long long range_start(const EvenTable& t, int w) {
   return t.tot * range_weight(w) / range_weight(t.nwe);
-}
-// the wavefront whose range holds global step x: range_start(w) <= x exactly
-// when tot * weight(w) < (x + 1) * weight(nwe), so after an estimate (within
-// one range of the answer) the search needs products only, no division
-__device__ __forceinline__ int range_of(const EvenTable& t, long long x) {
-  const long long lim = (x + 1) * range_weight(t.nwe);
-  int w = min(t.nwe - 1, max(0, (int)((float)x * (float)t.nwe / (float)t.tot)));
-  while (w + 1 < t.nwe && t.tot * range_weight(w + 1) < lim) ++w;
-  while (w > 0 && t.tot * range_weight(w) >= lim) --w;
-  return w;
 }
 
 // Rows [k0, k0+32) of one head -> one LDS stage: NPIECE copies of RP whole
@@ -301,6 +292,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
     slot = (size_t)b * p.Nkv + g + ev_w;
     ev_a += cnt;
     writer = s_in == 0;
+    // the merge reads which ranges hold the segment's first and last steps
+    if (lane == 0) {
+      int* seg = p.ws_seg + 2 * ((size_t)b * p.Nkv + g);
+      if (s_in == 0) seg[0] = ev_w;
+      if (s_in + cnt == ns_b) seg[1] = ev_w;
+    }
     load_new(s0 * STEP, nsteps * STEP);
   };
   if constexpr (EV) {
@@ -748,15 +745,13 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
     const int b = row / p.Nq;
     const int h = row % p.Nq;
     if constexpr (EV) {
-      const EvenTable t = even_table(p, lane);
-      const int ns_b = __builtin_amdgcn_readlane(t.ns, b);
-      if (ns_b > 0) {
-        const long long first = (long long)(__builtin_amdgcn_readlane(t.incl, b) - ns_b) * p.Nkv +
-                                (long long)(h / G) * ns_b;
-        const int wf = range_of(t, first);
-        const int wl = range_of(t, first + ns_b - 1);
-        ns = wl - wf + 1;
-        part0 = ((size_t)b * p.Nkv + h / G + wf) * G + h % G;  // slot x: part0 + x*G
+      // a segment with visible keys was taken by ranges wf .. wl, which the
+      // partial kernel recorded
+      const int n = max(0, min(p.lens[b], p.Tcap));
+      if (n > 0) {
+        const int2 fl = *reinterpret_cast<const int2*>(p.ws_seg + 2 * ((size_t)b * p.Nkv + h / G));
+        ns = fl.y - fl.x + 1;
+        part0 = ((size_t)b * p.Nkv + h / G + fl.x) * G + h % G;  // slot x: part0 + x*G
       }
     } else {
       const int n = min(p.lens[b], p.Tcap);
@@ -957,7 +952,8 @@ hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
 size_t decode_bf16_workspace(int B, int Nq, int Nkv, int Dh, int Tcap, int window) {
   const DecodePlan d = decode_plan(B, Nq, Nkv, Dh, Tcap, window);
   const size_t parts = (size_t)d.slots * (Nq / Nkv);
-  return parts * Dh * sizeof(float) + parts * 2 * sizeof(float);
+  return parts * Dh * sizeof(float) + parts * 2 * sizeof(float) +
+         (d.ev ? (size_t)B * Nkv * 2 * sizeof(int) : 0);
 }
 
 hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, const int32_t* lens,
@@ -996,6 +992,7 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   const size_t parts = (size_t)d.slots * (Nq / Nkv);
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = p.ws_o + parts * Dh;
+  p.ws_seg = reinterpret_cast<int*>(p.ws_ml + parts * 2);
   p.window = window;
   p.c = kLog2e * scale;
   p.rope = rope ? *rope : RopeQ{nullptr, 0, nullptr, nullptr, 0};
