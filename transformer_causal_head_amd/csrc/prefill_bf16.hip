@@ -651,17 +651,25 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
 
 
   // The pipelined loop: iteration i (tile t = t_lo + i) holds S(t) in
-  // registers, masked and with its running maximum applied; K(t+1) and V(t)
-  // are in LDS, and the copies of K(t+2) and V(t+1) are issued at its top.
-  // The iteration computes S(t+1) (QK^T), P(t) (exponentials, row sums),
-  // O += V(t)^T P(t), and the mask and running maximum of tile t+1.
+  // registers; K(t+1) and V(t) are in LDS, and the copies of K(t+2) and
+  // V(t+1) are issued at its top.  The iteration computes S(t+1) (QK^T), P(t)
+  // (exponentials, row sums) and O += V(t)^T P(t).  With the fused step, S(t)
+  // arrives masked and with its running maximum applied, and the iteration
+  // ends with the mask and maximum of tile t+1 (the fused step pairs them
+  // with the PV block).  Without it the mask and maximum of tile t come first,
+  // right after S(t+1) is issued: they need only S(t), so the VALU runs them
+  // while the matrix cores work on S(t+1).  Placing them after PV(t) instead
+  // (as the fused form must) made one-wave-per-SIMD head size 256 16 % slower
+  // and head size 64 and key-padded prefill 2-3 % slower.
   f32x16 sa[QB][2], sb[QB][2];
   wait_dma();
   __syncthreads();
   if (nt_h > 0 && live(t_base)) {
     qk_tile<D, QB>(K0, koff, qf, sa);
-    if (masked(t_base)) mask_tile(t_base, sa);
-    max_rescale(sa);
+    if constexpr (FUSED) {
+      if (masked(t_base)) mask_tile(t_base, sa);
+      max_rescale(sa);
+    }
   }
   auto iteration = [&](int i, f32x16 (&s_cur)[QB][2], f32x16 (&s_next)[QB][2], bool fused) {
     const int t = t_base + i;
@@ -678,10 +686,18 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
     } else {
       const bool nx = i + 1 < nt_h && live(t + 1);
       if (nx) qk_tile<D, QB>(Knext, koff, qf, s_next);
-      if (i < nt_h && live(t)) exp_pv(s_cur, Vcur);
-      if (nx) {
-        if (masked(t + 1)) mask_tile(t + 1, s_next);
-        max_rescale(s_next);
+      if constexpr (FUSED) {
+        if (i < nt_h && live(t)) exp_pv(s_cur, Vcur);
+        if (nx) {
+          if (masked(t + 1)) mask_tile(t + 1, s_next);
+          max_rescale(s_next);
+        }
+      } else {
+        if (i < nt_h && live(t)) {
+          if (masked(t)) mask_tile(t, s_cur);
+          max_rescale(s_cur);
+          exp_pv(s_cur, Vcur);
+        }
       }
     }
   };
