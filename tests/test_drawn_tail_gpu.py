@@ -124,3 +124,34 @@ def test_back_to_back_launches_on_one_stream():
     torch.cuda.synchronize()
     for i, (O, L) in enumerate(outs):
         assert _same(O, O0) and torch.equal(L, L0), i
+
+
+def test_key_padded_graph_replay_gives_the_eager_bits():
+    # the key-padded kernel draws its tail the same way
+    B, Nq, Nkv, S, Dh = 2, 32, 32, 8192, 128
+    say("drawn tail, key-padded: eager vs graph replay")
+    tq, tk, tv = _inputs(B, Nq, Nkv, S, Dh, seed=21)
+    mask = torch.ones(B, S, dtype=torch.bool, device=tq.device)
+    mask[0, :700] = False          # left padding
+    mask[1, 3000:3100] = False     # a hole
+    bits = torch.empty(B, (S + 63) // 64, dtype=torch.int64, device=tq.device)
+    tch.attn_pack_key_mask(mask, bits)
+    O = torch.empty_like(tq)
+    L = torch.empty((B, Nq, S), dtype=torch.float32, device=tq.device)
+    tch.attn_prefill_padded(tq, tk, tv, bits, O, L, causal=1)
+    torch.cuda.synchronize()
+    Og = torch.full_like(tq, float("nan"))
+    Lg = torch.full((B, Nq, S), float("nan"), dtype=torch.float32, device=tq.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            tch.attn_prefill_padded(tq, tk, tv, bits, Og, Lg, causal=1)
+    torch.cuda.synchronize()
+    for r in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(Og, O), f"replay {r}: O differs"
+        # rows that see no key carry LSE = -inf on both sides
+        assert torch.equal(Lg, L), f"replay {r}: LSE differs"

@@ -175,51 +175,111 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdMfmaParams p) {
     if (KM && kword == 0) return;
     const bool need_mask = t < tf_lo || t > tf_hi || (KM && kword != ~0ull);
     const int k0 = t * BN;
+    if constexpr (D == 256) {
+      // At head size 256 (one wave per SIMD) S and dP of both 32-key halves
+      // come first, so that the weights of half 0 can run beside the products
+      // of half 1 and those of half 1 beside dQ of half 0 (the backward at
+      // 16384 tokens 1-3 % faster).  With two waves per SIMD the other wave
+      // fills those gaps already (head size 128 unchanged, 64 4 % slower).
+      f32x16 s2[2], dp2[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) {
+        s2[kb] = f32x16{};
+        dp2[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * geo::RB + roff[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-      }
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * geo::RB + roff[ks]);
+          s2[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s2[kb], 0, 0, 0);
+        }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + kb * 32 * geo::RB + roff[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
-      }
-      // register r: key k0 + 32*kb + 8*(r/4) + 4*hl + r%4, query qa + ln
-      if (need_mask) {
-        // this lane's flags: register r holds key k0 + 32*kb + 8*(r/4) + 4*hl + r%4
-        const uint32_t kwl = (uint32_t)(kword >> (kb * 32)) >> (hl * 4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          bool hide = !visible(p, qa + ln, key);
-          if (KM) hide = hide || !((kwl >> ((r >> 2) * 8 + (r & 3))) & 1);
-          if (hide) s[r] = -INFINITY;
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + kb * 32 * geo::RB + roff[ks]);
+          dp2[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp2[kb], 0, 0, 0);
         }
       }
-      bf16x8 dsf[2];
+      bf16x8 dsf2[2][2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 pk;
+      for (int kb = 0; kb < 2; ++kb) {
+        // register r: key k0 + 32*kb + 8*(r/4) + 4*hl + r%4, query qa + ln
+        if (need_mask) {
+          const uint32_t kwl = (uint32_t)(kword >> (kb * 32)) >> (hl * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r0 = kk * 8 + 2 * j;
-          const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2));
-          const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2));
-          pk[j] = pack_bf16x2(p0 * (dp[r0] - dlt), p1 * (dp[r0 + 1] - dlt));
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+            bool hide = !visible(p, qa + ln, key);
+            if (KM) hide = hide || !((kwl >> ((r >> 2) * 8 + (r & 3))) & 1);
+            if (hide) s2[kb][r] = -INFINITY;
+          }
         }
-        dsf[kk] = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 pk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r0 = kk * 8 + 2 * j;
+            const float p0 = exp2_fast(__builtin_fmaf(s2[kb][r0], p.c, -lse2));
+            const float p1 = exp2_fast(__builtin_fmaf(s2[kb][r0 + 1], p.c, -lse2));
+            pk[j] = pack_bf16x2(p0 * (dp2[kb][r0] - dlt), p1 * (dp2[kb][r0 + 1] - dlt));
+          }
+          dsf2[kb][kk] = __builtin_bit_cast(bf16x8, pk);
+        }
       }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = read_tr_operand<D>(Kt, kb * 2 + kk, troff, db);
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], dq[db], 0, 0, 0);
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = read_tr_operand<D>(Kt, kb * 2 + kk, troff, db);
+            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf2[kb][kk], dq[db], 0, 0, 0);
+          }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + kb * 32 * geo::RB + roff[ks]);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + kb * 32 * geo::RB + roff[ks]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+        }
+        // register r: key k0 + 32*kb + 8*(r/4) + 4*hl + r%4, query qa + ln
+        if (need_mask) {
+          // this lane's flags: register r holds key k0 + 32*kb + 8*(r/4) + 4*hl + r%4
+          const uint32_t kwl = (uint32_t)(kword >> (kb * 32)) >> (hl * 4);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+            bool hide = !visible(p, qa + ln, key);
+            if (KM) hide = hide || !((kwl >> ((r >> 2) * 8 + (r & 3))) & 1);
+            if (hide) s[r] = -INFINITY;
+          }
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 pk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r0 = kk * 8 + 2 * j;
+            const float p0 = exp2_fast(__builtin_fmaf(s[r0], p.c, -lse2));
+            const float p1 = exp2_fast(__builtin_fmaf(s[r0 + 1], p.c, -lse2));
+            pk[j] = pack_bf16x2(p0 * (dp[r0] - dlt), p1 * (dp[r0 + 1] - dlt));
+          }
+          dsf[kk] = __builtin_bit_cast(bf16x8, pk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = read_tr_operand<D>(Kt, kb * 2 + kk, troff, db);
+            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], dq[db], 0, 0, 0);
+          }
+      }
     }
   };
   int i = 0;
