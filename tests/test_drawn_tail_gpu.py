@@ -155,3 +155,37 @@ def test_key_padded_graph_replay_gives_the_eager_bits():
         assert _same(Og, O), f"replay {r}: O differs"
         # rows that see no key carry LSE = -inf on both sides
         assert torch.equal(Lg, L), f"replay {r}: LSE differs"
+
+
+def test_three_streams_interleaved_shapes():
+    # three streams, each with its own counter set, take turns launching
+    # grids of different sizes (all long enough to draw their tails); every
+    # result must match the same call made alone
+    dev = device()
+    shapes = [(1, 32, 32, 8192, 128), (2, 16, 16, 8192, 128), (1, 32, 8, 12288, 128)]
+    inputs = [_inputs(B, Nq, Nkv, S, Dh, seed=30 + k) for k, (B, Nq, Nkv, S, Dh) in enumerate(shapes)]
+    say("drawn tail: three streams, interleaved shapes")
+    refs = []
+    for (B, Nq, Nkv, S, Dh), x in zip(shapes, inputs):
+        O = torch.empty_like(x[0])
+        L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+        tch.attn_prefill(*x, O, L, causal=1)
+        torch.cuda.synchronize()
+        refs.append((O, L))
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for r in range(6):
+        for k, s in enumerate(streams):
+            j = (k + r) % len(shapes)
+            B, Nq, Nkv, S, Dh = shapes[j]
+            O = torch.empty_like(inputs[j][0])
+            L = torch.empty((B, Nq, S), dtype=torch.float32, device=dev)
+            with torch.cuda.stream(s):
+                O.fill_(float("nan"))
+                tch.attn_prefill(*inputs[j], O, L, causal=1)
+            outs.append((j, O, L))
+    torch.cuda.synchronize()
+    for n, (j, O, L) in enumerate(outs):
+        assert _same(O, refs[j][0]) and torch.equal(L, refs[j][1]), (n, j)
