@@ -746,10 +746,12 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecParams p) {
     const int h = row % p.Nq;
     if constexpr (EV) {
       // a segment with visible keys was taken by ranges wf .. wl, which the
-      // partial kernel recorded
+      // partial kernel recorded.  The record is read together with the
+      // length, not after it (one memory round trip fewer); a segment without
+      // visible keys has no record, and its stale words are not used.
+      const int2 fl =*reinterpret_cast<const int2*>(p.ws_seg + 2 * ((size_t)b * p.Nkv + h / G));
       const int n = max(0, min(p.lens[b], p.Tcap));
       if (n > 0) {
-        const int2 fl = *reinterpret_cast<const int2*>(p.ws_seg + 2 * ((size_t)b * p.Nkv + h / G));
         ns = fl.y - fl.x + 1;
         part0 = ((size_t)b * p.Nkv + h / G + fl.x) * G + h % G;  // slot x: part0 + x*G
       }
