@@ -771,6 +771,43 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
     m_run[0] = M;
   }
 
+  // Epilogue through LDS (head size 128, and head size 64 with a key mask):
+  // every wave is done with the stages once all pass this barrier, and each
+  // live wave then stages its 32 output rows there (wave w: half w % 2 of
+  // stage w / 2) in the tiles' swizzled layout, so that it stores them as
+  // whole 16-byte chunks of consecutive rows instead of 8-byte pieces of 32
+  // rows at a time.  The unmasked head-size-64 form would spill at its
+  // register bound with it, and at head size 256 (one workgroup per CU) the
+  // barrier costs more than the wider stores gain.
+  if constexpr (!SK && QB == 1 && (D == 128 || (D == 64 && KM))) {
+    __syncthreads();
+    if (!wave_live) return;
+    char* const stage = w_all < 2 ? k0s : w_all < 4 ? k1s : w_all < 6 ? v0s : v1s;
+    char* const ob = stage + (w_all & 1) * (TILE / 2);
+    const float l_tot = xhalf_sum(l_run[0]);
+    const float inv = (KM && l_tot == 0.f) ? 0.f : 1.f / l_tot;
+    const int zr = swz<D>(ln);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        u32x2 st;
+        st[0] = pack_bf16x2(oacc[0][db][a4 * 4 + 0] * inv, oacc[0][db][a4 * 4 + 1] * inv);
+        st[1] = pack_bf16x2(oacc[0][db][a4 * 4 + 2] * inv, oacc[0][db][a4 * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(ob + ln * geo::RB + (((db * 4 + a4) ^ zr) << 4) + hl * 8) = st;
+      }
+    constexpr int RPI = 1024 / geo::RB;  // rows per 16-byte-per-lane instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / geo::NC, c = lane % geo::NC;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * geo::RB + ((c ^ swz<D>(r)) << 4));
+      if (qa_row + r < p.S) *reinterpret_cast<u32x4*>(p.O + q_base + (size_t)(qa_row + r) * D + c * 8) = v;
+    }
+    const int qi = qa_row + ln;
+    if (p.LSE != nullptr && hl == 0 && qi < p.S)
+      p.LSE[((size_t)b * p.Nq + head) * p.S + qi] = (m_run[0] + __log2f(l_tot)) * kLn2;
+    return;
+  }
   if (!wave_live) return;
   // epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
 #pragma unroll
