@@ -142,6 +142,7 @@ def test_prefill_cache_rope(dtype, B, Nq, Nkv, Sq, Dh, Tcap, lens, window, style
     ("bf16", 2, 16, 2, 64, 1500, [1500, 700], 300, "pairs", False, False),
     ("bf16", 2, 8, 2, 256, 1200, [1200, 333], 0, "half", True, False),
     ("bf16", 3, 16, 4, 128, 2000, [2000, 1000, 37], 0, "half", False, True),     # key mask
+    ("bf16", 64, 32, 8, 128, 2048, None, 0, "pairs", True, True),   # key mask, even split
     ("f32", 2, 8, 2, 64, 400, [400, 17], 0, "half", True, False),                 # general
 ])
 def test_decode_rope(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, style, explicit, padded):

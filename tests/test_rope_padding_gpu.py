@@ -215,6 +215,22 @@ def test_prefill_cache_padded(B, Nq, Nkv, Sq, Tcap, lens, window, pads, holes):
     say(f"prefill_cache padded Sq={Sq} dead rows {n_dead}: {errs}")
 
 
+def _takes_even_split(B, Nq, Nkv, Dh, Tcap, window):
+    # The even split's workspace ends in two int32 per (sequence, K/V head)
+    # after the fp32 partials of G (Dh + 2) floats per slot; the chunked form
+    # has the partials only.  With a key mask it also needs every wavefront's
+    # range to fit its 1024 staged flag words: at most B*Nkv*(L/32+2)*64/C(W)
+    # steps, far below that for these shapes.
+    G = Nq // Nkv
+    ws = tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, tch.ATTN_BF16)
+    per_slot = G * (Dh + 2) * 4
+    ev = (ws - B * Nkv * 8) % per_slot == 0 and ws % per_slot != 0
+    L = window if 0 < window < Tcap else Tcap
+    W = 512 if G >= 16 else 1024
+    cw = 64 * ((W + 1) // 2) + 55 * (W // 2)
+    return ev and B * Nkv * ((L + 31) // 32 + 1) * 64 // cw + 3 <= 1022
+
+
 class _Lazy:
     def __init__(self, arr, dtype):
         self.arr, self.dtype, self.shape = arr, dtype, arr.shape
@@ -231,6 +247,13 @@ class _Lazy:
     ("bf16", 3, 32, 1, 128, 2100, [1024, 1025, 2048], 0, [0, 1000, 0], 0.3, None),  # MQA
     ("bf16", 3, 4, 2, 256, 700, [700, 17, 250], 40, [0, 20, 220], 0.2, None),
     ("f32", 3, 4, 2, 64, 400, [400, 17, 250], 40, [0, 20, 100], 0.2, None),         # general
+    # grids large enough for the even split (ranges of steps over all sequences,
+    # the mask's flag words staged per piece); one sequence sees padding only
+    ("bf16", 64, 32, 8, 128, 4096, None, 0, [(37 * i) % 900 for i in range(63)] + [4096], 0.1,
+     None),
+    ("bf16", 32, 32, 1, 128, 8192, None, 0, [(101 * i) % 2500 for i in range(32)], 0.2, None),
+    ("bf16", 48, 16, 4, 64, 6000, None, 0, [(53 * i) % 1200 for i in range(48)], 0.1, None),
+    ("bf16", 64, 8, 8, 128, 8192, None, 3000, [(71 * i) % 4000 for i in range(64)], 0.3, None),
 ])
 def test_decode_padded(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, pads, holes, block):
     dev = device()
@@ -238,6 +261,8 @@ def test_decode_padded(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, pads, holes, b
                                                 lens=lens)
     m = workloads.key_mask(B, Tcap, pads=pads, hole_frac=holes, seed=Tcap, block=block)
     tq, tk, tv = (workloads.to_torch(a, dtype, dev) for a in (q, kc, vc))
+    if B >= 32:
+        assert _takes_even_split(B, Nq, Nkv, Dh, Tcap, window)
     O, L = tch.decode(tq, tk, tv, torch.from_numpy(lens_a).to(dev), window=window,
                       key_mask=torch.from_numpy(m).to(dev))
     torch.cuda.synchronize()

@@ -37,10 +37,11 @@
 //     ds_read_b64_tr_b16; row-XOR swizzles keep both conflict free.  More than
 //     16 query heads per K/V head (up to 32: MQA) take a second N block that
 //     reuses every K and V fragment.
-//   * Even split (small grids: at most 64 sequences and few chunk items): the
-//     visible steps of all (sequence, K/V head) pairs are laid end to end and
-//     cut into equal ranges, one per wavefront of a fixed grid of 1280 (five
-//     per CU).  Per-sequence chunks leave a grid of mixed-length items (every
+//   * Even split (at most 64 sequences, grids of at least 512 chunk items):
+//     the visible steps of all (sequence, K/V head) pairs are laid end to end
+//     and cut into ranges, one per wavefront of a fixed grid of 1024 (four per
+//     CU; 512 with 16 or more query heads per K/V head), weighted by XCD
+//     parity.  Per-sequence chunks leave a grid of mixed-length items (every
 //     sequence's last chunk is short, sequences end at different chunks) that
 //     the dispatcher spreads unevenly when they all run at once; equal ranges
 //     finish together.  A range crossing a (sequence, K/V head) boundary
@@ -80,6 +81,11 @@ constexpr int kMergeBatch = 16;
 // write and merge than their extra parallelism gains
 constexpr int kFloorKeys = 640;
 constexpr int kFloorKeysWide = 224;
+// even split with a key-padding mask: the 32-key flag words of a piece's steps
+// are copied into LDS when the piece starts (4 KB per wavefront), so a piece
+// spans at most kMaskWords - 2 steps; the host takes the even split only when
+// every range fits
+constexpr int kMaskWords = 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -216,7 +222,6 @@ __device__ __forceinline__ void wait_vm() {
 // (sequence, K/V head) pairs laid end to end); chunk mode otherwise.
 template <int D, int NB, bool KM, bool APP = false, bool RQ = false, bool EV = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
-  static_assert(!EV || !KM, "even split: no key-padding mask");
   using geo = DGeo<D>;
   constexpr int STAGE = geo::STAGE;
   constexpr int KS = geo::KS;
@@ -228,6 +233,9 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   __shared__ __attribute__((aligned(1024))) char k1s[STAGE];
   __shared__ __attribute__((aligned(1024))) char v0s[STAGE];
   __shared__ __attribute__((aligned(1024))) char v1s[STAGE];
+  // even split with a key mask: flag word of step s at kwl[s - kw_base]
+  __shared__ __attribute__((aligned(16))) uint32_t kwl[(KM && EV) ? kMaskWords : 1];
+  int kw_base = 0;
 
   lds_char* const K0 = (lds_char*)k0s;
   lds_char* const K1 = (lds_char*)k1s;
@@ -299,6 +307,18 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       if (s_in + cnt == ns_b) seg[1] = ev_w;
     }
     load_new(s0 * STEP, nsteps * STEP);
+    if constexpr (KM) {
+      // flag words of steps s0 .. nsteps-1 (two per 64-bit mask word, starting
+      // at an even step), 64 lanes x 4 bytes per copy; words past the
+      // sequence's mask read as zero
+      kw_base = s0 & ~1;
+      const int nw = min(nsteps - kw_base, kMaskWords);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.kbits + (size_t)b * p.kwords), (short)0, p.kwords * 8, 0x00020000);
+      for (int i = 0; i < nw; i += 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kwl + i), 4, (kw_base + i + lane) * 4, 0,
+                                                 0, 0);
+    }
   };
   if constexpr (EV) {
     tab = even_table(p, lane);
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
   // has at most 64 steps), read in the loop with v_readlane
   const int s_flags = s0;
   uint32_t kw_lane = 0;
-  if constexpr (KM) {
+  if constexpr (KM && !EV) {
     // drop the leading and trailing steps whose 32 keys are all padding, so
     // they are neither copied nor waited for; the ballot gives the ends
     const int s = s0 + lane;
@@ -580,7 +600,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecParams p) {
       // keys only changes nothing
       uint32_t kw = ~0u;
       if constexpr (KM) {
-        kw = __builtin_amdgcn_readlane(kw_lane, s - s_flags);
+        if constexpr (EV)
+          kw = __builtin_amdgcn_readfirstlane(kwl[min(s - kw_base, kMaskWords - 1)]);
+        else
+          kw = __builtin_amdgcn_readlane(kw_lane, s - s_flags);
         if (kw == 0) return;
       }
 #pragma unroll
@@ -936,9 +959,15 @@ hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
     }
     return launch_decode_km<D, NB, false, true>(p, stream);
   }
-  if (p.kbits)
+  if (p.kbits) {
+    if constexpr (D <= 128) {
+      if (p.ev_nw)
+        return p.rope.table ? launch_decode_km<D, NB, true, false, true, true>(p, stream)
+                            : launch_decode_km<D, NB, true, false, false, true>(p, stream);
+    }
     return p.rope.table ? launch_decode_km<D, NB, true, false, true>(p, stream)
                         : launch_decode_km<D, NB, true>(p, stream);
+  }
   if constexpr (D <= 128) {
     if (p.ev_nw)
       return p.rope.table ? launch_decode_km<D, NB, false, false, true, true>(p, stream)
@@ -986,8 +1015,18 @@ hipError_t launch_decode_bf16(const void* q, const void* Kc, const void* Vc, con
   p.ch = d.ch;
   p.n_slots = d.n_slots;
   // the even split at head size 256 only in its plain form (the rotating and
-  // appending forms spill there)
-  const bool ev = d.ev && kbits == nullptr && (Dh <= 128 || (rope == nullptr && knew == nullptr));
+  // appending forms spill there); with a key mask at head sizes up to 128, when
+  // every wavefront's range fits the flag words a wavefront holds in LDS (a
+  // range is at most tot * 64 / C(W) + 1 steps, tot counting every step of
+  // every (sequence, K/V head) pair up to the visible span)
+  bool ev = d.ev && (Dh <= 128 || (rope == nullptr && knew == nullptr && kbits == nullptr));
+  if (ev && kbits != nullptr) {
+    const int nw = Nq / Nkv >= 16 ? kEvenWavesWide : kEvenWaves;
+    const int L = (window > 0 && window < Tcap) ? window : Tcap;
+    const long long tot = (long long)B * Nkv * ((L + STEP - 1) / STEP + 1);
+    const long long cw = kWeightEven * ((nw + 1) / 2) + kWeightOdd * (nw / 2);
+    ev = tot * kWeightEven / cw + 3 <= kMaskWords - 2;
+  }
   p.ev_nw = ev ? (p.G >= 16 ? kEvenWavesWide : kEvenWaves) : 0;
   p.ev_min = (p.G >= 16 ? kFloorKeysWide : kFloorKeys) / STEP;
   p.mw = ev ? d.ev_mw : d.mw;
