@@ -772,18 +772,24 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && NW == 4) ? 2 : ((D == 64 && N
   }
 
   // Epilogue through LDS (head size 128, and head size 64 with a key mask):
-  // every wave is done with the stages once all pass this barrier, and each
-  // live wave then stages its 32 output rows there (wave w: half w % 2 of
-  // stage w / 2) in the tiles' swizzled layout, so that it stores them as
-  // whole 16-byte chunks of consecutive rows instead of 8-byte pieces of 32
-  // rows at a time.  The unmasked head-size-64 form would spill at its
-  // register bound with it, and at head size 256 (one workgroup per CU) the
-  // barrier costs more than the wider stores gain.
-  if constexpr (!SK && QB == 1 && (D == 128 || (D == 64 && KM))) {
-    __syncthreads();
+  // each live wave stages its 32 output rows in LDS in the tiles' swizzled
+  // layout, so that it stores them as whole 16-byte chunks of consecutive
+  // rows instead of 8-byte pieces of 32 rows at a time.  Without a key split
+  // every wave is done with the stages once all pass a barrier, and wave w
+  // takes half w % 2 of stage w / 2; with one, each query wave reuses its own
+  // merge buffer, which no other wave reads.  The unmasked head-size-64 form
+  // would spill at its register bound with it, and at head size 256 (one
+  // workgroup per CU) the barrier costs more than the wider stores gain.
+  if constexpr (QB == 1 && (D == 128 || (D == 64 && KM))) {
+    char* ob;
+    if constexpr (SK) {
+      ob = (w < 2 ? k0s : k1s) + (w & 1) * TILE;
+    } else {
+      __syncthreads();
+      char* const stage = w_all < 2 ? k0s : w_all < 4 ? k1s : w_all < 6 ? v0s : v1s;
+      ob = stage + (w_all & 1) * (TILE / 2);
+    }
     if (!wave_live) return;
-    char* const stage = w_all < 2 ? k0s : w_all < 4 ? k1s : w_all < 6 ? v0s : v1s;
-    char* const ob = stage + (w_all & 1) * (TILE / 2);
     const float l_tot = xhalf_sum(l_run[0]);
     const float inv = (KM && l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const int zr = swz<D>(ln);
