@@ -49,9 +49,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # FETCH_SIZE unit = 2047.9 bytes, one WRITE_SIZE unit = 1024 bytes); valid only
 # for the kernel source it was taken on (sha256[:16] of the .hip file).
 TRAFFIC = {
-    "prefill_bf16.hip": {"adf083e7a5d1248c": 3522252553},  # 3.250e+09 fetched + 2.727e+08 written
+    "prefill_bf16.hip": {"64e736153821d8b4": 3553643950},  # 3.281e+09 fetched + 2.727e+08 written
     # partial + merge kernels
-    "decode_bf16.hip": {"10b5908f1eec1680": 4520653941},   # 4.517e+09 fetched + 3.789e+06 written
+    "decode_bf16.hip": {"10b5908f1eec1680": 4520626259},   # 4.517e+09 fetched + 3.792e+06 written
 }
 
 
