@@ -21,7 +21,13 @@ from helpers import device, say
 pytestmark = pytest.mark.gpu
 
 BF16_REL = 1.6e-2   # per element: |err| <= BF16_REL * (1 + |ref|)
-BF16_MEAN = 1e-3
+# on average: mean |err| <= BF16_MEAN_REL * mean |ref| + BF16_MEAN_FLOOR.  The
+# bf16 roundings the backward's arithmetic requires (stored O, the P and dS
+# operands, the stored gradients) give a mean error of 2.3-2.8e-3 of mean |ref|
+# on every emulated shape, short or long (test_backward_tolerance.py), so the
+# bound scales with the gradients' size: twice 2^-8 of it, plus a floor
+BF16_MEAN_REL = 2.0 ** -7
+BF16_MEAN_FLOOR = 1e-4
 F32_REL = 1e-4
 
 
@@ -45,7 +51,8 @@ def _check(got, ref, dtype, what):
             f"{what} {name}: err {err.flat[worst]:.3g} at {np.unravel_index(worst, err.shape)} "
             f"ref {r.flat[worst]:.3g}")
         if dtype == "bf16":
-            assert err.mean() <= BF16_MEAN, f"{what} {name}: mean err {err.mean():.3g}"
+            bound = BF16_MEAN_REL * np.abs(r).mean() + BF16_MEAN_FLOOR
+            assert err.mean() <= bound, f"{what} {name}: mean err {err.mean():.3g} > {bound:.3g}"
         out.append(f"{name} {err.max():.2e}/{err.mean():.2e}")
     say(f"backward {what}: " + " ".join(out))
 
@@ -70,6 +77,8 @@ def _inputs(B, Nq, Nkv, S, Dh, dtype, seed):
     (1, 4, 4, 300, 256, True, 0),       # ragged, several key blocks
     (1, 8, 2, 257, 256, True, 0),       # GQA 4
     (1, 4, 1, 129, 256, False, 0),      # MQA, non-causal
+    (2, 8, 4, 4, 128, False, 0),        # 4 tokens: gradients of order 1, mean error scales with them
+    (2, 8, 2, 16, 64, False, 0),
 ])
 def test_backward_bf16(B, Nq, Nkv, S, Dh, causal, window):
     q, k, v, dO = _inputs(B, Nq, Nkv, S, Dh, "bf16", seed=S + Dh)

@@ -7,8 +7,11 @@ MFMA products take P and dS = P (dP - Delta) as bf16 operands; dQ, dK, dV are
 stored in bf16.  This test applies exactly those roundings, in float64, to the
 oracle's own forward and backward quantities and checks that the result stays
 within half of the bound the GPU parity test uses (|err| <= BF16_REL (1 + |ref|),
-mean <= BF16_MEAN), leaving the other half for fp32 accumulation order and the
-fp32 exponentials of the kernels.
+mean |err| <= BF16_MEAN_REL mean |ref| + BF16_MEAN_FLOOR), leaving the other
+half for fp32 accumulation order and the fp32 exponentials of the kernels.
+The emulated mean error is 2.3-2.8e-3 of mean |ref| on long and short shapes
+alike, so the mean bound scales with the gradients' size; the short
+non-causal shapes below have gradients several times larger than the long ones.
 """
 
 import numpy as np
@@ -16,27 +19,29 @@ import pytest
 
 import oracle
 import workloads
-from test_backward_gpu import BF16_MEAN, BF16_REL
+from test_backward_gpu import BF16_MEAN_FLOOR, BF16_MEAN_REL, BF16_REL
 
 
 def _bf16(x):
     return workloads.to_f64(workloads.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)), "bf16")
 
 
-@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window,seed", [
-    (1, 4, 2, 300, 128, 0, 1),
-    (1, 2, 2, 257, 64, 100, 2),
+@pytest.mark.parametrize("B,Nq,Nkv,S,Dh,window,causal,seed", [
+    (1, 4, 2, 300, 128, 0, True, 1),
+    (1, 2, 2, 257, 64, 100, True, 2),
+    (2, 8, 4, 4, 128, 0, False, 712),
+    (2, 8, 2, 16, 64, 0, False, 9),
 ])
-def test_emulated_roundings_fit_half_the_bound(B, Nq, Nkv, S, Dh, window, seed):
+def test_emulated_roundings_fit_half_the_bound(B, Nq, Nkv, S, Dh, window, causal, seed):
     q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=seed)
     Q, K, V = (workloads.to_f64(a, "bf16") for a in (q, k, v))
     dO = workloads.to_f64(workloads.draw((B, Nq, S, Dh), "bf16", seed, 3), "bf16")
-    dQ, dK, dV = oracle.backward_ref(Q, K, V, dO, causal=True, window=window)
-    O, L = oracle.attention_ref(Q, K, V, causal=True, window=window)
+    dQ, dK, dV = oracle.backward_ref(Q, K, V, dO, causal=causal, window=window)
+    O, L = oracle.attention_ref(Q, K, V, causal=causal, window=window)
     O_stored = _bf16(O)
     scale = 1.0 / np.sqrt(Dh)
     G = Nq // Nkv
-    ok = oracle.allowed_mask(np.arange(S), S, True, window)
+    ok = oracle.allowed_mask(np.arange(S), S, causal, window)
     eQ, eK, eV = np.zeros_like(dQ), np.zeros_like(dK), np.zeros_like(dV)
     for b in range(B):
         for h in range(Nq):
@@ -51,4 +56,5 @@ def test_emulated_roundings_fit_half_the_bound(B, Nq, Nkv, S, Dh, window, seed):
     for name, e, r in (("dQ", eQ, dQ), ("dK", eK, dK), ("dV", eV, dV)):
         err = np.abs(_bf16(e) - r)
         assert np.all(err <= 0.5 * BF16_REL * (1 + np.abs(r))), (name, float(np.max(err / (1 + np.abs(r)))))
-        assert err.mean() <= 0.5 * BF16_MEAN, (name, float(err.mean()))
+        assert err.mean() <= 0.5 * (BF16_MEAN_REL * np.abs(r).mean() + BF16_MEAN_FLOOR), (
+            name, float(err.mean()), float(np.abs(r).mean()))
