@@ -4,9 +4,11 @@ test_random_shapes_gpu.py draws small shapes, whose grids fit the chip once.
 These cases draw shapes whose prefill grids run several rounds (the 8-wave
 forms, the run-time drawn tail, ragged last tiles, key-padding masks) and
 decode batches large enough for the even split (with masks and windows), from a
-fixed seed.  The prefill is checked on seeded sampled rows (plus forced rows at
-the ends and at tile boundaries) against the oracle's single-row attention, the
-decode on every row; rows that see no key must be exactly O = 0, LSE = -inf.
+fixed seed, and backward passes of 1000-9000 tokens (several key blocks and
+query tiles per head, windows, key padding).  The prefill is checked on seeded
+sampled rows (plus forced rows at the ends and at tile boundaries) against the
+oracle's single-row attention, the decode on every row (rows that see no key
+must be exactly O = 0, LSE = -inf), the backward on sampled gradient rows.
 """
 
 import numpy as np
@@ -17,6 +19,7 @@ import oracle
 import transformer_causal_head_amd as tch
 import workloads
 from helpers import check, device, say
+from test_backward_gpu import BF16_REL
 from test_rope_padding_gpu import _split_dead
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +130,61 @@ def test_large_decode(i, B, Nq, Nkv, Dh, Tcap, window, pad):
     what = (i, B, Nq, Nkv, Dh, Tcap, window, pad)
     errs = check(Og[live], Lg[live], Or[live], Lr[live], "bf16", what, storage_allowance=True)
     say(f"large decode {what}: {errs}, {n_dead} rows without keys")
+
+
+def _backward_cases(n):
+    cases = []
+    for i in range(n):
+        Nkv = _pick([1, 2, 4, 8])
+        G = _pick([1, 2, 4])
+        Dh = _pick([64, 128, 128, 256])
+        B = int(_rng.integers(1, 3))
+        S = int(_rng.integers(1000, 9000))
+        while B * Nkv * G * S * Dh > 40 * 2 ** 20:
+            S //= 2
+        causal = bool(_rng.random() < 0.85)
+        window = int(_rng.integers(1, S + 65)) if (causal and _rng.random() < 0.3) else 0
+        pad = bool(_rng.random() < 0.25)
+        cases.append((i, B, Nkv * G, Nkv, S, Dh, causal, window, pad))
+    return cases
+
+
+@pytest.mark.parametrize("i,B,Nq,Nkv,S,Dh,causal,window,pad", _backward_cases(12))
+def test_large_backward(i, B, Nq, Nkv, S, Dh, causal, window, pad):
+    # sampled dQ rows (plus rows 0, S/2 and S-1) and the dK / dV rows of keys
+    # near the end (each seen by few queries) or, without a plain causal mask,
+    # anywhere; each row held to the backward's bound against its own scale,
+    # as the full-size backward test does
+    dev = device()
+    q, k, v = workloads.prefill_inputs(B, Nq, Nkv, S, Dh, "bf16", seed=3000 + i)
+    dO = workloads.draw((B, Nq, S, Dh), "bf16", 3000 + i, 3)
+    tq, tk, tv, tdo = (workloads.to_torch(x, "bf16", dev) for x in (q, k, v, dO))
+    m, km = None, None
+    if pad:
+        pads = [int(x) for x in np.random.default_rng(i).integers(0, S // 2, B)]
+        m = workloads.key_mask(B, S, pads=pads, hole_frac=0.1, seed=i)
+        km = torch.from_numpy(m).to(dev)
+    O, L = tch.prefill(tq, tk, tv, causal=causal, window=window, key_mask=km)
+    dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo, causal=causal, window=window, key_mask=km)
+    torch.cuda.synchronize()
+    qr = workloads.sample_rows(B, Nq, S, 12, seed=i, forced_rows=(0, S - 1, S // 2))
+    rng = np.random.default_rng(i + 7)
+    kr = [(int(rng.integers(0, B)), int(rng.integers(0, Nkv)), j) for j in (S - 1, S - 33, S - 100, S - 129)]
+    if not causal or window:
+        kr.append((0, 0, int(rng.integers(0, S))))
+    idx = lambda rows: tuple(torch.tensor(c, device=dev) for c in zip(*rows))
+    got = [workloads.to_f64(workloads.from_torch(t[idx(r)], "bf16"), "bf16")
+           for t, r in ((dQ, qr), (dK, kr), (dV, kr))]
+    del tq, tk, tv, tdo, O, L, dQ, dK, dV
+    ref = oracle.backward_rows_ref(_Lazy(q), _Lazy(k), _Lazy(v), _Lazy(dO), qr, kr, causal=causal,
+                                   window=window, key_mask=m)
+    what = (i, B, Nq, Nkv, S, Dh, causal, window, pad)
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        scale_row = np.maximum(np.abs(r).max(axis=1, keepdims=True), 1e-2 * np.abs(r).max())
+        scale_row = np.where(scale_row > 0, scale_row, 1.0)  # rows whose exact gradient is 0
+        ratio = np.abs(g - r) / scale_row
+        assert np.all(ratio <= BF16_REL), f"{what} {name}: worst row-relative error {ratio.max():.3g}"
+        out.append(f"{name} {ratio.max():.2e}")
+    say(f"large backward {what}, row-relative: " + " ".join(out))
