@@ -72,3 +72,20 @@ def run_decode(q, kc, vc, lens, dtype):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def takes_even_split(B, Nq, Nkv, Dh, Tcap, window):
+    # Whether a bf16 decode of this shape takes the even split.  Its workspace
+    # ends in two int32 per (sequence, K/V head) after the fp32 partials of
+    # G (Dh + 2) floats per slot; the chunked form has the partials only.  With
+    # a key mask the library also needs every wavefront's range to fit the 1024
+    # flag words it stages (at most B*Nkv*(L/32+1)*64/C(W) + 3 steps), which is
+    # checked here for every shape.
+    G = Nq // Nkv
+    ws = tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, tch.ATTN_BF16)
+    per_slot = G * (Dh + 2) * 4
+    ev = (ws - B * Nkv * 8) % per_slot == 0 and ws % per_slot != 0
+    L = window if 0 < window < Tcap else Tcap
+    W = 512 if G >= 16 else 1024
+    cw = 64 * ((W + 1) // 2) + 55 * (W // 2)
+    return ev and B * Nkv * ((L + 31) // 32 + 1) * 64 // cw + 3 <= 1022

@@ -11,7 +11,7 @@ import torch
 import oracle
 import transformer_causal_head_amd as tch
 import workloads
-from helpers import check, device, say
+from helpers import check, device, say, takes_even_split
 
 pytestmark = pytest.mark.gpu
 
@@ -206,12 +206,19 @@ def test_generation_over_window_cache(mode):
     ("bf16", 5, 32, 8, 128, 700, [700, 700, 350, 1, 699], 0, True, False),  # rolling buffer
     ("bf16", 3, 8, 2, 128, 600, [600, 17, 250], 40, False, True),           # unaligned new rows
     ("f32", 3, 4, 2, 64, 400, [400, 17, 250], 40, False, False),            # general kernels
+    # batches that take the even split (asserted through the workspace layout)
+    ("bf16", 64, 32, 8, 128, 4096, None, 0, False, False),
+    ("bf16", 64, 16, 8, 64, 8192, None, 2000, False, False),                # window
+    ("bf16", 64, 32, 8, 128, 2048, None, 0, True, False),                   # rolling buffer
+    ("bf16", 32, 32, 1, 128, 6000, None, 0, False, True),                   # MQA, unaligned rows
 ])
 def test_decode_append(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, rolling, unaligned):
     # one decode step whose new K/V rows are appended in the same call: the
     # cache must equal the oracle's append, and O / LSE must be bit-identical
     # to attn_kv_append followed by the decode, and match the oracle
     dev = device()
+    if B >= 32:
+        assert takes_even_split(B, Nq, Nkv, Dh, Tcap, window)
     if rolling:   # a full buffer: every slot holds a key
         lens = [Tcap] * B
     lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, dtype, seed=Dh,

@@ -19,7 +19,7 @@ import torch
 import oracle
 import transformer_causal_head_amd as tch
 import workloads
-from helpers import check, device, say
+from helpers import check, device, say, takes_even_split
 
 pytestmark = pytest.mark.gpu
 
@@ -215,22 +215,6 @@ def test_prefill_cache_padded(B, Nq, Nkv, Sq, Tcap, lens, window, pads, holes):
     say(f"prefill_cache padded Sq={Sq} dead rows {n_dead}: {errs}")
 
 
-def _takes_even_split(B, Nq, Nkv, Dh, Tcap, window):
-    # The even split's workspace ends in two int32 per (sequence, K/V head)
-    # after the fp32 partials of G (Dh + 2) floats per slot; the chunked form
-    # has the partials only.  With a key mask it also needs every wavefront's
-    # range to fit its 1024 staged flag words: at most B*Nkv*(L/32+2)*64/C(W)
-    # steps, far below that for these shapes.
-    G = Nq // Nkv
-    ws = tch.attn_decode_window_workspace_bytes(B, Nq, Nkv, Dh, Tcap, window, tch.ATTN_BF16)
-    per_slot = G * (Dh + 2) * 4
-    ev = (ws - B * Nkv * 8) % per_slot == 0 and ws % per_slot != 0
-    L = window if 0 < window < Tcap else Tcap
-    W = 512 if G >= 16 else 1024
-    cw = 64 * ((W + 1) // 2) + 55 * (W // 2)
-    return ev and B * Nkv * ((L + 31) // 32 + 1) * 64 // cw + 3 <= 1022
-
-
 class _Lazy:
     def __init__(self, arr, dtype):
         self.arr, self.dtype, self.shape = arr, dtype, arr.shape
@@ -262,7 +246,7 @@ def test_decode_padded(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, pads, holes, b
     m = workloads.key_mask(B, Tcap, pads=pads, hole_frac=holes, seed=Tcap, block=block)
     tq, tk, tv = (workloads.to_torch(a, dtype, dev) for a in (q, kc, vc))
     if B >= 32:
-        assert _takes_even_split(B, Nq, Nkv, Dh, Tcap, window)
+        assert takes_even_split(B, Nq, Nkv, Dh, Tcap, window)
     O, L = tch.decode(tq, tk, tv, torch.from_numpy(lens_a).to(dev), window=window,
                       key_mask=torch.from_numpy(m).to(dev))
     torch.cuda.synchronize()
