@@ -19,7 +19,7 @@ import torch
 import oracle
 import transformer_causal_head_amd as tch
 import workloads
-from helpers import check, device, say
+from helpers import check, device, say, takes_even_split
 
 pytestmark = pytest.mark.gpu
 
@@ -143,11 +143,15 @@ def test_prefill_cache_rope(dtype, B, Nq, Nkv, Sq, Dh, Tcap, lens, window, style
     ("bf16", 2, 8, 2, 256, 1200, [1200, 333], 0, "half", True, False),
     ("bf16", 3, 16, 4, 128, 2000, [2000, 1000, 37], 0, "half", False, True),     # key mask
     ("bf16", 64, 32, 8, 128, 2048, None, 0, "pairs", True, True),   # key mask, even split
+    ("bf16", 64, 32, 8, 128, 2048, None, 0, "half", False, False),  # even split
+    ("bf16", 32, 32, 1, 128, 4096, None, 0, "pairs", True, False),  # MQA, even split
     ("f32", 2, 8, 2, 64, 400, [400, 17], 0, "half", True, False),                 # general
 ])
 def test_decode_rope(dtype, B, Nq, Nkv, Dh, Tcap, lens, window, style, explicit, padded):
     dev = device()
     P = Tcap + 100
+    if B >= 32:
+        assert takes_even_split(B, Nq, Nkv, Dh, Tcap, window)
     lens_a, q, kc, vc = workloads.decode_inputs(B, Nq, Nkv, Dh, Tcap, 1, Tcap, dtype, seed=Dh + B,
                                                 lens=lens)
     tq, tk, tv = (workloads.to_torch(a, dtype, dev) for a in (q, kc, vc))
