@@ -53,6 +53,8 @@ def _t(a, dev):
     ("bf16", 1, 8, 8, 333, 128, True, 100, "half", "start"),
     ("bf16", 1, 8, 2, 300, 128, False, 0, "pairs", "start"),
     ("bf16", 1, 16, 16, 4096, 128, True, 0, "half", "implicit"),   # key-split form
+    ("bf16", 1, 32, 32, 8192, 128, True, 0, "pairs", "explicit"),  # four rounds, drawn tail
+    ("bf16", 2, 32, 8, 4096, 128, True, 1000, "half", "start"),    # GQA window, four rounds
     ("bf16", 2, 8, 8, 257, 64, True, 0, "pairs", "explicit"),
     ("bf16", 1, 8, 4, 300, 256, True, 0, "half", "implicit"),
     ("bf16", 1, 4, 2, 130, 80, True, 0, "half", "explicit"),       # general kernel
