@@ -53,6 +53,24 @@ def test_prefill_cache_bf16(B, Nq, Nkv, Sq, Tcap, lens, window):
         f"{check(O, L, Or, Lr, 'bf16', (Sq, lens, window), storage_allowance=True)}")
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("window", [0, 4096])
+def test_prefill_cache_full_size_sampled_rows(window):
+    # the chunk `bench.py --cache-paths` times: the last 2048 tokens of a
+    # 32768-token context, 32 query / 8 K/V heads, on seeded sampled rows plus
+    # the chunk's first and last rows, against the oracle's chunk attention
+    B, Nq, Nkv, Sq, Dh, Tcap = 1, 32, 8, 2048, 128, 32768
+    lens_a, Q, kc, vc = workloads.chunk_inputs(B, Nq, Nkv, Sq, Dh, Tcap, [Tcap], "bf16", seed=5)
+    O, L = _run_chunk(Q, kc, vc, lens_a, "bf16", window)
+    rows = workloads.sample_rows(B, Nq, Sq, 64, seed=11, forced_rows=(0, 1, Sq // 2, Sq - 1))
+    Or, Lr = oracle.chunk_ref(_Lazy(Q, "bf16"), _Lazy(kc, "bf16"), _Lazy(vc, "bf16"), lens_a,
+                              window=window, rows=rows)
+    Og = np.stack([O[b, h, i] for b, h, i in rows])
+    Lg = np.array([L[b, h, i] for b, h, i in rows])
+    say(f"prefill_cache full size window={window}: "
+        f"{check(Og, Lg, Or, Lr, 'bf16', ('chunk 2048 of 32768', window), storage_allowance=True)}")
+
+
 @pytest.mark.parametrize("Dh,dtype,window", [(64, "f32", 0), (80, "bf16", 9), (128, "f32", 20),
                                               (64, "bf16", 0), (256, "bf16", 30)])
 def test_prefill_cache_other_head_sizes(Dh, dtype, window):
