@@ -6,6 +6,7 @@ import math
 import numpy as np
 import torch
 
+import oracle
 import transformer_causal_head_amd as tch
 import workloads
 
@@ -89,3 +90,54 @@ def takes_even_split(B, Nq, Nkv, Dh, Tcap, window):
     W = 512 if G >= 16 else 1024
     cw = 64 * ((W + 1) // 2) + 55 * (W // 2)
     return ev and B * Nkv * ((L + 31) // 32 + 1) * 64 // cw + 3 <= 1022
+
+
+def set_oracle_rows(O, LSE, Q, K, V, dO, q_rows, causal=True, window=0, key_mask=None):
+    """Give the sampled query rows the oracle's forward output before a backward.
+
+    A row's dQ depends on its own O and LSE (and on K, V): the backward forms
+    P_i from LSE_i and Delta_i = rowsum(dO_i * O_i) from O_i as stored.  This
+    writes the oracle's O_i (rounded to bf16 from fp32, as the forward stores
+    it) and LSE_i into the device tensors O, LSE, so that those rows' gradient
+    is fixed by oracle values alone.  It returns, per row, what that rounding
+    of O does to the oracle's dQ_i: Delta_i moves by
+    dDelta_i = dO_i . (bf16(O_i) - O_i), every dS_ij = P_ij (dP_ij - Delta_i)
+    by -P_ij dDelta_i, so dQ_i = scale * sum_j dS_ij K_j moves by
+    -scale * dDelta_i * sum_j P_ij K_j.  In a row whose weight sits mostly on
+    one key the gradient is small while Delta is not; at head size 256 that
+    shift reaches 3 % of such a row's largest element.  Q, K, V, dO may be
+    lazily widened arrays.  Returns [len(q_rows), Dh], to add to the oracle's
+    dQ rows.
+    """
+    Nq, Dh = Q.shape[1], Q.shape[3]
+    Nkv = K.shape[1]
+    scale = 1.0 / math.sqrt(Dh)
+    heads = {}
+    shift = np.empty((len(q_rows), Dh))
+    o_rows = np.empty((len(q_rows), Dh), dtype=np.float32)
+    lse_rows = np.empty(len(q_rows), dtype=np.float32)
+    for t, (b, h, i) in enumerate(q_rows):
+        g = oracle.kv_head_of(h, Nq, Nkv)
+        if (b, g) not in heads:
+            heads[(b, g)] = (np.asarray(K[b, g], dtype=np.float64), np.asarray(V[b, g], dtype=np.float64))
+        Kb, Vb = heads[(b, g)]
+        o, lse, P = oracle.head_attention(np.asarray(Q[b, h, i], dtype=np.float64)[None, :], [i], Kb, Vb,
+                                          causal, window, scale, return_probs=True,
+                                          key_ok=None if key_mask is None else key_mask[b])
+        o_rows[t], lse_rows[t] = o[0], lse[0]
+        o_stored = workloads.to_f64(workloads.f32_to_bf16_bits(o_rows[t]), "bf16")
+        d_delta = np.dot(np.asarray(dO[b, h, i], dtype=np.float64), o_stored - o[0])
+        shift[t] = -scale * d_delta * (P[0] @ Kb)
+    idx = tuple(torch.tensor(c, device=O.device) for c in zip(*q_rows))
+    O[idx] = torch.from_numpy(o_rows).to(O.device).to(O.dtype)
+    LSE[idx] = torch.from_numpy(lse_rows).to(LSE.device)
+    return shift
+
+
+def grad_rows_ratio(g, r):
+    """Row-relative error of sampled gradient rows: |g - r| over the row's
+    largest |r|, floored at 1 % of the largest sampled element (and 1 for rows
+    whose exact gradient is 0)."""
+    scale_row = np.maximum(np.abs(r).max(axis=1, keepdims=True), 1e-2 * np.abs(r).max())
+    scale_row = np.where(scale_row > 0, scale_row, 1.0)
+    return np.abs(g - r) / scale_row
