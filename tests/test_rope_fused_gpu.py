@@ -3,7 +3,10 @@ and attn_decode_rope rotate the queries as they load them.
 
 Each fused call must give the same bits as the two passes it replaces (attn_rope
 on q, then the unrotated call on the rotated q), since the kernels compute the
-rotation with the same fp32 arithmetic and the same single rounding; and it
+rotation with the same fp32 arithmetic and the same single rounding, where both
+take the same launch form (at head size 256 an unrotated decode large enough
+for the even split takes it, while the rotating decode keeps chunk mode, whose
+accumulation order differs; no case here is of that kind); and it
 must match the oracle (oracle.rope_ref on q and k, rounded to the stored type,
 then the attention oracle) at the stated tolerance.  Keys are rotated before
 the call, by attn_rope or by the rotating cache append, as the page's layer
