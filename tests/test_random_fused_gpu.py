@@ -1,6 +1,6 @@
 """Seeded random shapes for the fused calls: each against the two calls it replaces.
 
-attn_prefill_rope, attn_decode_rope and attn_decode_append on shapes drawn
+attn_prefill_rope, attn_prefill_cache_rope, attn_decode_rope and attn_decode_append on shapes drawn
 from a fixed seed (head sizes 64-256, groups to 32, batches to 64, windows,
 key-padding masks, every position mode, both rotation layouts), each compared
 with attn_rope followed by the unrotated call, or with attn_kv_append followed
@@ -178,3 +178,56 @@ def test_decode_append_random(i, B, Nq, Nkv, Dh, Tcap, window, explicit, style, 
     assert _bits_equal(k1, k2) and _bits_equal(v1, v2), "cache rows"
     same_form = not (Dh == 256 and takes_even_split(B, Nq, Nkv, Dh, Tcap, window))
     assert _agree(O1, L1, O2, L2, same_form)
+
+
+def _chunk_cases(n):
+    out = []
+    for i in range(n):
+        Nkv, G, Dh = _pick([1, 2, 4, 8]), _pick([1, 2, 4, 8]), _pick([64, 128, 128, 256])
+        B = int(_rng.integers(1, 5))
+        Tcap = int(_rng.integers(16, 8193))
+        while B * Nkv * Tcap * Dh > 16 * 2 ** 20:
+            Tcap //= 2
+        Tcap = max(Tcap, 16)
+        Sq = int(_rng.integers(1, min(Tcap, 2048) + 1))
+        window = int(_rng.integers(1, Tcap + 65)) if _rng.random() < 0.3 else 0
+        out.append((i, B, Nkv * G, Nkv, Sq, Dh, Tcap, window, _pick(["implicit", "start", "explicit"]),
+                    _pick(["pairs", "half"]), bool(_rng.random() < 0.3)))
+    return out
+
+
+@pytest.mark.parametrize("i,B,Nq,Nkv,Sq,Dh,Tcap,window,mode,style,pad", _chunk_cases(30))
+def test_prefill_cache_rope_random(i, B, Nq, Nkv, Sq, Dh, Tcap, window, mode, style, pad):
+    # a chunk of Sq queries at the end of lens[b] cached keys; the two-pass form
+    # rotates the chunk at the positions the fused call uses (lens[b] - Sq + i
+    # when none are given)
+    dev = device()
+    g = np.random.default_rng(2500 + i)
+    torch.manual_seed(2500 + i)
+    q = torch.randn(B, Nq, Sq, Dh, device=dev).to(torch.bfloat16)
+    kc = torch.randn(B, Nkv, Tcap, Dh, device=dev).to(torch.bfloat16)
+    vc = torch.randn(B, Nkv, Tcap, Dh, device=dev).to(torch.bfloat16)
+    lens_np = g.integers(Sq, Tcap + 1, B).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
+    P = Tcap + 3000
+    table = tch.rope_table(P, Dh, device=dev)
+    pos = start = None
+    if mode == "start":
+        start_np = g.integers(0, P - Sq + 1, B).astype(np.int32)
+        start = torch.from_numpy(start_np).to(dev)
+        at = start_np[:, None] + np.arange(Sq, dtype=np.int32)[None, :]
+    elif mode == "explicit":
+        at = g.integers(0, P, (B, Sq)).astype(np.int32)
+        pos = torch.from_numpy(at).to(dev)
+    else:
+        at = (lens_np - Sq)[:, None] + np.arange(Sq, dtype=np.int32)[None, :]
+    bits = _key_bits(B, Tcap, g) if pad else None
+    say(f"random fused chunk {(i, B, Nq, Nkv, Sq, Dh, Tcap, window, mode, style, pad)}")
+    O1, L1 = torch.empty_like(q), torch.empty(B, Nq, Sq, device=dev)
+    tch.attn_prefill_cache_rope(q, kc, vc, lens, O1, L1, table, key_bits=bits, positions=pos,
+                                start=start, style=style, window=window)
+    qr = tch.rope(q, table, positions=torch.from_numpy(np.ascontiguousarray(at)).to(dev), style=style)
+    O2, L2 = torch.empty_like(q), torch.empty(B, Nq, Sq, device=dev)
+    tch.attn_prefill_cache(qr, kc, vc, lens, O2, L2, window=window, key_bits=bits)
+    torch.cuda.synchronize()
+    assert _agree(O1, L1, O2, L2, True)
