@@ -1,9 +1,11 @@
 """Seeded random shapes for the fused calls: each against the two calls it replaces.
 
-attn_prefill_rope, attn_prefill_cache_rope, attn_decode_rope and attn_decode_append on shapes drawn
+attn_prefill_rope, attn_prefill_cache_rope, attn_decode_rope, attn_decode_append and
+attn_kv_append_rope on shapes drawn
 from a fixed seed (head sizes 64-256, groups to 32, batches to 64, windows,
 key-padding masks, every position mode, both rotation layouts), each compared
-with attn_rope followed by the unrotated call, or with attn_kv_append followed
+with attn_rope followed by the unrotated call (for the rotating append: attn_rope
+on the new keys, then attn_kv_append), or with attn_kv_append followed
 by attn_decode_window.  Both sides compute the same rows in the same order, so
 the bits must match (the caches too, for the append).  One exception: at head
 size 256 an unrotated or non-appending decode large enough for the even split
@@ -231,3 +233,43 @@ def test_prefill_cache_rope_random(i, B, Nq, Nkv, Sq, Dh, Tcap, window, mode, st
     tch.attn_prefill_cache(qr, kc, vc, lens, O2, L2, window=window, key_bits=bits)
     torch.cuda.synchronize()
     assert _agree(O1, L1, O2, L2, True)
+
+
+def _append_cases(n):
+    out = []
+    for i in range(n):
+        B, Nkv, Dh = int(_rng.integers(1, 9)), _pick([1, 2, 4, 8]), _pick([40, 64, 80, 128, 256])
+        Tcap = int(_rng.integers(16, 4097))
+        rolling = bool(_rng.random() < 0.4)
+        Snew = int(_rng.integers(1, 301)) if rolling else int(_rng.integers(1, min(300, Tcap) + 1))
+        out.append((i, B, Nkv, Snew, Dh, Tcap, rolling, bool(_rng.random() < 0.5),
+                    _pick(["pairs", "half"]), _pick(["bf16", "f32"])))
+    return out
+
+
+@pytest.mark.parametrize("i,B,Nkv,Snew,Dh,Tcap,rolling,explicit,style,dtype", _append_cases(30))
+def test_kv_append_rope_random(i, B, Nkv, Snew, Dh, Tcap, rolling, explicit, style, dtype):
+    dev = device()
+    g = np.random.default_rng(3500 + i)
+    torch.manual_seed(3500 + i)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    knew = torch.randn(B, Nkv, Snew, Dh, device=dev).to(dt)
+    vnew = torch.randn(B, Nkv, Snew, Dh, device=dev).to(dt)
+    kc = torch.randn(B, Nkv, Tcap, Dh, device=dev).to(dt)
+    vc = torch.randn(B, Nkv, Tcap, Dh, device=dev).to(dt)
+    hi = 3 * Tcap if rolling else Tcap - Snew
+    pos_np = g.integers(0, hi + 1, B).astype(np.int32)
+    P = int(pos_np.max()) + Snew + 500
+    table = tch.rope_table(P, Dh, device=dev)
+    at = g.integers(0, P, (B, Snew)).astype(np.int32) if explicit else \
+        pos_np[:, None] + np.arange(Snew, dtype=np.int32)[None, :]
+    pos = torch.from_numpy(pos_np).to(dev)
+    say(f"random rotating append {(i, B, Nkv, Snew, Dh, Tcap, rolling, explicit, style, dtype)}")
+    k1, v1, k2, v2 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    tch.attn_kv_append_rope(knew, vnew, k1, v1, pos, table,
+                            positions=torch.from_numpy(at).to(dev) if explicit else None,
+                            rolling=int(rolling), style=style)
+    kr = tch.rope(knew, table, positions=torch.from_numpy(np.ascontiguousarray(at)).to(dev), style=style)
+    tch.attn_kv_append(kr, vnew, k2, v2, pos, rolling=int(rolling))
+    torch.cuda.synchronize()
+    assert _bits_equal(k1, k2) and _bits_equal(v1, v2)
