@@ -141,3 +141,37 @@ def grad_rows_ratio(g, r):
     scale_row = np.maximum(np.abs(r).max(axis=1, keepdims=True), 1e-2 * np.abs(r).max())
     scale_row = np.where(scale_row > 0, scale_row, 1.0)
     return np.abs(g - r) / scale_row
+
+
+def stored_o_backward(Q, K, V, dO, causal=True, window=0, scale=None):
+    """The oracle's forward and backward with O as the forward stores it.
+
+    The backward takes O and LSE as inputs and forms Delta = rowsum(dO * O)
+    from the O it is given.  Returns O rounded to bf16 (from fp32, as the
+    forward rounds it), the exact LSE, and the oracle's dQ, dK, dV shifted to
+    that stored O: with dDelta_i = dO_i . (bf16(O_i) - O_i), every
+    dS_ij = P_ij (dP_ij - Delta_i) moves by -P_ij dDelta_i, so dQ_i moves by
+    -scale * dDelta_i * sum_j P_ij K_j and dK_j by -scale * sum_i P_ij dDelta_i Q_i
+    (over the group's query heads); dV does not depend on Delta.  Giving the
+    backward these O and LSE makes its expected gradients a function of
+    oracle values alone; in rows whose weight sits on a few keys the rounding
+    of O moves Delta by far more than the rest of the backward's roundings.
+    """
+    B, Nq, S, Dh = Q.shape
+    Nkv = K.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dh)
+    dQ, dK, dV = oracle.backward_ref(Q, K, V, dO, causal=causal, window=window, scale=scale)
+    O_st = np.empty((B, Nq, S, Dh))
+    LSE = np.empty((B, Nq, S))
+    for b in range(B):
+        for h in range(Nq):
+            g = oracle.kv_head_of(h, Nq, Nkv)
+            o, lse, P = oracle.head_attention(Q[b, h], np.arange(S), K[b, g], V[b, g], causal, window,
+                                              scale, return_probs=True)
+            O_st[b, h] = workloads.to_f64(workloads.f32_to_bf16_bits(o.astype(np.float32)), "bf16")
+            LSE[b, h] = lse
+            d_delta = np.sum(dO[b, h] * (O_st[b, h] - o), axis=1)
+            dQ[b, h] -= scale * d_delta[:, None] * (P @ K[b, g])
+            dK[b, g] -= scale * (P * d_delta[:, None]).T @ Q[b, h]
+    return O_st, LSE, dQ, dK, dV

@@ -31,10 +31,16 @@ BF16_MEAN_FLOOR = 1e-4
 F32_REL = 1e-4
 
 
-def _grads(q, k, v, dO, dtype, causal, window, scale=None):
+def _grads(q, k, v, dO, dtype, causal, window, scale=None, given=None):
+    # given: (O, LSE) as float64 arrays to pass to the backward instead of the
+    # library's own forward output
     dev = device()
     tq, tk, tv, tdo = (workloads.to_torch(x, dtype, dev) for x in (q, k, v, dO))
-    O, L = tch.prefill(tq, tk, tv, causal=causal, window=window, scale=scale)
+    if given is None:
+        O, L = tch.prefill(tq, tk, tv, causal=causal, window=window, scale=scale)
+    else:
+        O = torch.from_numpy(given[0].astype(np.float32)).to(dev).to(tq.dtype)
+        L = torch.from_numpy(given[1].astype(np.float32)).to(dev)
     dQ, dK, dV = tch.backward(tq, tk, tv, O, L, tdo, causal=causal, window=window, scale=scale)
     torch.cuda.synchronize()
     return [workloads.to_f64(workloads.from_torch(t, dtype), dtype) for t in (dQ, dK, dV)]

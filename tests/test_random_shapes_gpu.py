@@ -20,7 +20,7 @@ import torch
 import oracle
 import transformer_causal_head_amd as tch
 import workloads
-from helpers import check, device, run_prefill, say
+from helpers import check, device, run_prefill, say, stored_o_backward
 from test_backward_gpu import _check as _check_grads, _grads, _inputs as _grad_inputs
 from test_rope_padding_gpu import _split_dead
 
@@ -139,9 +139,16 @@ def _backward_cases(n):
 @pytest.mark.parametrize("i,B,Nq,Nkv,S,Dh,dtype,causal,window", _backward_cases(16))
 def test_random_backward(i, B, Nq, Nkv, S, Dh, dtype, causal, window):
     q, k, v, dO = _grad_inputs(B, Nq, Nkv, S, Dh, dtype, seed=700 + i)
-    got = _grads(q, k, v, dO, dtype, causal, window)
-    ref = oracle.backward_ref(*(workloads.to_f64(x, dtype) for x in (q, k, v, dO)),
-                              causal=causal, window=window)
+    if dtype == "bf16":
+        # the backward is given the oracle's O (stored in bf16) and LSE, and
+        # held to the oracle's gradients for that stored O
+        O_st, LSE, *ref = stored_o_backward(*(workloads.to_f64(x, dtype) for x in (q, k, v, dO)),
+                                            causal=causal, window=window)
+        got = _grads(q, k, v, dO, dtype, causal, window, given=(O_st, LSE))
+    else:
+        got = _grads(q, k, v, dO, dtype, causal, window)
+        ref = oracle.backward_ref(*(workloads.to_f64(x, dtype) for x in (q, k, v, dO)),
+                                  causal=causal, window=window)
     _check_grads(got, ref, dtype, (i, B, Nq, Nkv, S, Dh, causal, window))
 
 
